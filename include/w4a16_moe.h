@@ -1,0 +1,207 @@
+/*
+ * w4a16_moe.h -- C ABI of the fused grouped W4A16 mixture-of-experts layer for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer is the routed-expert part of ExactMoE (page "Every Expert Counts:
+ * ExactMoE for Memory-Efficient W4A16 Inference", Abstract): routed experts'
+ * weights are symmetric four-bit integers with one scale per group of 128 input
+ * channels, activations and the router stay BF16, the top-k routing procedure
+ * is unchanged, every selected expert runs (none pruned or substituted), the
+ * quantised experts may live in pinned host memory and reach the GPU through a
+ * configurable number of resident slots, and all selected experts of a step run
+ * through one fused grouped pass.  Expert FFN = SwiGLU: h = silu(x Wg^T) *
+ * (x Wu^T), y = h Wd^T; out[t] = sum_j w[t,j] * y[t,j].
+ *
+ * Conventions for every call
+ *  - Pointers named *_dev / all tensor pointers are device pointers unless the
+ *    parameter says "host".  bf16 values travel as uint16_t bit patterns.  All
+ *    arrays are dense row-major with the shapes given; no hidden transposes.
+ *  - The caller owns every buffer.  No call allocates device memory.
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Calls only
+ *    enqueue work; nothing synchronises except where stated.
+ *  - Return value: MOE_OK (0) or a moe_status code.  Argument and shape checks
+ *    run on the host before anything is enqueued; on failure nothing is
+ *    enqueued and moe_last_error() (thread-local) describes the problem.
+ *  - Inputs must be finite; NaN / Inf inputs give unspecified outputs.
+ */
+#ifndef W4A16_MOE_H
+#define W4A16_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,      /* null pointer, negative size, bad enum */
+  MOE_ERR_UNSUPPORTED_SHAPE = 2,/* K % 128 != 0, N % 16 != 0, E > 1024, k > 16, ... */
+  MOE_ERR_WORKSPACE = 3,        /* workspace too small or misaligned */
+  MOE_ERR_CAPACITY = 4,         /* slot cache: fewer slots than experts a token needs */
+  MOE_ERR_HIP = 5               /* a HIP launch or copy failed */
+};
+
+#define MOE_GROUP 128           /* quantisation group along K (input channels) */
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOPK 16
+
+/* Status name of a code (static string). */
+const char* moe_status_string(int status);
+/* Message of the last failing call on this thread ("" if none). */
+const char* moe_last_error(void);
+/* ABI version of this library. */
+int moe_abi_version(void);
+
+/*
+ * Byte layout of one packed expert ("blob"): w13 codes | w13 scales | w2 codes
+ * | w2 scales, each section starting on a 256-byte boundary.  w13 is [2I, d]
+ * (gate rows then up rows, packed with gate/up interleaving), w2 is [d, I].
+ * A bank of experts (resident or slots) is an array of blobs at a fixed stride.
+ */
+typedef struct {
+  int64_t w13_codes, w13_scales, w2_codes, w2_scales; /* byte offsets in the blob */
+  int64_t blob_bytes;                                  /* total, multiple of 256 */
+} moe_expert_layout;
+int moe_expert_layout_get(int d, int I, moe_expert_layout* out);
+
+/*
+ * pack_w4_g128 -- quantise and pack E weight matrices (ExactMoE, Abstract:
+ * symmetric group-128 four-bit routed-expert weights).
+ *
+ *  w       [E][N][K] bf16, device.
+ *  scale of (row, group) = bf16_rne(amax / 7), amax = max |w| over the 128
+ *  inputs of the group; q = clamp(rne(w / scale), -8, 7), q = 0 when scale = 0;
+ *  stored code = q + 8 (4 bits).
+ *  codes   device, expert e at codes + e * codes_stride (bytes), N*K/2 bytes each,
+ *          packed layout v1: 16x128 tiles of 1024 bytes at (nb*K/128 + kb)*1024;
+ *          lane L = 0..63 of a tile owns bytes 16L..16L+15 = row nb*16 + L%16,
+ *          columns kb*128 + 32i + 8(L/16) + m in 32-bit word i; element m's code
+ *          is the 4-bit field at bit (3 + 4(m/2) + 16(m%2)) mod 32 (wrapping).
+ *  scales  device, expert e at (uint8_t*)scales + e * scales_stride (bytes),
+ *          bf16 [N/16][K/128][16].
+ *  gateup_interleave: 1 = W is [gate; up] (N = 2I); packed row tile 2j holds gate
+ *          rows 16j.., tile 2j+1 up rows 16j.. (N % 32 == 0 required).
+ *  Errors: MOE_ERR_UNSUPPORTED_SHAPE unless N % 16 == 0 and K % 128 == 0.
+ *  The result is bit-identical to the reference quantiser.
+ */
+int pack_w4_g128(const uint16_t* w, int E, int N, int K, int gateup_interleave,
+                 uint8_t* codes, int64_t codes_stride,
+                 uint16_t* scales, int64_t scales_stride, void* stream);
+
+/*
+ * moe_route -- BF16 router and unchanged top-k (ExactMoE, Abstract).
+ *
+ *  x            [T][d] bf16 activations.  w_router [E][d] bf16.
+ *  logits       [T][E] float32 output (required): sum_c x[t,c] * w_router[e,c],
+ *               products exact, summed in float64, rounded once to float32.
+ *  topk_ids     [T][k] int32 output: experts ordered by (logit desc, index asc).
+ *  topk_weights [T][k] float32 output: exp(l_j - l_max) / sum over the selected
+ *               experts (renormalize = 1) or over all E (renormalize = 0).
+ *  Limits: 1 <= k <= min(E, 16), E <= 1024, d % 8 == 0.  T == 0 is a no-op.
+ */
+int moe_route(const uint16_t* x, const uint16_t* w_router, int T, int d, int E, int k,
+              int renormalize, float* logits, int32_t* topk_ids, float* topk_weights,
+              void* stream);
+
+/*
+ * moe_align -- expert-sorted permutation of the T*k (token, slot) pairs that
+ * feeds the grouped kernels.  Stable counting sort, pair p = t*k + j.
+ *
+ *  expert_offsets [E+1] int32: exclusive prefix sum of per-expert pair counts.
+ *  sorted_pairs   [T*k] int32: pair ids grouped by expert, increasing within a group.
+ *  pair_pos       [T*k] int32: position of pair p in sorted_pairs.
+ *  active_experts [E+1] int32: [0] = U (experts with >= 1 pair), [1..U] their ids ascending.
+ *  tile_offsets   [E+1] int32 or NULL: exclusive prefix sum of ceil(count / block_m)
+ *                 (only when block_m > 0).
+ *  Limits: E <= 1024, k <= 16, T*k <= 2^24.  Entries of topk_ids must lie in [0, E).
+ *  Bit-exact: the output is unique.
+ */
+int moe_align(const int32_t* topk_ids, int T, int k, int E, int block_m,
+              int32_t* expert_offsets, int32_t* sorted_pairs, int32_t* pair_pos,
+              int32_t* active_experts, int32_t* tile_offsets, void* stream);
+
+/*
+ * moe_w4a16_grouped_ffn -- the fused grouped expert pass (ExactMoE, Abstract:
+ * all selected experts through fused grouped kernels): gate/up + SwiGLU, down,
+ * routing-weighted combine, over the expert-sorted pairs from moe_align.
+ */
+enum moe_ffn_mode { MOE_MODE_AUTO = 0, MOE_MODE_DECODE = 1, MOE_MODE_PREFILL = 2 };
+
+typedef struct {
+  const uint16_t* x;              /* [T][d] bf16 */
+  int T, d, I, E, k;
+  const int32_t* topk_ids;        /* [T][k] from moe_route */
+  const float* topk_weights;      /* [T][k] from moe_route */
+  const int32_t* expert_offsets;  /* from moe_align */
+  const int32_t* sorted_pairs;
+  const int32_t* pair_pos;
+  const int32_t* active_experts;
+  const int32_t* tile_offsets;    /* required for prefill mode with block_m = 128; else may be NULL */
+  const uint8_t* bank;            /* expert blobs (moe_expert_layout), device */
+  int64_t bank_stride;            /* bytes between blobs */
+  const int32_t* slot_of_expert;  /* [E] device or NULL: blob index of each expert;
+                                     -1 = skip the expert in this call */
+  int mode;                       /* moe_ffn_mode */
+  int combine;                    /* 1 = finish with the combine into `out`;
+                                     0 = leave per-pair results in the workspace */
+  uint16_t* out;                  /* [T][d] bf16 (written when combine = 1) */
+  void* workspace;                /* device, 256-byte aligned */
+  int64_t workspace_bytes;
+} moe_ffn_args;
+
+/* Workspace the call needs for these sizes and mode (bytes). */
+int64_t moe_ffn_workspace_bytes(int T, int d, int I, int E, int k, int mode);
+int moe_w4a16_grouped_ffn(const moe_ffn_args* args, void* stream);
+
+/*
+ * Expert slot cache (ExactMoE, Abstract: quantised experts in pinned host
+ * memory, executed from a configurable GPU-resident slot cache).
+ *
+ * moe_slot_cache_create: host bookkeeping for E experts and S device slots.
+ *   host_store   pinned host memory (hipHostMalloc), E blobs at blob_bytes stride.
+ *   device_slots device memory, S blobs at blob_bytes stride.
+ *   The cache allocates (once, here) a small ring of pinned host staging
+ *   tables for the expert->slot map; nothing is allocated afterwards.
+ * slot_cache_load: one round for the pending experts (host bitmask, ceil(E/64)
+ *   words).  Takes the pending experts already resident (hits), then missing ones
+ *   in ascending id until the S slots are full; each miss replaces the least
+ *   recently used slot not holding a hit (empty slots first, ties to the lower
+ *   slot).  On copy_stream, after wait_event (may be NULL; record it after the
+ *   last kernel that read the slots), it enqueues the H2D copies of the misses,
+ *   then the copy of the round's expert->slot table into slot_table_dev ([E]
+ *   int32: slot of each expert of this round, -1 for every other expert), and
+ *   records done_event (the grouped kernels wait on it).
+ *   round_mask (host out, ceil(E/64) words) = experts of this round; the caller
+ *   clears them from pending and calls again until nothing is pending (one round
+ *   when the pending set fits in S).  n_hits / n_misses (host out, may be NULL).
+ *   Errors: MOE_ERR_HIP when a copy cannot be enqueued; the slot it was meant
+ *   for is then marked empty, so no slot is ever reported half-loaded.
+ */
+typedef struct moe_slot_cache moe_slot_cache;
+int moe_slot_cache_create(int E, int S, int64_t blob_bytes, const void* host_store,
+                          void* device_slots, moe_slot_cache** out);
+int moe_slot_cache_destroy(moe_slot_cache* cache);
+int slot_cache_load(moe_slot_cache* cache, const uint64_t* pending_mask, uint64_t* round_mask,
+                    int32_t* slot_table_dev, int32_t* n_hits, int32_t* n_misses,
+                    void* copy_stream, void* wait_event, void* done_event);
+/* Current slot contents ([S] expert id or -1) and cumulative hit / miss counts. */
+int moe_slot_cache_state(const moe_slot_cache* cache, int32_t* slot_expert,
+                         int64_t* hits, int64_t* misses);
+
+/*
+ * Kernel timing: when enabled, each launch of the named kernel is bracketed by
+ * hipEvents on its own stream.  moe_timing_read synchronises on the recorded
+ * events and returns the summed duration and launch count since the last reset.
+ * Kernel ids: 0 = gate/up (decode), 1 = down (decode), 2 = gate/up (prefill),
+ * 3 = down (prefill), 4 = combine, 5 = route logits, 6 = align.
+ */
+int moe_timing_enable(int on);
+int moe_timing_reset(void);
+int moe_timing_read(int kernel_id, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* W4A16_MOE_H */

@@ -1,0 +1,125 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol that
+include/w4a16_moe.h declares, and rejects bad arguments on the host before
+anything is enqueued (no HIP call is reached on these paths)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER_DIR = os.path.join(ROOT, "include")
+
+
+def declared_functions():
+    names = []
+    for fn in sorted(os.listdir(HEADER_DIR)):
+        if not fn.endswith(".h"):
+            continue
+        src = open(os.path.join(HEADER_DIR, fn)).read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        src = re.sub(r"^\s*#.*$", " ", src, flags=re.M)
+        src = re.sub(r"typedef\s+struct\s*\{.*?\}\s*\w+\s*;", " ", src, flags=re.S)
+        src = re.sub(r"enum\s+\w*\s*\{.*?\}\s*;", " ", src, flags=re.S)
+        for m in re.finditer(r"(?:^|;)\s*(?:const\s+)?[A-Za-z_][\w]*\s*\**\s+\**\s*([A-Za-z_]\w*)\s*\(", src, re.M):
+            names.append(m.group(1))
+    return names
+
+
+@pytest.fixture(scope="module")
+def L():
+    from w4a16_grouped_expert_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail(f"library not built: {_lib.LIB_PATH}")
+    return _lib.lib()
+
+
+def test_header_declares_the_five_entry_points():
+    names = set(declared_functions())
+    for n in ("moe_route", "moe_align", "moe_w4a16_grouped_ffn", "pack_w4_g128", "slot_cache_load"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) >= 15
+    raw = ctypes.CDLL(os.path.join(ROOT, "w4a16_grouped_expert_amd", "lib", "libw4a16moe.so"))
+    missing = [n for n in names if not hasattr(raw, n)]
+    assert not missing, missing
+
+
+def test_binding_covers_every_declared_symbol(L):
+    from w4a16_grouped_expert_amd import _lib
+    assert set(declared_functions()) == set(_lib.SIGNATURES)
+
+
+def test_status_strings(L):
+    assert L.moe_status_string(0) == b"MOE_OK"
+    assert L.moe_status_string(2) == b"MOE_ERR_UNSUPPORTED_SHAPE"
+    assert L.moe_abi_version() == 1
+
+
+def test_layout_matches_oracle_blob_layout(L):
+    from oracle import quant
+    from w4a16_grouped_expert_amd import _lib
+    for d, I in ((256, 512), (2048, 1024), (4096, 14336), (128, 128)):
+        lay = _lib.ExpertLayout()
+        assert L.moe_expert_layout_get(d, I, ctypes.byref(lay)) == 0
+        offs, total = quant.blob_layout(d, I)
+        assert (lay.w13_codes, lay.w13_scales, lay.w2_codes, lay.w2_scales) == offs
+        assert lay.blob_bytes == total
+    lay = _lib.ExpertLayout()
+    assert L.moe_expert_layout_get(2000, 1024, ctypes.byref(lay)) == 2
+    assert b"multiples of 128" in L.moe_last_error()
+
+
+def test_host_side_argument_checks(L):
+    vp = ctypes.c_void_p(16)  # never dereferenced: every call below fails its host checks first
+    # pack: K not a multiple of 128, N not a multiple of 16, interleave needs N % 32
+    assert L.pack_w4_g128(vp, 1, 16, 100, 0, vp, 0, vp, 0, None) == 2
+    assert L.pack_w4_g128(vp, 1, 24, 128, 0, vp, 0, vp, 0, None) == 2
+    assert L.pack_w4_g128(vp, 1, 48, 128, 1, vp, 0, vp, 0, None) == 2
+    assert L.pack_w4_g128(vp, -1, 16, 128, 0, vp, 0, vp, 0, None) == 1
+    assert L.pack_w4_g128(None, 1, 16, 128, 0, vp, 0, vp, 0, None) == 1
+    assert L.pack_w4_g128(None, 0, 16, 128, 0, None, 0, None, 0, None) == 0   # empty: no-op
+    # route: k > E, E > 1024, d % 8, null outputs
+    assert L.moe_route(vp, vp, 4, 64, 8, 9, 1, vp, vp, vp, None) == 2
+    assert L.moe_route(vp, vp, 4, 64, 2000, 8, 1, vp, vp, vp, None) == 2
+    assert L.moe_route(vp, vp, 4, 60, 8, 2, 1, vp, vp, vp, None) == 2
+    assert L.moe_route(vp, vp, 4, 64, 8, 2, 1, None, vp, vp, None) == 1
+    assert L.moe_route(None, None, 0, 64, 8, 2, 1, None, None, None, None) == 0  # T = 0: no-op
+    # align: E > 1024, k > 16, block_m without tile_offsets
+    assert L.moe_align(vp, 4, 2, 1025, 0, vp, vp, vp, vp, None, None) == 2
+    assert L.moe_align(vp, 4, 17, 64, 0, vp, vp, vp, vp, None, None) == 2
+    assert L.moe_align(vp, 4, 2, 8, 64, vp, vp, vp, vp, None, None) == 1
+    # ffn: null args, bad shapes, small workspace
+    from w4a16_grouped_expert_amd import _lib
+    assert L.moe_w4a16_grouped_ffn(None, None) == 1
+    a = _lib.FfnArgs()
+    a.T, a.d, a.I, a.E, a.k = 4, 200, 512, 8, 2
+    assert L.moe_w4a16_grouped_ffn(ctypes.byref(a), None) == 2
+    a.d = 256
+    assert L.moe_w4a16_grouped_ffn(ctypes.byref(a), None) == 1            # null pointers
+    for f in ("x", "topk_ids", "topk_weights", "expert_offsets", "sorted_pairs", "pair_pos", "active_experts",
+              "out"):
+        setattr(a, f, 256)
+    a.bank, a.bank_stride, a.workspace, a.combine = 256, 202752, 256, 1
+    a.workspace_bytes = 16
+    assert L.moe_w4a16_grouped_ffn(ctypes.byref(a), None) == 3           # workspace too small
+    assert b"workspace" in L.moe_last_error()
+    a.bank_stride = 1000
+    assert L.moe_w4a16_grouped_ffn(ctypes.byref(a), None) == 1           # stride below one blob
+    # slot cache: argument validation before any allocation
+    h = ctypes.c_void_p()
+    assert L.moe_slot_cache_create(0, 16, 100, vp, vp, ctypes.byref(h)) == 1
+    assert L.moe_slot_cache_create(64, 16, 100, None, vp, ctypes.byref(h)) == 1
+    assert L.slot_cache_load(None, None, None, None, None, None, None, None, None) == 1
+    assert L.moe_timing_read(99, None, None) == 1
+
+
+def test_workspace_bytes_sizes(L):
+    # h [T*k, I] bf16 + y [ksplit, T*k, d] fp32, each rounded up to 256 bytes
+    ws = L.moe_ffn_workspace_bytes(16, 2048, 1024, 64, 8, 1)
+    assert ws >= 16 * 8 * 1024 * 2 + 16 * 8 * 2048 * 4
+    assert L.moe_ffn_workspace_bytes(-1, 2048, 1024, 64, 8, 0) == -1

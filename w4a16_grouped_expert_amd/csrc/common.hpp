@@ -1,0 +1,87 @@
+// Internal helpers shared by the HIP sources of the W4A16 MoE library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+
+#include "w4a16_moe.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- host-side errors
+
+void set_error(const char* fmt, ...);
+void clear_error();
+
+#define MOE_CHECK_ARG(cond, code, ...)      \
+  do {                                       \
+    if (!(cond)) {                           \
+      ::moe::set_error(__VA_ARGS__);         \
+      return (code);                         \
+    }                                        \
+  } while (0)
+
+// Check the launch that was just enqueued.
+int check_launch(const char* what);
+
+// Timing hooks (see moe_timing_*): bracket one launch of `kernel_id`.
+enum KernelId { K_GATEUP_DECODE = 0, K_DOWN_DECODE = 1, K_GATEUP_PREFILL = 2, K_DOWN_PREFILL = 3,
+                K_COMBINE = 4, K_ROUTE = 5, K_ALIGN = 6, K_NUM = 7 };
+void timing_begin(int kernel_id, hipStream_t s);
+void timing_end(int kernel_id, hipStream_t s);
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------- device types
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kGroup = 128;          // quantisation group along K
+constexpr int kTileRows = 16;        // rows per packed tile
+constexpr int kTileBytes = 1024;     // bytes per packed tile (16 x 128 x 4 bit)
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// float32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t rotr32(uint32_t v, int n) {
+  return __builtin_amdgcn_alignbit(v, v, n);
+}
+
+// 16x16x32 bf16 MFMA, fp32 accumulate: C[16 x 16] += A[16 x 32] * B[32 x 16].
+// Lane l supplies A row (l % 16) and B column (l % 16), eight consecutive k each;
+// C: lane l holds column l % 16, rows 4*(l / 16) + 0..3.
+__device__ __forceinline__ f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// One 32-bit word of packed codes (8 elements) -> 8 bf16 values (1 + code/16).
+// Element m's code sits at bit (3 + 4(m/2) + 16(m%2)) mod 32, so rotating right by
+// 4p puts elements 2p and 2p+1 at bits 3..6 and 19..22, i.e. straight into the
+// top mantissa bits of two bf16 values with exponent 0 (0x3F80 = 1.0).
+__device__ __forceinline__ u32x4_t decode_word_biased(uint32_t w) {
+  u32x4_t r;
+  r[0] = (w & 0x00780078u) | 0x3F803F80u;
+  r[1] = (rotr32(w, 4) & 0x00780078u) | 0x3F803F80u;
+  r[2] = (rotr32(w, 8) & 0x00780078u) | 0x3F803F80u;
+  r[3] = (rotr32(w, 12) & 0x00780078u) | 0x3F803F80u;
+  return r;
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+}  // namespace moe

@@ -1,0 +1,158 @@
+// moe_w4a16_grouped_ffn: host dispatch of the fused grouped expert pass and the
+// routing-weighted combine (ExactMoE, page "Every Expert Counts: ExactMoE for
+// Memory-Efficient W4A16 Inference", Abstract: every selected expert executes
+// through fused grouped kernels; none is pruned or substituted).
+//
+// Workspace: h [T*k][I] bf16 (SwiGLU output, expert-sorted rows) followed by
+// y [ksplit][T*k][d] fp32 (down-projection partials, expert-sorted rows).
+// The combine reads y through pair_pos, sums the K-split partials in a fixed
+// order and the k routed outputs in slot order, in fp32, and rounds once to bf16.
+#include "ffn_common.hpp"
+
+namespace moe {
+
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, int ksplit, int64_t P, int d, int k,
+                                                 const int32_t* __restrict__ pair_pos,
+                                                 const float* __restrict__ w, uint16_t* __restrict__ out,
+                                                 int nchunks) {
+  const int64_t t = blockIdx.x / nchunks;
+  const int n = ((blockIdx.x % nchunks) * 256 + threadIdx.x) * 4;
+  if (n >= d) return;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < k; ++j) {
+    const int64_t pos = pair_pos[t * k + j];
+    const float wj = w[t * k + j];
+    f32x4_t v = *reinterpret_cast<const f32x4_t*>(y + pos * d + n);
+    for (int s = 1; s < ksplit; ++s) {
+      const f32x4_t p = *reinterpret_cast<const f32x4_t*>(y + ((int64_t)s * P + pos) * d + n);
+      v[0] += p[0];
+      v[1] += p[1];
+      v[2] += p[2];
+      v[3] += p[3];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = fmaf(wj, v[r], acc[r]);
+  }
+  u32x2_t o = {f32_to_bf16_bits(acc[0]) | (f32_to_bf16_bits(acc[1]) << 16),
+               f32_to_bf16_bits(acc[2]) | (f32_to_bf16_bits(acc[3]) << 16)};
+  *reinterpret_cast<u32x2_t*>(out + t * d + n) = o;
+}
+
+static int resolve_mode(int T, int E, int k, int mode) {
+  if (mode == MOE_MODE_DECODE || mode == MOE_MODE_PREFILL) return mode;
+  const double per_expert = (double)T * k / E;  // expected pairs per expert
+  return per_expert <= 48.0 ? MOE_MODE_DECODE : MOE_MODE_PREFILL;
+}
+
+static int down_ksplit(int T, int d, int I, int E, int k, int mode) {
+  if (mode == MOE_MODE_PREFILL) return 1;
+  const int64_t umax = std::min<int64_t>(E, (int64_t)T * k);
+  const int64_t blocks = umax * (d / 32);
+  const int max_split = std::max(1, (I / kGroup) / 4);
+  int ks = 1;
+  while (ks * 2 <= max_split && blocks * ks < 2048) ks *= 2;
+  return ks;
+}
+
+static int64_t align256(int64_t v) { return (v + 255) / 256 * 256; }
+
+struct WsLayout {
+  int64_t h_off, y_off, total;
+};
+
+static WsLayout ws_layout(int T, int d, int I, int E, int k, int mode) {
+  const int64_t P = (int64_t)T * k;
+  const int ks = down_ksplit(T, d, I, E, k, mode);
+  WsLayout L;
+  L.h_off = 0;
+  L.y_off = align256(P * I * 2);
+  L.total = L.y_off + align256((int64_t)ks * P * d * 4);
+  return L;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" int64_t moe_ffn_workspace_bytes(int T, int d, int I, int E, int k, int mode) {
+  if (T < 0 || d <= 0 || I <= 0 || E <= 0 || k <= 0) return -1;
+  return ws_layout(T, d, I, E, k, resolve_mode(T, E, k, mode)).total;
+}
+
+extern "C" int moe_w4a16_grouped_ffn(const moe_ffn_args* a, void* stream) {
+  clear_error();
+  MOE_CHECK_ARG(a != nullptr, MOE_ERR_INVALID_ARG, "moe_w4a16_grouped_ffn: args is NULL");
+  MOE_CHECK_ARG(a->T >= 0 && a->d > 0 && a->I > 0 && a->E > 0 && a->k > 0, MOE_ERR_INVALID_ARG,
+                "moe_w4a16_grouped_ffn: bad sizes T=%d d=%d I=%d E=%d k=%d", a->T, a->d, a->I, a->E, a->k);
+  MOE_CHECK_ARG(a->mode >= 0 && a->mode <= 2, MOE_ERR_INVALID_ARG, "moe_w4a16_grouped_ffn: bad mode %d", a->mode);
+  MOE_CHECK_ARG(a->d % kGroup == 0 && a->I % kGroup == 0 && a->E <= MOE_MAX_EXPERTS && a->k <= MOE_MAX_TOPK &&
+                    a->k <= a->E && (int64_t)a->T * a->k <= (1 << 24),
+                MOE_ERR_UNSUPPORTED_SHAPE,
+                "moe_w4a16_grouped_ffn: unsupported shape d=%d I=%d E=%d k=%d T=%d (d, I multiples of 128, "
+                "E <= 1024, k <= min(E,16))",
+                a->d, a->I, a->E, a->k, a->T);
+  if (a->T == 0) return MOE_OK;
+  MOE_CHECK_ARG(a->x && a->topk_ids && a->topk_weights && a->expert_offsets && a->sorted_pairs && a->pair_pos &&
+                    a->active_experts && a->bank && a->workspace,
+                MOE_ERR_INVALID_ARG, "moe_w4a16_grouped_ffn: null pointer");
+  MOE_CHECK_ARG(!a->combine || a->out, MOE_ERR_INVALID_ARG, "moe_w4a16_grouped_ffn: combine needs out");
+  moe_expert_layout lay;
+  int rc = moe_expert_layout_get(a->d, a->I, &lay);
+  if (rc) return rc;
+  MOE_CHECK_ARG(a->bank_stride >= lay.blob_bytes && a->bank_stride % 256 == 0 && ((uintptr_t)a->bank % 256) == 0,
+                MOE_ERR_INVALID_ARG,
+                "moe_w4a16_grouped_ffn: bank must be 256-byte aligned with stride >= %lld (multiple of 256), got %lld",
+                (long long)lay.blob_bytes, (long long)a->bank_stride);
+  MOE_CHECK_ARG(((uintptr_t)a->x % 16) == 0 && ((uintptr_t)a->workspace % 256) == 0 &&
+                    (!a->out || ((uintptr_t)a->out % 8) == 0),
+                MOE_ERR_INVALID_ARG, "moe_w4a16_grouped_ffn: misaligned x, out or workspace");
+  const int mode = resolve_mode(a->T, a->E, a->k, a->mode);
+  const WsLayout L = ws_layout(a->T, a->d, a->I, a->E, a->k, mode);
+  MOE_CHECK_ARG(a->workspace_bytes >= L.total, MOE_ERR_WORKSPACE,
+                "moe_w4a16_grouped_ffn: workspace %lld bytes < %lld needed", (long long)a->workspace_bytes,
+                (long long)L.total);
+
+  FfnDev f;
+  f.x = a->x;
+  f.T = a->T;
+  f.d = a->d;
+  f.I = a->I;
+  f.E = a->E;
+  f.k = a->k;
+  f.P = (int64_t)a->T * a->k;
+  f.umax = (int)std::min<int64_t>(a->E, f.P);
+  f.offsets = a->expert_offsets;
+  f.sorted_pairs = a->sorted_pairs;
+  f.pair_pos = a->pair_pos;
+  f.active = a->active_experts;
+  f.tile_offsets = a->tile_offsets;
+  f.bank = a->bank;
+  f.bank_stride = a->bank_stride;
+  f.slot_of_expert = a->slot_of_expert;
+  f.off_w13_codes = lay.w13_codes;
+  f.off_w13_scales = lay.w13_scales;
+  f.off_w2_codes = lay.w2_codes;
+  f.off_w2_scales = lay.w2_scales;
+
+  uint8_t* ws = static_cast<uint8_t*>(a->workspace);
+  uint16_t* h = reinterpret_cast<uint16_t*>(ws + L.h_off);
+  float* y = reinterpret_cast<float*>(ws + L.y_off);
+  hipStream_t s = (hipStream_t)stream;
+  const int ks = down_ksplit(a->T, a->d, a->I, a->E, a->k, mode);
+  if (mode == MOE_MODE_DECODE) {
+    const double per_expert = (double)a->T * a->k / a->E;
+    rc = launch_decode(f, h, y, ks, per_expert <= 8.0 ? 1 : 2, s);
+  } else {
+    rc = launch_prefill(f, h, y, s);
+  }
+  if (rc) return rc;
+  if (a->combine) {
+    const int nchunks = (int)ceil_div(a->d, 1024);
+    timing_begin(K_COMBINE, s);
+    hipLaunchKernelGGL(k_combine, dim3((unsigned)(a->T * (int64_t)nchunks)), dim3(256), 0, s, y, ks, f.P, a->d,
+                       a->k, a->pair_pos, a->topk_weights, a->out, nchunks);
+    timing_end(K_COMBINE, s);
+    rc = check_launch("combine");
+  }
+  return rc;
+}

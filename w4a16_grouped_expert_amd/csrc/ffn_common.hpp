@@ -1,0 +1,35 @@
+// Device-side view of one grouped FFN call, shared by the decode and prefill kernels.
+#pragma once
+
+#include "common.hpp"
+
+namespace moe {
+
+struct FfnDev {
+  const uint16_t* x;  // [T][d] bf16
+  int T, d, I, E, k;
+  int64_t P;          // T * k
+  int umax;           // upper bound on active experts: min(E, P)
+  const int32_t* offsets;
+  const int32_t* sorted_pairs;
+  const int32_t* pair_pos;
+  const int32_t* active;
+  const int32_t* tile_offsets;
+  const uint8_t* bank;
+  int64_t bank_stride;
+  const int32_t* slot_of_expert;
+  int64_t off_w13_codes, off_w13_scales, off_w2_codes, off_w2_scales;
+
+  // Blob of expert e, or nullptr when the expert is not part of this call.
+  __device__ __forceinline__ const uint8_t* blob(int e) const {
+    const int s = slot_of_expert ? slot_of_expert[e] : e;
+    return s < 0 ? nullptr : bank + (int64_t)s * bank_stride;
+  }
+};
+
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
+
+int launch_decode(const FfnDev& f, uint16_t* h, float* y, int ksplit, int nb, hipStream_t s);
+int launch_prefill(const FfnDev& f, uint16_t* h, float* y, hipStream_t s);
+
+}  // namespace moe

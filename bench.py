@@ -1,0 +1,299 @@
+"""Benchmark: W4A16 grouped-expert MoE layers on one MI355X.
+
+Workload: OLMoE-1B-7B-shaped decode, 16 MoE layers (d_model 2048, 64 experts,
+top-8, expert intermediate 1024, SwiGLU), int4 symmetric group-128 experts with
+bf16 scales, bf16 router and activations, all 64 experts of every layer
+resident in HBM (16 x 207.6 MB).  One step = route -> align -> grouped FFN
+(gate/up + SwiGLU, down, combine) for each of the 16 layers on fresh
+activations, T tokens per step (headline T = 16).
+
+Prints one JSON line: MoE-layer tokens/s (T * layers / step time), the
+achieved algorithmic HBM GB/s, the roofline of the dominant kernel (grouped
+gate/up) timed with HIP events on its own stream, and the CPU oracle timed on a
+bounded sample of the same workload.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + achieved HBM GB/s (W4A16, OLMoE shape, T=1..4096)"
+HBM_PEAK_GBPS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--tokens", type=int, default=16, help="tokens per decode step (headline 16)")
+    p.add_argument("--sweep", default="1,4", help="extra decode T values reported beside the headline")
+    p.add_argument("--x-sets", type=int, default=8, help="distinct activation sets cycled over steps")
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU-oracle baseline")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain device copy of known size (for HBM counter calibration)")
+    return p.parse_args()
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
+
+
+class Decoder:
+    """16 resident W4A16 MoE layers with shared per-step buffers."""
+
+    def __init__(self, wl, T_max, device):
+        import torch
+        import synth
+        import w4a16_grouped_expert_amd as moe
+        self.moe, self.torch = moe, torch
+        s = wl.shape
+        self.wl, self.s = wl, s
+        self.layers = []
+        for l in range(wl.layers):
+            w13, w2 = synth.expert_weights(wl, l, device=device)
+            bank, lay = moe.pack_experts(w13, w2)
+            del w13, w2
+            wr = synth.router_weight(wl, l, device="cpu").to(device)
+            self.layers.append((wr, bank))
+        torch.cuda.synchronize()
+        self.blob_bytes = lay["blob_bytes"]
+        self.T_max = T_max
+        self.route = moe.alloc_route(T_max, s.E, s.k, device)
+        self.align = moe.alloc_align(T_max, s.k, s.E, device)
+        need = max(moe.ffn_workspace_bytes(t, s.d, s.I, s.E, s.k) for t in range(1, T_max + 1))
+        self.ws = torch.empty(need, dtype=torch.uint8, device=device)
+        self.out = [torch.empty((T_max, s.d), dtype=torch.bfloat16, device=device) for _ in range(wl.layers)]
+
+    def layer(self, l, x):
+        moe, s = self.moe, self.s
+        T = x.shape[0]
+        wr, bank = self.layers[l]
+        r = moe.RouteOut(self.route.logits[:T], self.route.ids[:T], self.route.weights[:T])
+        a = moe.AlignOut(self.align.offsets, self.align.sorted_pairs[:T * s.k], self.align.pair_pos[:T * s.k],
+                         self.align.active, None, 0)
+        moe.moe_route_into(x, wr, s.k, r)
+        moe.moe_align_into(r.ids, s.E, a)
+        moe.moe_w4a16_grouped_ffn_into(x, r, a, bank, s.I, self.out[l][:T], self.ws)
+        return a
+
+    def step(self, xs):
+        for l, x in enumerate(xs):
+            self.layer(l, x)
+
+    def distinct_experts(self, xs):
+        """Active experts per layer for this step (untimed pre-pass)."""
+        us = []
+        for l, x in enumerate(xs):
+            a = self.layer(l, x)
+            us.append(int(a.active[0].item()))
+        return us
+
+
+def expert_section_bytes(d, I):
+    codes13, scales13 = 2 * I * d // 2, 2 * I * (d // 128) * 2
+    codes2, scales2 = d * I // 2, d * (I // 128) * 2
+    return codes13 + scales13, codes2 + scales2
+
+
+def capture_graphs(dec, xs_sets):
+    """One HIP graph per activation set, each holding a whole 16-layer step."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for xs in xs_sets:
+            dec.step(xs)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for xs in xs_sets:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            dec.step(xs)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
+
+
+def run_decode(dec, T, steps, warmup, x_sets):
+    """Time K steps replayed from HIP graphs (value), then K eager steps with the
+    dominant kernels bracketed by HIP events on their stream (roofline)."""
+    import torch
+    import synth
+    moe = dec.moe
+    wl, s = dec.wl, dec.s
+    xs = [[synth.activations(wl, T, l, step=st, device="cuda") for l in range(wl.layers)] for st in range(x_sets)]
+    U = [dec.distinct_experts(x) for x in xs]
+    graphs = capture_graphs(dec, xs)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for i in range(warmup):
+        graphs[i % x_sets].replay()
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(steps):
+        graphs[i % x_sets].replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    del graphs
+
+    for i in range(warmup):
+        dec.step(xs[i % x_sets])
+    torch.cuda.synchronize()
+    moe.timing_reset()
+    moe.timing_enable(True)
+    t0.record()
+    for i in range(steps):
+        dec.step(xs[i % x_sets])
+    t1.record()
+    torch.cuda.synchronize()
+    moe.timing_enable(False)
+    ms_eager = t0.elapsed_time(t1) / steps
+    res = {"T": T, "ms_per_step": ms, "ms_per_step_eager": ms_eager, "kernels": {}}
+    for kname in ("gateup_decode", "down_decode", "combine", "route", "align"):
+        tot, n = moe.timing_read(kname)
+        if n:
+            res["kernels"][kname] = {"avg_us": 1e3 * tot / n, "launches": n}
+    used = [U[i % x_sets] for i in range(steps)]
+    u_mean = sum(sum(u) for u in used) / (steps * wl.layers)
+    b13, b2 = expert_section_bytes(s.d, s.I)
+    router = s.E * s.d * 2
+    io = 2 * T * s.d * 2
+    layer_bytes = u_mean * (b13 + b2) + router + io
+    res["mean_distinct_experts"] = u_mean
+    res["layer_bytes"] = layer_bytes
+    res["tokens_per_s"] = T * wl.layers / (ms * 1e-3)
+    res["hbm_gbps"] = layer_bytes * wl.layers / (ms * 1e-3) / 1e9
+    # dominant kernel: grouped gate/up; algorithmic bytes per launch = distinct experts x
+    # (W13 codes + scales) + activations read + h written (bf16)
+    gu_bytes = u_mean * b13 + T * s.d * 2 + T * s.k * s.I * 2
+    res["gateup_bytes_per_launch"] = gu_bytes
+    return res
+
+
+def cpu_baseline(wl, T, budget_s):
+    """The CPU oracle on a bounded sample of the same workload: one OLMoE-shaped
+    layer at T tokens (route, align, per-pair SwiGLU FFN in float64, combine),
+    repeated until the time budget is used.  The experts' quantise/dequantise is
+    done up front and not timed, as the GPU path packs its weights offline."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+    import torch
+    import synth
+    from oracle import ffn as offn
+    from oracle import route as oroute
+
+    def bits(t):
+        return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    layer = 0
+    w13, w2 = synth.expert_weights(wl, layer, device="cuda")
+    wr = bits(synth.router_weight(wl, layer))
+    x = bits(synth.activations(wl, T, layer, step=0))
+    used = sorted(set(oroute.route(x, wr, wl.shape.k)[1].reshape(-1).tolist()))
+    host13 = {e: bits(w13[e].cpu()) for e in used}
+    host2 = {e: bits(w2[e].cpu()) for e in used}
+    del w13, w2
+    bank = offn.DequantBank(lambda e: host13[e], lambda e: host2[e])
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        deq = dict(zip(used, ex.map(lambda e: offn.DequantBank(lambda _: host13[e], lambda _: host2[e]).get(e),
+                                    used)))
+    bank._cache.update(deq)
+    calls, elapsed = 0, 0.0
+    while elapsed < budget_s or calls == 0:
+        t0 = time.perf_counter()
+        offn.moe_layer(x, wr, bank, wl.shape.k)
+        elapsed += time.perf_counter() - t0
+        calls += 1
+    return {"value": round(calls * T / elapsed, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"1 OLMoE-shaped layer (d=2048, E=64, top-8, I=1024) at T={T}, {len(used)} distinct "
+                      f"experts, run {calls} times in {elapsed:.1f} s (float64 numpy oracle; expert "
+                      "dequantisation done beforehand, untimed)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the multi-GPU sharding is described, not built)", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    import torch
+    import synth
+    wl = synth.OLMOE_DECODE
+    s = wl.shape
+    Ts = sorted({args.tokens} | {int(t) for t in args.sweep.split(",") if t})
+    dec = Decoder(wl, max(Ts), "cuda")
+    head = run_decode(dec, args.tokens, args.steps, args.warmup, args.x_sets)
+    sweep = {}
+    for T in Ts:
+        if T == args.tokens:
+            continue
+        r = run_decode(dec, T, args.steps, args.warmup, args.x_sets)
+        sweep[f"T={T}"] = {k: r[k] for k in ("tokens_per_s", "hbm_gbps", "ms_per_step", "ms_per_step_eager",
+                                             "mean_distinct_experts")}
+        if "gateup_decode" in r.get("kernels", {}):
+            kt = r["kernels"]["gateup_decode"]["avg_us"]
+            sweep[f"T={T}"]["gateup_gbps"] = r["gateup_bytes_per_launch"] / (kt * 1e-6) / 1e9
+    kern = head["kernels"]["gateup_decode"]
+    achieved = head["gateup_bytes_per_launch"] / (kern["avg_us"] * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "kernel": "k_gateup_decode", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": None, "avg_us": round(kern["avg_us"], 3),
+                "bytes_per_launch": int(head["gateup_bytes_per_launch"])}
+    out = {
+        "metric": METRIC,
+        "value": round(head["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 4),
+        "ms_per_step_eager": round(head["ms_per_step_eager"], 4),
+        "timing": "value: K steps replayed from HIP graphs (one per activation set); roofline: the same K "
+                  "steps run eagerly with HIP events around each grouped gate/up launch on its stream",
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights, random-init; no trained checkpoint)",
+        "config": {"workload": f"olmoe_decode: 16 MoE layers, d=2048, E=64, top-8, I=1024, SwiGLU, "
+                               f"W4 g128 experts all resident, T={args.tokens} tokens/step",
+                   "tokens_per_step": args.tokens, "layers": wl.layers},
+        "hbm_gbps": round(head["hbm_gbps"], 1),
+        "hbm_frac": round(head["hbm_gbps"] / HBM_PEAK_GBPS, 4),
+        "mean_distinct_experts": round(head["mean_distinct_experts"], 2),
+        "roofline": roofline,
+        "kernels_us": {k: round(v["avg_us"], 3) for k, v in head["kernels"].items()},
+        "decode_sweep": sweep,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, args.tokens, args.cpu_seconds)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -84,7 +84,8 @@ int moe_expert_layout_get(int d, int I, moe_expert_layout* out);
  *  gateup_interleave: 1 = W is [gate; up] (N = 2I); packed row tile 2j holds gate
  *          rows 16j.., tile 2j+1 up rows 16j.. (N % 32 == 0 required).
  *  Errors: MOE_ERR_UNSUPPORTED_SHAPE unless N % 16 == 0 and K % 128 == 0.
- *  The result is bit-identical to the reference quantiser.
+ *  Deterministic; bit-identical to the definition above (fp32 quotients are exact
+ *  enough that every rounding decision equals the exact one).
  */
 int pack_w4_g128(const uint16_t* w, int E, int N, int K, int gateup_interleave,
                  uint8_t* codes, int64_t codes_stride,
@@ -112,10 +113,13 @@ int moe_route(const uint16_t* x, const uint16_t* w_router, int T, int d, int E, 
  *  expert_offsets [E+1] int32: exclusive prefix sum of per-expert pair counts.
  *  sorted_pairs   [T*k] int32: pair ids grouped by expert, increasing within a group.
  *  pair_pos       [T*k] int32: position of pair p in sorted_pairs.
- *  active_experts [E+1] int32: [0] = U (experts with >= 1 pair), [1..U] their ids ascending.
+ *  active_experts [4 + 4E] int32, 16-byte aligned: the work list of the U experts
+ *                 with >= 1 pair.  [0] = U, [1..3] = 0; entry u (ascending expert
+ *                 id) at [4+4u .. 7+4u] = {expert id, expert_offsets[id], pair count, 0}.
  *  tile_offsets   [E+1] int32 or NULL: exclusive prefix sum of ceil(count / block_m)
  *                 (only when block_m > 0).
- *  Limits: E <= 1024, k <= 16, T*k <= 2^24.  Entries of topk_ids must lie in [0, E).
+ *  Limits: E <= 1024, k <= 16, T*k <= 2^24.  Entries of topk_ids outside [0, E)
+ *  are dropped: not counted, not placed, pair_pos = -1 (the combine skips them).
  *  Bit-exact: the output is unique.
  */
 int moe_align(const int32_t* topk_ids, int T, int k, int E, int block_m,
@@ -137,7 +141,7 @@ typedef struct {
   const int32_t* expert_offsets;  /* from moe_align */
   const int32_t* sorted_pairs;
   const int32_t* pair_pos;
-  const int32_t* active_experts;
+  const int32_t* active_experts;  /* work list from moe_align */
   const int32_t* tile_offsets;    /* required for prefill mode with block_m = 128; else may be NULL */
   const uint8_t* bank;            /* expert blobs (moe_expert_layout), device */
   int64_t bank_stride;            /* bytes between blobs */

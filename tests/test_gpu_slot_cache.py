@@ -40,8 +40,7 @@ def run_slot_steps(wl, S, steps, T, seed_layer=0):
         x = xs[st].to(DEV)
         r = moe.moe_route(x, wr, s.k)
         a = moe.moe_align(r.ids, s.E)
-        act = a.active.cpu().numpy()
-        need = set(act[1:1 + act[0]].tolist())
+        need = {w[0] for w in moe.active_experts(a)}
         expect = sim.step(need)
         pending = set(need)
         out = torch.empty((T, s.d), dtype=torch.bfloat16, device=DEV)

@@ -5,7 +5,7 @@ include/w4a16_moe.h); this package is its argument-marshalling binding.  The
 library has to be built in-tree first (``w4a16_grouped_expert_amd._build.build``);
 there is no fallback implementation.
 """
-from .api import (MODE_AUTO, MODE_DECODE, MODE_PREFILL, AlignOut, MoELayer, RouteOut, SlotCache,  # noqa: F401
+from .api import (MODE_AUTO, active_experts, MODE_DECODE, MODE_PREFILL, AlignOut, MoELayer, RouteOut, SlotCache,  # noqa: F401
                   alloc_align, alloc_route, alloc_workspace, expert_layout, ffn_workspace_bytes,
                   moe_align, moe_align_into, moe_route, moe_route_into, moe_w4a16_grouped_ffn,
                   moe_w4a16_grouped_ffn_into, pack_experts, pack_w4_g128, timing_enable, timing_read,

@@ -116,7 +116,7 @@ class AlignOut:
     offsets: torch.Tensor        # [E+1]
     sorted_pairs: torch.Tensor   # [T*k]
     pair_pos: torch.Tensor       # [T*k]
-    active: torch.Tensor         # [E+1]
+    active: torch.Tensor         # [4 + 4E] work list: U, then {expert, first position, count, 0}
     tile_offsets: Optional[torch.Tensor]  # [E+1] or None
     block_m: int = 0
 
@@ -124,7 +124,14 @@ class AlignOut:
 def alloc_align(T: int, k: int, E: int, device, block_m: int = 0) -> AlignOut:
     i32 = dict(dtype=torch.int32, device=device)
     return AlignOut(torch.empty(E + 1, **i32), torch.empty(max(T * k, 1), **i32), torch.empty(max(T * k, 1), **i32),
-                    torch.empty(E + 1, **i32), torch.empty(E + 1, **i32) if block_m > 0 else None, block_m)
+                    torch.empty(4 + 4 * E, **i32), torch.empty(E + 1, **i32) if block_m > 0 else None, block_m)
+
+
+def active_experts(al: AlignOut):
+    """Host copy of the active-expert work list: list of (expert, first position, count)."""
+    w = al.active.cpu()
+    U = int(w[0])
+    return [tuple(int(v) for v in w[4 + 4 * u: 7 + 4 * u]) for u in range(U)]
 
 
 def moe_align_into(ids, E, out: AlignOut, stream=None) -> AlignOut:
@@ -259,6 +266,11 @@ class SlotCache:
 
     def load(self, pending: set, slot_table_dev: torch.Tensor, copy_stream, wait_event, done_event):
         """One round: returns (round experts set, hits, misses)."""
+        # torch creates an event's HIP handle on its first record; make sure both exist
+        if done_event.cuda_event == 0:
+            done_event.record(copy_stream)
+        if wait_event is not None and wait_event.cuda_event == 0:
+            wait_event.record(torch.cuda.current_stream())
         pm = (ctypes.c_uint64 * self.words)()
         for e in pending:
             pm[e >> 6] |= 1 << (e & 63)

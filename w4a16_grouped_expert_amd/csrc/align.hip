@@ -4,8 +4,8 @@
 // Inference", Abstract).  A stable counting sort in one 1024-thread workgroup:
 //
 //  1. histogram of expert ids (LDS atomics; the counts do not depend on order);
-//  2. one block-wide scan gives the offsets, the compacted list of active
-//     experts and the per-expert tile counts together;
+//  2. one block-wide scan gives the offsets, the compacted work list of active
+//     experts ({id, first position, count} each) and the per-expert tile counts;
 //  3. placement, 1024 pairs per pass in pair order: inside a wavefront the lanes
 //     that carry the same expert are found with ballots over the id bits, their
 //     rank is a popcount of the lower lanes; the per-wave counts are exchanged in
@@ -45,7 +45,10 @@ __global__ __launch_bounds__(kAlignThreads) void k_align(const int32_t* __restri
     for (int w = 0; w < kAlignWaves; ++w) s_wcnt[w][e] = 0;
   }
   __syncthreads();
-  for (int p = tid; p < P; p += kAlignThreads) atomicAdd(&s_count[ids[p]], 1);
+  for (int p = tid; p < P; p += kAlignThreads) {
+    const int e = ids[p];
+    if (e >= 0 && e < E) atomicAdd(&s_count[e], 1);
+  }
   __syncthreads();
 
   // block scan over experts (E <= 1024: one expert per thread)
@@ -69,12 +72,17 @@ __global__ __launch_bounds__(kAlignThreads) void k_align(const int32_t* __restri
   if (tid < E) {
     s_off[tid] = ex_c;
     offsets[tid] = ex_c;
-    if (a) active[1 + ex_a] = tid;
+    if (a) {
+      // work item of the active expert: {id, first sorted position, pair count, 0}
+      const i32x4_t item = {tid, ex_c, c, 0};
+      *reinterpret_cast<i32x4_t*>(active + 4 + 4 * ex_a) = item;
+    }
     if (tile_offsets) tile_offsets[tid] = ex_t;
   }
   if (tid == E - 1) {
     offsets[E] = ex_c + c;
-    active[0] = ex_a + a;
+    const i32x4_t head = {ex_a + a, 0, 0, 0};
+    *reinterpret_cast<i32x4_t*>(active) = head;
     if (tile_offsets) tile_offsets[E] = ex_t + tl;
   }
   __syncthreads();
@@ -84,8 +92,10 @@ __global__ __launch_bounds__(kAlignThreads) void k_align(const int32_t* __restri
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int base = 0; base < P; base += kAlignThreads) {
     const int p = base + tid;
-    const bool valid = p < P;
-    const int e = valid ? ids[p] : 0;
+    const int e_in = p < P ? ids[p] : 0;
+    const bool valid = p < P && e_in >= 0 && e_in < E;   // out-of-range ids are dropped
+    const int e = valid ? e_in : 0;
+    if (p < P && !valid) pair_pos[p] = -1;
     uint64_t m = __ballot(valid);
     for (int b = 0; b < id_bits; ++b) {
       const bool bit = (e >> b) & 1;

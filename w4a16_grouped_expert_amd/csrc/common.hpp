@@ -42,10 +42,14 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kGroup = 128;          // quantisation group along K
 constexpr int kTileRows = 16;        // rows per packed tile
 constexpr int kTileBytes = 1024;     // bytes per packed tile (16 x 128 x 4 bit)
+// Word 3 of a raw (unswizzled, stride 0) buffer resource on gfx9: 32-bit data
+// format; offsets at or past num_records read as zero.
+constexpr int kBufferRsrcWord3 = 0x00020000;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
@@ -69,16 +73,28 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t 
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+// A constant the compiler cannot see through, materialised in a VGPR.  gfx9 VOP3
+// encodings take no literal operand, so with visible constants the compiler
+// splits (a & m) | o into v_and + v_or; with m and o in VGPRs it emits one
+// v_and_or_b32 (and still tracks every hazard itself, as it is ordinary code).
+__device__ __forceinline__ uint32_t vgpr_const(uint32_t c) {
+  uint32_t v;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "i"(c));
+  return v;
+}
+
 // One 32-bit word of packed codes (8 elements) -> 8 bf16 values (1 + code/16).
-// Element m's code sits at bit (3 + 4(m/2) + 16(m%2)) mod 32, so rotating right by
-// 4p puts elements 2p and 2p+1 at bits 3..6 and 19..22, i.e. straight into the
-// top mantissa bits of two bf16 values with exponent 0 (0x3F80 = 1.0).
-__device__ __forceinline__ u32x4_t decode_word_biased(uint32_t w) {
+// Element m's code sits at bit (3 + 4(m/2) + 16(m%2)) mod 32, so shifting right by
+// 4p (rotating for p = 3, whose high field wraps to bits 0..2) puts elements 2p and
+// 2p+1 at bits 3..6 and 19..22, i.e. straight into the top mantissa bits of two
+// bf16 values with exponent 0 (0x3F80 = 1.0): seven VALU instructions per word.
+// mask = 0x00780078, one = 0x3F803F80, passed as vgpr_const values by the caller.
+__device__ __forceinline__ u32x4_t decode_word_biased(uint32_t w, uint32_t mask, uint32_t one) {
   u32x4_t r;
-  r[0] = (w & 0x00780078u) | 0x3F803F80u;
-  r[1] = (rotr32(w, 4) & 0x00780078u) | 0x3F803F80u;
-  r[2] = (rotr32(w, 8) & 0x00780078u) | 0x3F803F80u;
-  r[3] = (rotr32(w, 12) & 0x00780078u) | 0x3F803F80u;
+  r[0] = (w & mask) | one;
+  r[1] = ((w >> 4) & mask) | one;
+  r[2] = ((w >> 8) & mask) | one;
+  r[3] = (rotr32(w, 12) & mask) | one;
   return r;
 }
 

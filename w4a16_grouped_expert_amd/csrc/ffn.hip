@@ -21,6 +21,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, in
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < k; ++j) {
     const int64_t pos = pair_pos[t * k + j];
+    if (pos < 0) continue;  // pair dropped by moe_align (expert id out of range)
     const float wj = w[t * k + j];
     f32x4_t v = *reinterpret_cast<const f32x4_t*>(y + pos * d + n);
     for (int s = 1; s < ksplit; ++s) {
@@ -47,7 +48,7 @@ static int resolve_mode(int T, int E, int k, int mode) {
 static int down_ksplit(int T, int d, int I, int E, int k, int mode) {
   if (mode == MOE_MODE_PREFILL) return 1;
   const int64_t umax = std::min<int64_t>(E, (int64_t)T * k);
-  const int64_t blocks = umax * (d / 32);
+  const int64_t blocks = umax * (d / 64);  // down blocks own 64 output rows
   const int max_split = std::max(1, (I / kGroup) / 4);
   int ks = 1;
   while (ks * 2 <= max_split && blocks * ks < 2048) ks *= 2;
@@ -104,6 +105,7 @@ extern "C" int moe_w4a16_grouped_ffn(const moe_ffn_args* a, void* stream) {
                 "moe_w4a16_grouped_ffn: bank must be 256-byte aligned with stride >= %lld (multiple of 256), got %lld",
                 (long long)lay.blob_bytes, (long long)a->bank_stride);
   MOE_CHECK_ARG(((uintptr_t)a->x % 16) == 0 && ((uintptr_t)a->workspace % 256) == 0 &&
+                    ((uintptr_t)a->active_experts % 16) == 0 &&
                     (!a->out || ((uintptr_t)a->out % 8) == 0),
                 MOE_ERR_INVALID_ARG, "moe_w4a16_grouped_ffn: misaligned x, out or workspace");
   const int mode = resolve_mode(a->T, a->E, a->k, a->mode);
@@ -121,6 +123,7 @@ extern "C" int moe_w4a16_grouped_ffn(const moe_ffn_args* a, void* stream) {
   f.k = a->k;
   f.P = (int64_t)a->T * a->k;
   f.umax = (int)std::min<int64_t>(a->E, f.P);
+  f.topk_ids = a->topk_ids;
   f.offsets = a->expert_offsets;
   f.sorted_pairs = a->sorted_pairs;
   f.pair_pos = a->pair_pos;

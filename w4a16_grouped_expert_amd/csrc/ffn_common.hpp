@@ -9,11 +9,12 @@ struct FfnDev {
   const uint16_t* x;  // [T][d] bf16
   int T, d, I, E, k;
   int64_t P;          // T * k
+  const int32_t* topk_ids;  // [T][k]
   int umax;           // upper bound on active experts: min(E, P)
   const int32_t* offsets;
   const int32_t* sorted_pairs;
   const int32_t* pair_pos;
-  const int32_t* active;
+  const int32_t* active;  // work list: [0] = U, entry u at 4 + 4u = {expert, row0, count, 0}
   const int32_t* tile_offsets;
   const uint8_t* bank;
   int64_t bank_stride;

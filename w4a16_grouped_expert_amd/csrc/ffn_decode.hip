@@ -15,273 +15,437 @@
 // scale is applied once per group in fp32, so the arithmetic is that of the
 // dequantised weights q * scale with fp32 accumulation.
 //
-// Work split: a block (4 wavefronts) owns one active expert and one stripe of
-// two packed 16-row tiles (gate/up: the gate and up tiles of 16 output columns,
-// so SwiGLU is applied in the block; down: 32 output rows).  The wavefronts
-// split the expert's K groups; their partial sums meet in LDS in a fixed order.
-// Down may further split K over blocks (partials summed by the combine kernel).
+// Work split: a block (4 wavefronts) owns one active expert and a stripe of RT
+// packed 16-row tiles (gate/up: RT/2 gate+up tile pairs, so SwiGLU is applied
+// in the block; down: RT*16 output rows).  The wavefronts split the expert's K
+// groups; each issues the loads of up to GPW groups x RT tiles at once (8-16 KiB
+// per wavefront in flight) before decoding, then the partial sums meet in LDS in
+// a fixed order.  Down may further split K over blocks (partials summed in a
+// fixed order by the combine kernel).
 #include "ffn_common.hpp"
 
 namespace moe {
 
-template <int NB>
-__global__ __launch_bounds__(256) void k_gateup_decode(FfnDev f, uint16_t* __restrict__ h) {
-  const int n_stripes = f.I / 16;
-  const int u = blockIdx.x / n_stripes;
-  const int stripe = blockIdx.x % n_stripes;
-  if (u >= f.active[0]) return;
-  const int e = f.active[1 + u];
-  const uint8_t* blob = f.blob(e);
-  if (!blob) return;
-  const int row0 = f.offsets[e];
-  const int n_e = f.offsets[e + 1] - row0;
-  const int G = f.d / kGroup;
-  const int wave = threadIdx.x >> 6, lane = lane_id();
+// Decode with at most 16 tokens in the step (so at most 16 pairs per expert):
+// one 16-column MFMA block covers every pair of an expert.
+//
+// Persistent workers.  Every wavefront is an independent worker that walks the
+// work items (active expert u, stripe of RT 16-row tiles, K split) with a stride
+// of the total worker count, so the items in flight at any moment are
+// neighbours and the weight stream sweeps memory in order.  A worker owns the
+// whole K range of its item (no cross-wavefront reduction, no barrier) and runs
+// a two-stage software pipeline over the groups: group j+1's weights (RT tiles),
+// scales and activation fragments are in flight while group j is decoded and
+// multiplied.  The work item {expert, first position, count} of the next item is
+// fetched while the current one streams.
+// DENSE (gate/up): the 16 MFMA columns are the step's tokens themselves, so the
+// activation addresses need no permutation lookup; columns whose token is not
+// routed to the expert read zeros (buffer loads past the end) and store nothing,
+// and the SwiGLU row of a routed token goes to its expert-sorted position
+// row0 + (rank of the token among the expert's tokens), which is where the
+// stable permutation puts it.
+template <int RT>
+struct GroupBuf {
+  u32x4_t c[RT];  // packed codes, one 16-byte slice per tile
+  u32x2_t s[RT];  // four bf16 scales per tile (the lane's C rows)
+  u32x4_t x[4];   // activation fragments, one per 32-wide K step
+};
+
+template <int RT, int NG, bool GATEUP, bool DENSE>
+__global__ __launch_bounds__(256) void k_decode_persist(FfnDev f, const uint16_t* __restrict__ hin,
+                                                        uint16_t* __restrict__ hout, float* __restrict__ y,
+                                                        int ksplit) {
+  const int K = GATEUP ? f.d : f.I;
+  const int N = GATEUP ? 2 * f.I : f.d;
+  const int G = K / kGroup;
+  const int n_stripes = N / (kTileRows * RT);
+  const int per_u = n_stripes * ksplit;
+  const int n_items = f.umax * per_u;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = lane_id();
   const int col = lane & 15, kq = lane >> 4;
-  const int g_per = (G + 3) / 4;
-  const int g0 = min(G, wave * g_per), g1 = min(G, g0 + g_per);
+  const int worker = blockIdx.x * 4 + wave, n_workers = gridDim.x * 4;
+  const int U = f.active[0];
+  const int gs_per = (G + ksplit - 1) / ksplit;
 
-  const uint8_t* codes_g = blob + f.off_w13_codes + (int64_t)(2 * stripe) * G * kTileBytes + 16 * lane;
-  const uint8_t* codes_u = codes_g + (int64_t)G * kTileBytes;
-  const uint16_t* sc = reinterpret_cast<const uint16_t*>(blob + f.off_w13_scales);
-  const uint16_t* sc_g = sc + (int64_t)(2 * stripe) * G * kTileRows + 4 * kq;
-  const uint16_t* sc_u = sc_g + (int64_t)G * kTileRows;
-  const u32x4_t ones_w = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-  const bf16x8_t ones = as_bf16x8(ones_w);
-
-  __shared__ float red[4][2][NB][4][64];
-
-  for (int tb0 = 0; tb0 < n_e; tb0 += 16 * NB) {
-    const uint16_t* arow[NB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int c = tb0 + 16 * b + col;
-      arow[b] = (c < n_e) ? f.x + (int64_t)(f.sorted_pairs[row0 + c] / f.k) * f.d + 8 * kq : nullptr;
-    }
-    f32x4_t tg[NB], tu[NB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      tg[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      tu[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-    for (int g = g0; g < g1; ++g) {
-      const u32x4_t cg = *reinterpret_cast<const u32x4_t*>(codes_g + (int64_t)g * kTileBytes);
-      const u32x4_t cu = *reinterpret_cast<const u32x4_t*>(codes_u + (int64_t)g * kTileBytes);
-      const u32x2_t sg = *reinterpret_cast<const u32x2_t*>(sc_g + g * kTileRows);
-      const u32x2_t su = *reinterpret_cast<const u32x2_t*>(sc_u + g * kTileRows);
-      u32x4_t xb[NB][4];
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          xb[b][i] = arow[b] ? *reinterpret_cast<const u32x4_t*>(arow[b] + g * kGroup + 32 * i)
-                             : u32x4_t{0u, 0u, 0u, 0u};
-      f32x4_t ag[NB], au[NB], as[NB];
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        ag[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        au[b] = ag[b];
-        as[b] = ag[b];
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bf16x8_t wg = as_bf16x8(decode_word_biased(cg[i]));
-        const bf16x8_t wu = as_bf16x8(decode_word_biased(cu[i]));
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          const bf16x8_t xv = as_bf16x8(xb[b][i]);
-          ag[b] = mfma16x16x32(wg, xv, ag[b]);
-          au[b] = mfma16x16x32(wu, xv, au[b]);
-          as[b] = mfma16x16x32(ones, xv, as[b]);
-        }
-      }
-      const float sgr[4] = {bf16_bits_to_f32(sg[0] & 0xFFFFu), bf16_bits_to_f32(sg[0] >> 16),
-                            bf16_bits_to_f32(sg[1] & 0xFFFFu), bf16_bits_to_f32(sg[1] >> 16)};
-      const float sur[4] = {bf16_bits_to_f32(su[0] & 0xFFFFu), bf16_bits_to_f32(su[0] >> 16),
-                            bf16_bits_to_f32(su[1] & 0xFFFFu), bf16_bits_to_f32(su[1] >> 16)};
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float xs = 24.f * as[b][r];
-          tg[b][r] = fmaf(sgr[r], fmaf(16.f, ag[b][r], -xs), tg[b][r]);
-          tu[b][r] = fmaf(sur[r], fmaf(16.f, au[b][r], -xs), tu[b][r]);
-        }
-    }
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        red[wave][0][b][r][lane] = tg[b][r];
-        red[wave][1][b][r][lane] = tu[b][r];
-      }
-    __syncthreads();
-    if (wave < NB) {
-      const int b = wave;
-      const int c = tb0 + 16 * b + col;
-      uint32_t hv[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float gsum = 0.f, usum = 0.f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          gsum += red[w][0][b][r][lane];
-          usum += red[w][1][b][r][lane];
-        }
-        hv[r] = f32_to_bf16_bits(silu_f32(gsum) * usum);
-      }
-      if (c < n_e) {
-        u32x2_t o = {hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16)};
-        *reinterpret_cast<u32x2_t*>(h + (int64_t)(row0 + c) * f.I + 16 * stripe + 4 * kq) = o;
-      }
+  // DENSE: the step's routing table (token -> its k experts) staged once in LDS
+  __shared__ int s_ids[16][MOE_MAX_TOPK];
+  if (DENSE) {
+    for (int i = threadIdx.x; i < 16 * MOE_MAX_TOPK; i += 256) {
+      const int t = i / MOE_MAX_TOPK, j = i % MOE_MAX_TOPK;
+      s_ids[t][j] = (j < f.k && t < f.T) ? f.topk_ids[t * f.k + j] : -1;
     }
     __syncthreads();
   }
+  const uint32_t kMask = vgpr_const(0x00780078u), kOne = vgpr_const(0x3F803F80u);
+  const u32x4_t ones_w = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  const bf16x8_t ones = as_bf16x8(ones_w);
+  const uint32_t kNoRow = 0x7F000000u;
+  const __amdgpu_buffer_rsrc_t xres =
+      GATEUP ? __builtin_amdgcn_make_buffer_rsrc((void*)f.x, (short)0, (int)(f.T * f.d * 2), kBufferRsrcWord3)
+             : __builtin_amdgcn_make_buffer_rsrc((void*)hin, (short)0, (int)(f.P * f.I * 2), kBufferRsrcWord3);
+  const i32x4_t* work = reinterpret_cast<const i32x4_t*>(f.active + 4);
+
+  int item = worker;
+  i32x4_t next_w = work[min(item / per_u, f.umax - 1)];
+  for (; item < n_items; item += n_workers) {
+    const int u = item / per_u;
+    const int rem = item % per_u;
+    const int stripe = rem / ksplit, split = rem % ksplit;
+    const i32x4_t w4 = next_w;
+    next_w = work[min((item + n_workers) / per_u, f.umax - 1)];  // next item's record, in flight now
+    if (u >= U) break;  // items are visited in increasing u: nothing active remains
+    const int e = w4[0], row0 = w4[1], n_e = w4[2];
+    const uint8_t* blob = f.blob(e);
+    if (!blob) continue;
+    const int g0 = min(G, split * gs_per), g1 = min(G, g0 + gs_per);
+
+    const uint8_t* codes = blob + (GATEUP ? f.off_w13_codes : f.off_w2_codes) +
+                           (int64_t)(RT * stripe) * G * kTileBytes + 16 * lane;
+    const uint16_t* scales =
+        reinterpret_cast<const uint16_t*>(blob + (GATEUP ? f.off_w13_scales : f.off_w2_scales)) +
+        (int64_t)(RT * stripe) * G * kTileRows + 4 * kq;
+    const int64_t tile_stride_c = (int64_t)G * kTileBytes;
+    const int64_t tile_stride_s = (int64_t)G * kTileRows;
+
+    int out_row;
+    bool valid;
+    uint32_t xoff;
+    if (DENSE) {
+      bool routed = false;
+      for (int j = 0; j < f.k; ++j) routed |= (s_ids[col][j] == e);
+      const uint32_t colmask = (uint32_t)__ballot(routed) & 0xFFFFu;
+      valid = routed;
+      out_row = row0 + __popc(colmask & ((1u << col) - 1u));
+      xoff = routed ? (uint32_t)(col * f.d + 8 * kq) * 2u : kNoRow;
+    } else {
+      valid = col < n_e;
+      out_row = row0 + col;
+      xoff = !valid ? kNoRow
+                    : (GATEUP ? (uint32_t)((f.sorted_pairs[row0 + col] / f.k) * f.d + 8 * kq) * 2u
+                              : (uint32_t)((row0 + col) * f.I + 8 * kq) * 2u);
+    }
+
+    f32x4_t tot[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) tot[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // Group g's loads; past the item's last group the reads repeat an in-range
+    // group and the group's weight (gv) is 0, so no load or compute sits under a
+    // branch and the compiler can count exactly which loads to wait for.
+    auto load = [&](GroupBuf<RT>& b, int g) {
+      const int gl = min(g, G - 1);
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        b.c[r] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4_t*>(codes + r * tile_stride_c + (int64_t)gl * kTileBytes));
+        b.s[r] = *reinterpret_cast<const u32x2_t*>(scales + r * tile_stride_s + gl * kTileRows);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        b.x[i] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xres, xoff + (uint32_t)(gl * kGroup + 32 * i) * 2u, 0, 0));
+    };
+    auto compute = [&](const GroupBuf<RT>& b, float gv) {
+      f32x4_t acc[RT], as = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int r = 0; r < RT; ++r) acc[r] = as;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x8_t xv = as_bf16x8(b.x[i]);
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+          acc[r] = mfma16x16x32(as_bf16x8(decode_word_biased(b.c[r][i], kMask, kOne)), xv, acc[r]);
+        as = mfma16x16x32(ones, xv, as);
+      }
+      float xs[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) xs[q] = -24.f * as[q];
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        const float s4[4] = {__uint_as_float(b.s[r][0] << 16), __uint_as_float(b.s[r][0] & 0xFFFF0000u),
+                             __uint_as_float(b.s[r][1] << 16), __uint_as_float(b.s[r][1] & 0xFFFF0000u)};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) tot[r][q] = fmaf(gv * s4[q], fmaf(16.f, acc[r][q], xs[q]), tot[r][q]);
+      }
+    };
+
+    GroupBuf<RT> buf[2];
+    for (int gc = g0; gc < g1; gc += NG) {
+      load(buf[0], gc);
+#pragma unroll
+      for (int j = 0; j < NG; ++j) {
+        if (j + 1 < NG) load(buf[(j + 1) & 1], gc + j + 1);
+        compute(buf[j & 1], (gc + j < g1) ? 1.f : 0.f);
+      }
+    }
+
+    if (GATEUP) {
+#pragma unroll
+      for (int p = 0; p < RT / 2; ++p) {
+        uint32_t hv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) hv[q] = f32_to_bf16_bits(silu_f32(tot[2 * p][q]) * tot[2 * p + 1][q]);
+        if (valid) {
+          const int hcol = kTileRows * ((RT / 2) * stripe + p) + 4 * kq;
+          u32x2_t o = {hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16)};
+          *reinterpret_cast<u32x2_t*>(hout + (int64_t)out_row * f.I + hcol) = o;
+        }
+      }
+    } else {
+      float* yout = y + (int64_t)split * f.P * f.d;
+      if (valid) {
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+          const int n = kTileRows * (RT * stripe + r) + 4 * kq;
+          *reinterpret_cast<f32x4_t*>(yout + (int64_t)out_row * f.d + n) = tot[r];
+        }
+      }
+    }
+  }
 }
 
-template <int NB>
-__global__ __launch_bounds__(256) void k_down_decode(FfnDev f, const uint16_t* __restrict__ h, float* __restrict__ y,
-                                                     int ksplit) {
-  const int n_stripes = f.d / 32;
+template <int NB, int RT, int GPW, bool GATEUP>
+__global__ __launch_bounds__(256) void k_ffn_decode(FfnDev f, const uint16_t* __restrict__ hin,
+                                                    uint16_t* __restrict__ hout, float* __restrict__ y, int ksplit) {
+  const int K = GATEUP ? f.d : f.I;
+  const int N = GATEUP ? 2 * f.I : f.d;
+  const int G = K / kGroup;
+  const int n_stripes = N / (kTileRows * RT);
   const int per_u = n_stripes * ksplit;
   const int u = blockIdx.x / per_u;
   const int rem = blockIdx.x % per_u;
   const int stripe = rem / ksplit, split = rem % ksplit;
-  if (u >= f.active[0]) return;
-  const int e = f.active[1 + u];
+  // both loads issued together: one round trip before the weight stream starts
+  const int U = f.active[0];
+  const i32x4_t item = reinterpret_cast<const i32x4_t*>(f.active + 4)[u];  // u < min(E, T*k): in bounds
+  if (u >= U) return;
+  const int e = item[0], row0 = item[1], n_e = item[2];
   const uint8_t* blob = f.blob(e);
   if (!blob) return;
-  const int row0 = f.offsets[e];
-  const int n_e = f.offsets[e + 1] - row0;
-  const int G = f.I / kGroup;
-  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = lane_id();
   const int col = lane & 15, kq = lane >> 4;
-  // groups of this block, then of this wavefront
   const int gs_per = (G + ksplit - 1) / ksplit;
   const int gs0 = min(G, split * gs_per), gs1 = min(G, gs0 + gs_per);
-  const int g_per = (gs1 - gs0 + 3) / 4;
-  const int g0 = min(gs1, gs0 + wave * g_per), g1 = min(gs1, g0 + g_per);
+  const int gw_per = (gs1 - gs0 + 3) / 4;
+  const int g0 = min(gs1, gs0 + wave * gw_per), g1 = min(gs1, g0 + gw_per);
 
-  const uint8_t* codes0 = blob + f.off_w2_codes + (int64_t)(2 * stripe) * G * kTileBytes + 16 * lane;
-  const uint8_t* codes1 = codes0 + (int64_t)G * kTileBytes;
-  const uint16_t* sc = reinterpret_cast<const uint16_t*>(blob + f.off_w2_scales);
-  const uint16_t* sc0 = sc + (int64_t)(2 * stripe) * G * kTileRows + 4 * kq;
-  const uint16_t* sc1 = sc0 + (int64_t)G * kTileRows;
+  const uint8_t* codes = blob + (GATEUP ? f.off_w13_codes : f.off_w2_codes) +
+                         (int64_t)(RT * stripe) * G * kTileBytes + 16 * lane;
+  const uint16_t* scales = reinterpret_cast<const uint16_t*>(blob + (GATEUP ? f.off_w13_scales : f.off_w2_scales)) +
+                           (int64_t)(RT * stripe) * G * kTileRows + 4 * kq;
+  const int64_t tile_stride_c = (int64_t)G * kTileBytes;  // bytes between row tiles
+  const int64_t tile_stride_s = (int64_t)G * kTileRows;   // scales between row tiles
   const u32x4_t ones_w = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   const bf16x8_t ones = as_bf16x8(ones_w);
-  float* yout = y + (int64_t)split * f.P * f.d;
 
-  __shared__ float red[4][2][NB][4][64];
+  u32x4_t cw[GPW][RT];
+  u32x2_t sw[GPW][RT];
+  auto load_chunk = [&](int gc) {
+#pragma unroll
+    for (int gi = 0; gi < GPW; ++gi) {
+      const int g = gc + gi;
+      if (g < g1) {
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+          cw[gi][r] = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4_t*>(codes + r * tile_stride_c + (int64_t)g * kTileBytes));
+          sw[gi][r] = *reinterpret_cast<const u32x2_t*>(scales + r * tile_stride_s + g * kTileRows);
+        }
+      }
+    }
+  };
+  load_chunk(g0);
+
+  __shared__ float red[4][RT][NB][4][64];
 
   for (int tb0 = 0; tb0 < n_e; tb0 += 16 * NB) {
     const uint16_t* arow[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const int c = tb0 + 16 * b + col;
-      arow[b] = (c < n_e) ? h + (int64_t)(row0 + c) * f.I + 8 * kq : nullptr;
+      if (c < n_e) {
+        arow[b] = GATEUP ? f.x + (int64_t)(f.sorted_pairs[row0 + c] / f.k) * f.d + 8 * kq
+                         : hin + (int64_t)(row0 + c) * f.I + 8 * kq;
+      } else {
+        arow[b] = nullptr;
+      }
     }
-    f32x4_t t0[NB], t1[NB];
+    f32x4_t tot[RT][NB];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      t0[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      t1[b] = t0[b];
-    }
-    for (int g = g0; g < g1; ++g) {
-      const u32x4_t c0 = *reinterpret_cast<const u32x4_t*>(codes0 + (int64_t)g * kTileBytes);
-      const u32x4_t c1 = *reinterpret_cast<const u32x4_t*>(codes1 + (int64_t)g * kTileBytes);
-      const u32x2_t s0 = *reinterpret_cast<const u32x2_t*>(sc0 + g * kTileRows);
-      const u32x2_t s1 = *reinterpret_cast<const u32x2_t*>(sc1 + g * kTileRows);
-      u32x4_t xb[NB][4];
+    for (int r = 0; r < RT; ++r)
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
+      for (int b = 0; b < NB; ++b) tot[r][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    for (int gc = g0; gc < g1; gc += GPW) {
+      if (gc != g0 || tb0 != 0) load_chunk(gc);
+      // activation fragments: with one token block the whole chunk's are issued
+      // together (they come from L2); with more blocks, group by group (registers)
+      constexpr int XG = (NB == 1) ? GPW : 1;
+      u32x4_t xb[XG][NB][4];
+      auto load_x = [&](int slot, int g) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          xb[b][i] = arow[b] ? *reinterpret_cast<const u32x4_t*>(arow[b] + g * kGroup + 32 * i)
-                             : u32x4_t{0u, 0u, 0u, 0u};
-      f32x4_t a0[NB], a1[NB], as[NB];
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        a0[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        a1[b] = a0[b];
-        as[b] = a0[b];
+          for (int i = 0; i < 4; ++i)
+            xb[slot][b][i] = (arow[b] && g < g1)
+                                 ? *reinterpret_cast<const u32x4_t*>(arow[b] + g * kGroup + 32 * i)
+                                 : u32x4_t{0u, 0u, 0u, 0u};
+      };
+      if constexpr (XG == GPW) {
+#pragma unroll
+        for (int gi = 0; gi < GPW; ++gi) load_x(gi, gc + gi);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bf16x8_t w0 = as_bf16x8(decode_word_biased(c0[i]));
-        const bf16x8_t w1 = as_bf16x8(decode_word_biased(c1[i]));
+      for (int gi = 0; gi < GPW; ++gi) {
+        if (gc + gi >= g1) break;
+        const int xs = (XG == GPW) ? gi : 0;
+        if constexpr (XG != GPW) load_x(0, gc + gi);
+        f32x4_t acc[RT][NB], as[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-          const bf16x8_t xv = as_bf16x8(xb[b][i]);
-          a0[b] = mfma16x16x32(w0, xv, a0[b]);
-          a1[b] = mfma16x16x32(w1, xv, a1[b]);
-          as[b] = mfma16x16x32(ones, xv, as[b]);
+          as[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int r = 0; r < RT; ++r) acc[r][b] = as[b];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+          for (int r = 0; r < RT; ++r) {
+            const bf16x8_t w = as_bf16x8(decode_word_biased(cw[gi][r][i], 0x00780078u, 0x3F803F80u));
+#pragma unroll
+            for (int b = 0; b < NB; ++b) acc[r][b] = mfma16x16x32(w, as_bf16x8(xb[xs][b][i]), acc[r][b]);
+          }
+#pragma unroll
+          for (int b = 0; b < NB; ++b) as[b] = mfma16x16x32(ones, as_bf16x8(xb[xs][b][i]), as[b]);
+        }
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+          const float s4[4] = {bf16_bits_to_f32(sw[gi][r][0] & 0xFFFFu), bf16_bits_to_f32(sw[gi][r][0] >> 16),
+                               bf16_bits_to_f32(sw[gi][r][1] & 0xFFFFu), bf16_bits_to_f32(sw[gi][r][1] >> 16)};
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              tot[r][b][q] = fmaf(s4[q], fmaf(16.f, acc[r][b][q], -24.f * as[b][q]), tot[r][b][q]);
         }
       }
-      const float s0r[4] = {bf16_bits_to_f32(s0[0] & 0xFFFFu), bf16_bits_to_f32(s0[0] >> 16),
-                            bf16_bits_to_f32(s0[1] & 0xFFFFu), bf16_bits_to_f32(s0[1] >> 16)};
-      const float s1r[4] = {bf16_bits_to_f32(s1[0] & 0xFFFFu), bf16_bits_to_f32(s1[0] >> 16),
-                            bf16_bits_to_f32(s1[1] & 0xFFFFu), bf16_bits_to_f32(s1[1] >> 16)};
+    }
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float xs = 24.f * as[b][r];
-          t0[b][r] = fmaf(s0r[r], fmaf(16.f, a0[b][r], -xs), t0[b][r]);
-          t1[b][r] = fmaf(s1r[r], fmaf(16.f, a1[b][r], -xs), t1[b][r]);
-        }
-    }
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        red[wave][0][b][r][lane] = t0[b][r];
-        red[wave][1][b][r][lane] = t1[b][r];
-      }
+        for (int q = 0; q < 4; ++q) red[wave][r][b][q][lane] = tot[r][b][q];
     __syncthreads();
-    if (wave < NB) {
-      const int b = wave;
-      const int c = tb0 + 16 * b + col;
-      f32x4_t o0, o1;
+    if (GATEUP) {
+      for (int combo = wave; combo < (RT / 2) * NB; combo += 4) {
+        const int p = combo / NB, b = combo % NB;
+        const int c = tb0 + 16 * b + col;
+        uint32_t hv[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float v0 = 0.f, v1 = 0.f;
+        for (int q = 0; q < 4; ++q) {
+          float gsum = 0.f, usum = 0.f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          v0 += red[w][0][b][r][lane];
-          v1 += red[w][1][b][r][lane];
+          for (int w = 0; w < 4; ++w) {
+            gsum += red[w][2 * p][b][q][lane];
+            usum += red[w][2 * p + 1][b][q][lane];
+          }
+          hv[q] = f32_to_bf16_bits(silu_f32(gsum) * usum);
         }
-        o0[r] = v0;
-        o1[r] = v1;
+        if (c < n_e) {
+          const int hcol = kTileRows * ((RT / 2) * stripe + p) + 4 * kq;
+          u32x2_t o = {hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16)};
+          *reinterpret_cast<u32x2_t*>(hout + (int64_t)(row0 + c) * f.I + hcol) = o;
+        }
       }
-      if (c < n_e) {
-        float* dst = yout + (int64_t)(row0 + c) * f.d + 32 * stripe + 4 * kq;
-        *reinterpret_cast<f32x4_t*>(dst) = o0;
-        *reinterpret_cast<f32x4_t*>(dst + 16) = o1;
+    } else {
+      float* yout = y + (int64_t)split * f.P * f.d;
+      for (int combo = wave; combo < RT * NB; combo += 4) {
+        const int r = combo / NB, b = combo % NB;
+        const int c = tb0 + 16 * b + col;
+        f32x4_t o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float v = 0.f;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) v += red[w][r][b][q][lane];
+          o[q] = v;
+        }
+        if (c < n_e) {
+          const int n = kTileRows * (RT * stripe + r) + 4 * kq;
+          *reinterpret_cast<f32x4_t*>(yout + (int64_t)(row0 + c) * f.d + n) = o;
+        }
       }
     }
     __syncthreads();
   }
 }
 
+constexpr int kGateUpRT = 2, kDownRT = 4;
+constexpr int kPersistRT = 4, kPersistNG = 8;
+
+int decode_down_gpw(int I, int ksplit) {
+  const int G = I / kGroup;
+  const int gs_per = (G + ksplit - 1) / ksplit;
+  return (gs_per + 3) / 4 <= 2 ? 2 : 4;
+}
+
+// Resident 256-thread blocks per CU for a kernel, times the CU count (cached).
+template <typename Kern>
+static int persistent_grid(Kern kern, int slot) {
+  static int cached[8] = {0};
+  if (!cached[slot]) {
+    int dev = 0, cus = 0, per_cu = 0;
+    (void)hipGetDevice(&dev);
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, 0);
+    cached[slot] = std::max(1, cus) * std::max(1, per_cu);
+  }
+  return cached[slot];
+}
+
+template <int NB>
+static void launch_nb(const FfnDev& f, uint16_t* h, float* y, int ksplit, hipStream_t s, int64_t grid_gu,
+                      int64_t grid_dn, int gpw_dn) {
+  timing_begin(K_GATEUP_DECODE, s);
+  hipLaunchKernelGGL((k_ffn_decode<NB, kGateUpRT, 4, true>), dim3((unsigned)grid_gu), dim3(256), 0, s, f,
+                     (const uint16_t*)nullptr, h, (float*)nullptr, 1);
+  timing_end(K_GATEUP_DECODE, s);
+  timing_begin(K_DOWN_DECODE, s);
+  if (gpw_dn == 2)
+    hipLaunchKernelGGL((k_ffn_decode<NB, kDownRT, 2, false>), dim3((unsigned)grid_dn), dim3(256), 0, s, f,
+                       (const uint16_t*)h, (uint16_t*)nullptr, y, ksplit);
+  else
+    hipLaunchKernelGGL((k_ffn_decode<NB, kDownRT, 4, false>), dim3((unsigned)grid_dn), dim3(256), 0, s, f,
+                       (const uint16_t*)h, (uint16_t*)nullptr, y, ksplit);
+  timing_end(K_DOWN_DECODE, s);
+}
+
 int launch_decode(const FfnDev& f, uint16_t* h, float* y, int ksplit, int nb, hipStream_t s) {
   const int64_t umax = f.umax;
-  const int64_t grid_gu = umax * (f.I / 16);
-  const int64_t grid_dn = umax * (f.d / 32) * ksplit;
-  timing_begin(K_GATEUP_DECODE, s);
+  if (f.T <= 16) {
+    auto kgu = k_decode_persist<kPersistRT, kPersistNG, true, true>;
+    auto kdn = k_decode_persist<kPersistRT, kPersistNG, false, false>;
+    const int64_t items_gu = umax * (2 * f.I / (kTileRows * kPersistRT));
+    const int64_t items_dn = umax * (f.d / (kTileRows * kPersistRT)) * ksplit;
+    const int64_t grid_gu = std::min<int64_t>(persistent_grid(kgu, 0), ceil_div(items_gu, 4));
+    const int64_t grid_dn = std::min<int64_t>(persistent_grid(kdn, 1), ceil_div(items_dn, 4));
+    timing_begin(K_GATEUP_DECODE, s);
+    hipLaunchKernelGGL(kgu, dim3((unsigned)grid_gu), dim3(256), 0, s, f, (const uint16_t*)nullptr, h, (float*)nullptr, 1);
+    timing_end(K_GATEUP_DECODE, s);
+    timing_begin(K_DOWN_DECODE, s);
+    hipLaunchKernelGGL(kdn, dim3((unsigned)grid_dn), dim3(256), 0, s, f, (const uint16_t*)h, (uint16_t*)nullptr, y, ksplit);
+    timing_end(K_DOWN_DECODE, s);
+    return check_launch("grouped expert FFN (decode, T <= 16)");
+  }
+  const int64_t grid_gu = umax * (2 * f.I / (kTileRows * kGateUpRT));
+  const int64_t grid_dn = umax * (f.d / (kTileRows * kDownRT)) * ksplit;
+  const int gpw_dn = decode_down_gpw(f.I, ksplit);
   if (nb <= 1)
-    hipLaunchKernelGGL(k_gateup_decode<1>, dim3((unsigned)grid_gu), dim3(256), 0, s, f, h);
+    launch_nb<1>(f, h, y, ksplit, s, grid_gu, grid_dn, gpw_dn);
   else
-    hipLaunchKernelGGL(k_gateup_decode<2>, dim3((unsigned)grid_gu), dim3(256), 0, s, f, h);
-  timing_end(K_GATEUP_DECODE, s);
-  int rc = check_launch("grouped gate/up (decode)");
-  if (rc) return rc;
-  timing_begin(K_DOWN_DECODE, s);
-  if (nb <= 1)
-    hipLaunchKernelGGL(k_down_decode<1>, dim3((unsigned)grid_dn), dim3(256), 0, s, f, h, y, ksplit);
-  else
-    hipLaunchKernelGGL(k_down_decode<2>, dim3((unsigned)grid_dn), dim3(256), 0, s, f, h, y, ksplit);
-  timing_end(K_DOWN_DECODE, s);
-  return check_launch("grouped down (decode)");
+    launch_nb<2>(f, h, y, ksplit, s, grid_gu, grid_dn, gpw_dn);
+  return check_launch("grouped expert FFN (decode)");
 }
 
 }  // namespace moe

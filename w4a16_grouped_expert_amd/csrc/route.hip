@@ -2,100 +2,45 @@
 // "Every Expert Counts: ExactMoE for Memory-Efficient W4A16 Inference",
 // Abstract: the router stays BF16 and the top-k routing procedure is unchanged).
 //
-// Logits: products of bf16 values are exact, and the sum is kept in float64 so
-// that the float32 logit is (to within one rounding of a float64 sum) the
-// correctly rounded dot product; on MI355X an fp64 FMA issues at the same rate
-// as a non-packed fp32 FMA, so the exactness costs nothing here.  A block of
-// four wavefronts covers TB tokens x 16 experts; each wavefront owns four
-// experts and its lanes stride through d in 16-byte chunks.
-//
-// Top-k: one wavefront per token holds the E logits in registers (lane l owns
-// experts l, l+64, ...) and extracts the k largest with a wave-wide (value desc,
-// index asc) argmax per step, then forms the softmax weights in float32.
+// One kernel per call.  Logits: products of bf16 values are exact; they are
+// summed in float64 and rounded once to float32 (on MI355X a non-packed fp64 FMA
+// issues at the fp32 rate, so the near-exact sum costs nothing extra).  The
+// selection orders by (logit desc, index asc); softmax weights in float32.
+// Two launch shapes: one 1024-thread block per token for small T (latency), and
+// blocks of TB tokens x all experts for large T (router weights reused across
+// the TB tokens).
 #include "common.hpp"
 
 namespace moe {
 
-template <int TB>
-__global__ __launch_bounds__(256) void k_route_logits(const uint16_t* __restrict__ x,
-                                                      const uint16_t* __restrict__ wr, int T, int d, int E,
-                                                      float* __restrict__ logits) {
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
-  const int t0 = blockIdx.x * TB;
-  const int e0 = blockIdx.y * 16 + wave * 4;
-  const int nch = d / 8;
-  double acc[TB][4];
-#pragma unroll
-  for (int a = 0; a < TB; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
+constexpr int kRouteMaxTB = 4;
 
-  for (int ch = lane; ch < nch; ch += 64) {
-    double xv[TB][8];
-#pragma unroll
-    for (int a = 0; a < TB; ++a) {
-      const int t = t0 + a;
-      u32x4_t q = {0, 0, 0, 0};
-      if (t < T) q = *reinterpret_cast<const u32x4_t*>(x + (int64_t)t * d + 8 * ch);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        xv[a][2 * j] = (double)bf16_bits_to_f32(q[j] & 0xFFFFu);
-        xv[a][2 * j + 1] = (double)bf16_bits_to_f32(q[j] >> 16);
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int e = e0 + b;
-      u32x4_t q = {0, 0, 0, 0};
-      if (e < E) q = *reinterpret_cast<const u32x4_t*>(wr + (int64_t)e * d + 8 * ch);
-      double wv[8];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        wv[2 * j] = (double)bf16_bits_to_f32(q[j] & 0xFFFFu);
-        wv[2 * j + 1] = (double)bf16_bits_to_f32(q[j] >> 16);
-      }
-#pragma unroll
-      for (int a = 0; a < TB; ++a)
-#pragma unroll
-        for (int m = 0; m < 8; ++m) acc[a][b] = fma(xv[a][m], wv[m], acc[a][b]);
-    }
-  }
-#pragma unroll
-  for (int a = 0; a < TB; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      double v = acc[a][b];
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-      const int t = t0 + a, e = e0 + b;
-      if (lane == 0 && t < T && e < E) logits[(int64_t)t * E + e] = (float)v;
-    }
-}
+__device__ __forceinline__ double bf16_to_f64(uint32_t bits16) { return (double)bf16_bits_to_f32(bits16); }
 
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
-__global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ logits, int T, int E, int k,
-                                                    int renormalize, int32_t* __restrict__ ids,
-                                                    float* __restrict__ weights) {
+// Top-k of one token's E logits (in LDS) by one wavefront: lane l owns experts
+// l, l+64, ...; k rounds of a wave-wide (value desc, index asc) argmax.
+__device__ __forceinline__ void topk_wave(const float* __restrict__ lg, int E, int k, int renormalize, int t,
+                          int32_t* __restrict__ ids, float* __restrict__ weights) {
   const int lane = lane_id();
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
   const int nper = (E + 63) / 64;  // <= 16
   float v[16];
-  uint32_t taken = 0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int e = lane + 64 * i;
-    v[i] = (i < nper && e < E) ? logits[(int64_t)t * E + e] : 0.f;
+    v[i] = (i < nper && e < E) ? lg[e] : -INFINITY;
   }
-  float sel_v[16];
-  int sel_i[16];
+  uint32_t taken = 0;
+  float sel_v[MOE_MAX_TOPK];
+  int sel_i[MOE_MAX_TOPK];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
     if (j >= k) break;
-    float bv = 0.f;
+    // sentinel below every finite logit: a real candidate always wins the reduction
+    float bv = -INFINITY;
     int bi = 0x7FFFFFFF;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -114,6 +59,7 @@ __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ lo
         bi = oi;
       }
     }
+    bi = min(bi, E - 1);  // unreachable for finite logits; keeps ids in range regardless
     sel_v[j] = bv;
     sel_i[j] = bi;
     if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
@@ -122,7 +68,7 @@ __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ lo
   float den = 0.f;
   if (renormalize) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
+    for (int j = 0; j < MOE_MAX_TOPK; ++j)
       if (j < k) den += expf(sel_v[j] - lmax);
   } else {
     float part = 0.f;
@@ -136,12 +82,176 @@ __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ lo
     den = part;
   }
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
     if (j < k && lane == j) {
       ids[(int64_t)t * k + j] = sel_i[j];
       weights[(int64_t)t * k + j] = expf(sel_v[j] - lmax) / den;
     }
   }
+}
+
+// Few tokens: one 1024-thread block per token.  Thread (expert slot el = tid/16,
+// d-lane r = tid%16) accumulates expert eb+el over the 16-byte chunks r, r+16, ...
+// of d, so a wavefront reads four 256-byte runs of four router rows per load and
+// the sixteen partial sums of an expert meet in one 16-lane row (four shuffle
+// steps).  Each thread issues eight chunks of loads before its FMAs.  The top-k
+// is a rank computation: every thread ranks one expert against all E logits in
+// LDS (broadcast reads) and the k winners write themselves.
+constexpr int kRouteBatch = 8;
+
+__global__ __launch_bounds__(1024) void k_route_token(const uint16_t* __restrict__ x,
+                                                      const uint16_t* __restrict__ wr, int T, int d, int E, int k,
+                                                      int renormalize, float* __restrict__ logits,
+                                                      int32_t* __restrict__ ids, float* __restrict__ weights) {
+  __shared__ float s_logit[MOE_MAX_EXPERTS];
+  __shared__ float s_sel_v[MOE_MAX_TOPK];
+  __shared__ int s_sel_i[MOE_MAX_TOPK];
+  __shared__ float s_den;
+  const int tid = threadIdx.x, r = tid & 15, el = tid >> 4;
+  const int t = blockIdx.x;
+  const int nch = d / 8;
+  const uint16_t* xr = x + (int64_t)t * d;
+  for (int eb = 0; eb < E; eb += 64) {
+    const int e = eb + el;
+    double acc = 0.0;
+    for (int c0 = 0; c0 < nch; c0 += 16 * kRouteBatch) {
+      u32x4_t xq[kRouteBatch], wq[kRouteBatch];
+#pragma unroll
+      for (int c = 0; c < kRouteBatch; ++c) {
+        const int ch = c0 + r + 16 * c;
+        xq[c] = ch < nch ? *reinterpret_cast<const u32x4_t*>(xr + 8 * ch) : u32x4_t{0u, 0u, 0u, 0u};
+        wq[c] = (ch < nch && e < E) ? *reinterpret_cast<const u32x4_t*>(wr + (int64_t)e * d + 8 * ch)
+                                    : u32x4_t{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int c = 0; c < kRouteBatch; ++c)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          acc = fma(bf16_to_f64(xq[c][m] & 0xFFFFu), bf16_to_f64(wq[c][m] & 0xFFFFu), acc);
+          acc = fma(bf16_to_f64(xq[c][m] >> 16), bf16_to_f64(wq[c][m] >> 16), acc);
+        }
+    }
+    acc += __shfl_xor(acc, 8);
+    acc += __shfl_xor(acc, 4);
+    acc += __shfl_xor(acc, 2);
+    acc += __shfl_xor(acc, 1);
+    if (r == 0 && e < E) s_logit[e] = (float)acc;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 1024) {
+    const float v = s_logit[e];
+    logits[(int64_t)t * E + e] = v;
+    int rank = 0;
+    for (int o = 0; o < E; ++o) rank += better(s_logit[o], o, v, e) ? 1 : 0;
+    if (rank < k) {
+      s_sel_v[rank] = v;
+      s_sel_i[rank] = e;
+    }
+  }
+  __syncthreads();
+  const float lmax = s_sel_v[0];
+  if (tid < 64) {
+    float part = 0.f;
+    if (renormalize) {
+      if (tid < k) part = expf(s_sel_v[tid] - lmax);
+    } else {
+      for (int e = tid; e < E; e += 64) part += expf(s_logit[e] - lmax);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+    if (tid == 0) s_den = part;
+  }
+  __syncthreads();
+  if (tid < k) {
+    ids[(int64_t)t * k + tid] = s_sel_i[tid];
+    weights[(int64_t)t * k + tid] = expf(s_sel_v[tid] - lmax) / s_den;
+  }
+}
+
+template <int TB>
+__global__ __launch_bounds__(256) void k_route(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+                                               int T, int d, int E, int k, int renormalize,
+                                               float* __restrict__ logits, int32_t* __restrict__ ids,
+                                               float* __restrict__ weights) {
+  __shared__ float s_logit[TB][MOE_MAX_EXPERTS];
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * TB;
+  const int nch = d / 8;
+
+  for (int eb = wave * 8; eb < E; eb += 32) {
+    double acc[TB][8];
+#pragma unroll
+    for (int a = 0; a < TB; ++a)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[a][j] = 0.0;
+    for (int ch = lane; ch < nch; ch += 64) {
+      double xv[TB][8];
+#pragma unroll
+      for (int a = 0; a < TB; ++a) {
+        u32x4_t q = {0u, 0u, 0u, 0u};
+        if (t0 + a < T) q = *reinterpret_cast<const u32x4_t*>(x + (int64_t)(t0 + a) * d + 8 * ch);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          xv[a][2 * m] = bf16_to_f64(q[m] & 0xFFFFu);
+          xv[a][2 * m + 1] = bf16_to_f64(q[m] >> 16);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int e = eb + j;
+        u32x4_t q = {0u, 0u, 0u, 0u};
+        if (e < E) q = *reinterpret_cast<const u32x4_t*>(wr + (int64_t)e * d + 8 * ch);
+        double wv[8];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          wv[2 * m] = bf16_to_f64(q[m] & 0xFFFFu);
+          wv[2 * m + 1] = bf16_to_f64(q[m] >> 16);
+        }
+#pragma unroll
+        for (int a = 0; a < TB; ++a)
+#pragma unroll
+          for (int m = 0; m < 8; ++m) acc[a][j] = fma(xv[a][m], wv[m], acc[a][j]);
+      }
+    }
+    // halving butterfly: after the xor-32/16/8 steps lane l holds the partial sum of
+    // expert j = 4*b5 + 2*b4 + b3 (b = lane bits) over 8 lanes; xor-4/2/1 finish it.
+#pragma unroll
+    for (int a = 0; a < TB; ++a) {
+      const bool h5 = lane & 32, h4 = lane & 16, h3 = lane & 8;
+      double v4[4], v2[2], v1;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const double send = h5 ? acc[a][j] : acc[a][j + 4];
+        const double keep = h5 ? acc[a][j + 4] : acc[a][j];
+        v4[j] = keep + __shfl_xor(send, 32);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const double send = h4 ? v4[j] : v4[j + 2];
+        const double keep = h4 ? v4[j + 2] : v4[j];
+        v2[j] = keep + __shfl_xor(send, 16);
+      }
+      {
+        const double send = h3 ? v2[0] : v2[1];
+        const double keep = h3 ? v2[1] : v2[0];
+        v1 = keep + __shfl_xor(send, 8);
+      }
+      v1 += __shfl_xor(v1, 4);
+      v1 += __shfl_xor(v1, 2);
+      v1 += __shfl_xor(v1, 1);
+      const int j = (h5 ? 4 : 0) + (h4 ? 2 : 0) + (h3 ? 1 : 0);
+      if ((lane & 7) == 0 && eb + j < E) s_logit[a][eb + j] = (float)v1;
+    }
+  }
+  __syncthreads();
+
+  for (int i = threadIdx.x; i < TB * E; i += 256) {
+    const int a = i / E, e = i % E;
+    if (t0 + a < T) logits[(int64_t)(t0 + a) * E + e] = s_logit[a][e];
+  }
+
+  if (wave >= TB || t0 + wave >= T) return;
+  topk_wave(s_logit[wave], E, k, renormalize, t0 + wave, ids, weights);
 }
 
 }  // namespace moe
@@ -162,16 +272,13 @@ extern "C" int moe_route(const uint16_t* x, const uint16_t* w_router, int T, int
                 "moe_route: x and w_router must be 16-byte aligned");
   hipStream_t s = (hipStream_t)stream;
   timing_begin(K_ROUTE, s);
-  if (T <= 64) {
-    hipLaunchKernelGGL(k_route_logits<1>, dim3(T, ceil_div(E, 16)), dim3(256), 0, s, x, w_router, T, d, E, logits);
+  if (T <= 256) {
+    hipLaunchKernelGGL(k_route_token, dim3(T), dim3(1024), 0, s, x, w_router, T, d, E, k, renormalize, logits,
+                       topk_ids, topk_weights);
   } else {
-    hipLaunchKernelGGL(k_route_logits<4>, dim3(ceil_div(T, 4), ceil_div(E, 16)), dim3(256), 0, s, x, w_router, T,
-                       d, E, logits);
+    hipLaunchKernelGGL(k_route<kRouteMaxTB>, dim3((unsigned)ceil_div(T, kRouteMaxTB)), dim3(256), 0, s, x, w_router,
+                       T, d, E, k, renormalize, logits, topk_ids, topk_weights);
   }
-  int rc = check_launch("moe_route (logits)");
-  if (rc) return rc;
-  hipLaunchKernelGGL(k_route_topk, dim3(ceil_div(T, 4)), dim3(256), 0, s, logits, T, E, k, renormalize, topk_ids,
-                     topk_weights);
   timing_end(K_ROUTE, s);
-  return check_launch("moe_route (top-k)");
+  return check_launch("moe_route");
 }

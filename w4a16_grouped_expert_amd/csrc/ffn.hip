@@ -58,7 +58,7 @@ static int down_ksplit(int T, int d, int I, int E, int k, int mode) {
 static int64_t align256(int64_t v) { return (v + 255) / 256 * 256; }
 
 struct WsLayout {
-  int64_t h_off, y_off, total;
+  int64_t h_off, y_off, xsum_off, hsum_off, total;
 };
 
 static WsLayout ws_layout(int T, int d, int I, int E, int k, int mode) {
@@ -67,7 +67,13 @@ static WsLayout ws_layout(int T, int d, int I, int E, int k, int mode) {
   WsLayout L;
   L.h_off = 0;
   L.y_off = align256(P * I * 2);
-  L.total = L.y_off + align256((int64_t)ks * P * d * 4);
+  L.xsum_off = L.y_off + align256((int64_t)ks * P * d * 4);
+  L.hsum_off = L.xsum_off;
+  L.total = L.xsum_off;
+  if (mode == MOE_MODE_PREFILL) {
+    L.hsum_off = L.xsum_off + align256((int64_t)T * (d / kGroup) * 4);
+    L.total = L.hsum_off + align256(P * ((2 * I) / 128) * 4);
+  }
   return L;
 }
 
@@ -146,7 +152,8 @@ extern "C" int moe_w4a16_grouped_ffn(const moe_ffn_args* a, void* stream) {
     const double per_expert = (double)a->T * a->k / a->E;
     rc = launch_decode(f, h, y, ks, per_expert <= 8.0 ? 1 : 2, s);
   } else {
-    rc = launch_prefill(f, h, y, s);
+    rc = launch_prefill(f, h, y, reinterpret_cast<float*>(ws + L.xsum_off), reinterpret_cast<float*>(ws + L.hsum_off),
+                        s);
   }
   if (rc) return rc;
   if (a->combine) {

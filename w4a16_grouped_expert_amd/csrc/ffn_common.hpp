@@ -31,6 +31,7 @@ struct FfnDev {
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
 
 int launch_decode(const FfnDev& f, uint16_t* h, float* y, int ksplit, int nb, hipStream_t s);
-int launch_prefill(const FfnDev& f, uint16_t* h, float* y, hipStream_t s);
+int launch_prefill(const FfnDev& f, uint16_t* h, float* y, float* xsum, float* hsum, hipStream_t s);
+int64_t prefill_extra_bytes(int T, int d, int I, int k);
 
 }  // namespace moe

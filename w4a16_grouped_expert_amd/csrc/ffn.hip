@@ -72,7 +72,7 @@ static WsLayout ws_layout(int T, int d, int I, int E, int k, int mode) {
   L.total = L.xsum_off;
   if (mode == MOE_MODE_PREFILL) {
     L.hsum_off = L.xsum_off + align256((int64_t)T * (d / kGroup) * 4);
-    L.total = L.hsum_off + align256(P * ((2 * I) / 128) * 4);
+    L.total = L.hsum_off + align256(P * (I / kGroup) * 4);
   }
   return L;
 }

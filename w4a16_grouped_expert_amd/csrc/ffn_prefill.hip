@@ -3,25 +3,41 @@
 // Inference", Abstract: all selected experts through fused grouped kernels on
 // four-bit group-128 weights).
 //
-// A block computes a 128 (weight rows) x 128 (tokens of one expert) tile with
-// four wavefronts of 64 x 64 (4 x 4 blocks of 16x16x32 bf16 MFMA).  Per K group
-// of 128: the block stages the tile's 128 activation rows (gathered through the
-// permutation) in LDS by LDS-DMA loads (no registers), double-buffered, with an
-// XOR swizzle of the 16-byte chunks so the MFMA B-fragment reads are bank-conflict
-// free; each wavefront loads its four packed
-// weight tiles straight from HBM (one 16-byte load per lane per tile) and decodes
-// them in registers to bf16 1 + c/16.  The group is finished in fp32 as
-//   total += scale * (16 * acc - 24 * sum_k x)
-// with the per-token group sums sum_k x precomputed (activations: a small pass;
-// SwiGLU output: written by the gate/up epilogue as two half-group partials).
-// Tiles are walked by persistent blocks; the tile list (active expert, row tile,
-// token tile) is built per block from the work list of moe_align.
+// A block of eight wavefronts computes a 512 (weight rows) x 128 (tokens of one
+// expert) tile; wavefront w owns rows 64 w .. 64 w + 63 for all 128 tokens as
+// 4 x 8 blocks of 16x16x32 bf16 MFMA.  Per K group of 128 the block stages,
+// double-buffered in LDS by LDS-DMA (global_load_lds, no registers): the 128
+// activation rows (gathered through the permutation; 16-byte chunks XOR-swizzled
+// so the MFMA B-fragment reads are bank-conflict free), the 32 packed 16 x 128
+// weight tiles and the per-token activation sums; the bf16 scales run one group
+// further ahead in a ring of their own.  Weights are decoded in registers to
+// bf16 1 + c/16.
+//
+// One accumulator per output carries the whole K loop.  With D_g the group's
+// sum of (c - 8) x / 16 and e_g the group's scale (a zero scale replaced by the
+// previous one: its group is all zero codes and adds nothing), the accumulator
+// holds A_g = sum over g' <= g of D_g' e_g' / e_g, i.e.
+//   A_g = A_{g-1} * (e_{g-1} / e_g) - 1.5 * sum_k x + MFMA sum of (1 + c/16) x,
+// one fma per output per group before that group's MFMAs, and the result is
+// 16 e_last A_last.  The ratio of each row is computed once per group by the
+// thread that owns the row and handed over in LDS.  sum_k x per token and group
+// is precomputed (activations: a small pass; SwiGLU output: written by the
+// gate/up epilogue, whose block covers exactly two groups of h).
+//
+// Blocks are persistent; the tile list (active expert, token tile, row tile) is
+// built per block from the work list of moe_align and walked in an order that
+// keeps the blocks resident on one XCD on the same expert, so its weights and
+// activations are fetched into that XCD's L2 once.
 #include "ffn_common.hpp"
 
 namespace moe {
 
-constexpr int kPBM = 128;               // tokens per block tile
-constexpr int kPBN = 128;               // weight rows per block tile
+constexpr int kPBM = 128;                  // tokens per block tile
+constexpr int kPBN = 256;                  // weight rows per block tile
+constexpr int kPTiles = kPBN / kTileRows;  // packed 16-row tiles per block tile
+constexpr int kPWaves = 8;                 // 4 row quarters x 2 token halves of the block tile
+constexpr int kPThreads = 64 * kPWaves;
+constexpr int kXcds = 8;
 
 // xsum[t][g] = sum of x[t][128 g .. 128 g + 127] in fp32 (one wavefront per token).
 __global__ __launch_bounds__(256) void k_group_sums(const uint16_t* __restrict__ x, int T, int d,
@@ -46,35 +62,99 @@ __global__ __launch_bounds__(256) void k_group_sums(const uint16_t* __restrict__
   }
 }
 
+// ---------------------------------------------------------------- LDS DMA
+// global_load_lds: each lane's 16 (or 4) bytes at `g` land in LDS at
+// lds_base + 16 * lane (4 * lane), with no registers in between.  Written as
+// inline asm with M0 saved and restored around it: the compiler neither sees
+// these loads in its wait counts nor assumes anything about the LDS they fill,
+// so every consumer waits explicitly (stage_barrier) and the stages are only
+// filled through these calls and read with plain LDS reads.
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(g), "s"(lds_base) : "memory");
+}
+__device__ __forceinline__ void lds_dma4(const void* g, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(g), "s"(lds_base) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
+
+// The same through a buffer resource: the address is base + voff (per lane) + soff
+// (wave-uniform), so advancing a stream by one K group costs no vector ALU work.
+__device__ __forceinline__ i32x4_t raw_rsrc(const void* base) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return i32x4_t{__builtin_amdgcn_readfirstlane((int)(uint32_t)a), __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xFFFF)),
+                 -1, kBufferRsrcWord3};
+}
+__device__ __forceinline__ void buf_dma16(i32x4_t rsrc, uint32_t voff, uint32_t soff, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %4 offen lds\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(voff), "s"(rsrc), "s"(lds_base), "s"(soff) : "memory");
+}
+__device__ __forceinline__ void buf_dma4(i32x4_t rsrc, uint32_t voff, uint32_t soff, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %4 offen lds\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(voff), "s"(rsrc), "s"(lds_base), "s"(soff) : "memory");
+}
+
+// One stage of the LDS pipeline: the activations and weights of one K group.
+struct PrefillStage {
+  u32x4_t x[kPBM * 16];     // chunk kc of token t at slot 16 t + (kc ^ (t & 15))
+  u32x4_t w[kPTiles * 64];  // packed tile j: lane l's 16 bytes at [64 j + l], as in HBM
+};
+constexpr int kStages = 3;
+
+// Wait until at most N vector-memory operations of this wavefront are in flight
+// (they retire in order; LDS-DMA included), finish its LDS operations, then meet
+// the block.
+template <int N>
+__device__ __forceinline__ void stage_wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// SiLU in fp32 with the hardware exp and reciprocal (a few ulp; h is rounded to bf16).
+__device__ __forceinline__ float silu_fast(float z) { return z * __builtin_amdgcn_rcpf(1.f + __expf(-z)); }
+
+// Pipeline, in K groups g = 0 .. G-1 (a "top of g" is the block barrier that
+// starts group g, after which batch g is resident):
+//   batch k, issued during group k - 2: activations and weights of group k
+//     (stage k % 3), the group sums of group k + 1 (ring of 4) and the scales of
+//     group k + 2 (ring of 4);
+//   at the top of k, the thread that owns row r turns the scales of group k + 2
+//     into the ratio e_{k+1} / e_{k+2} (16 e_last once past the end), ring of 2;
+//   during group g - 1 every lane reads the ratios and group sums it needs at the
+//     top of g into registers, so group g starts with the rescale fma right away.
 template <bool GATEUP>
-__global__ __launch_bounds__(256) void k_prefill(
+__global__ __launch_bounds__(kPThreads) void k_prefill(
     FfnDev f, const uint16_t* __restrict__ act, const float* __restrict__ asum, uint16_t* __restrict__ hout,
     float* __restrict__ hsum_out, float* __restrict__ yout) {
   const int K = GATEUP ? f.d : f.I;
   const int N = GATEUP ? 2 * f.I : f.d;
   const int G = K / kGroup;
-  const int NT = N / kPBN;
-  const int GH = (2 * f.I) / kPBN;  // h-sum partials per pair (two per group of h)
+  const int NT = (N + kPBN - 1) / kPBN;
+  const int GH = f.I / kGroup;  // groups of h = row tiles of gate/up
 
-  // activation tile of one K group: 128 tokens x 16 chunks of 16 bytes; chunk kc of
-  // token t sits at slot 16 t + (kc ^ (t & 15)), so the 16 tokens of an MFMA
-  // B fragment read 16 different 16-byte bank groups
-  __shared__ u32x4_t sx[2][kPBM * 16];
-  __shared__ int s_row[kPBM];        // activation row (token for gate/up, sorted position for down), -1 = none
+  __shared__ PrefillStage st[kStages];
+  __shared__ float s_xs[4][kPBM];      // group sums of group g at [g % 4]: token 64 h + 16 b + c at [64 h + 4 c + b]
+  __shared__ uint16_t s_sc[4][kPBN];   // bf16 scales of group g at [g % 4], row r of the block tile at [r]
+  __shared__ float s_ratio[2][kPBN];   // e_{g-1} / e_g per row at [g % 2]; 16 e_last at [G % 2]
+  __shared__ int s_row[kPBM];          // activation row (token for gate/up, sorted position for down), -1 = none
   __shared__ int s_pref[MOE_MAX_EXPERTS + 1];
-  __shared__ float s_hs[2][kPBM];    // gate/up: per-token h sums of the two row halves
-  __shared__ int s_wsum[4];
+  __shared__ float s_hs[4][kPBM];      // gate/up: per-token h sums of each row quarter's 32 columns
+  __shared__ int s_wsum[kPWaves];
 
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wr = wave & 1, wt = wave >> 1;  // row half, token half of the block tile
+  const int wr = wave & 3, wt = wave >> 2;  // rows 64 wr .. + 63, tokens 64 wt .. + 63 of the block tile
   const int col = lane & 15, kq = lane >> 4;
   const int U = f.active[0];
   const i32x4_t* work = reinterpret_cast<const i32x4_t*>(f.active + 4);
 
   // tiles of active expert u: ceil(count / 128) token tiles x NT row tiles; exclusive prefix in LDS
   if (tid == 0) s_pref[0] = 0;
-  for (int base = 0; base < U; base += 256) {
+  for (int base = 0; base < U; base += kPThreads) {
     __syncthreads();
     const int u = base + tid;
     const int n_e = u < U ? work[u][2] : 0;
@@ -93,9 +173,14 @@ __global__ __launch_bounds__(256) void k_prefill(
   __syncthreads();
   const int total = s_pref[U];
 
+  // Workgroups are dealt to the XCDs round robin; renumber them so each XCD owns
+  // a contiguous run of tile slots (consecutive tiles share an expert).
+  const int nblk = gridDim.x;
+  const int vb = (nblk % kXcds == 0) ? (blockIdx.x % kXcds) * (nblk / kXcds) + blockIdx.x / kXcds : blockIdx.x;
+
   const uint32_t kMask = vgpr_const(0x00780078u), kOne = vgpr_const(0x3F803F80u);
 
-  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+  for (int tile = vb; tile < total; tile += nblk) {
     int lo = 0, hi = U;  // s_pref[lo] <= tile < s_pref[hi]
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
@@ -104,136 +189,223 @@ __global__ __launch_bounds__(256) void k_prefill(
     const int u = lo;
     const i32x4_t w4 = work[u];
     const int e = w4[0], row0 = w4[1], n_e = w4[2];
-    const int n_mt = (n_e + kPBM - 1) / kPBM;
     const int local = tile - s_pref[u];
-    const int nt = local / n_mt, mt = local % n_mt;
+    const int mt = local / NT, nt = local % NT;  // row tiles fastest: neighbours share the token tile
     const uint8_t* blob = f.blob(e);
     if (!blob) continue;  // uniform over the block
 
-    __syncthreads();  // the previous tile is done with s_row / sx / s_hs
+    __syncthreads();  // the previous tile is done with every LDS buffer
     if (tid < kPBM) {
       const int r = mt * kPBM + tid;
       s_row[tid] = r < n_e ? (GATEUP ? f.sorted_pairs[row0 + r] / f.k : row0 + r) : -1;
     }
     __syncthreads();
 
-    const uint8_t* codes = blob + (GATEUP ? f.off_w13_codes : f.off_w2_codes) +
-                           (int64_t)(nt * (kPBN / kTileRows) + wr * 4) * G * kTileBytes + 16 * lane;
-    const uint16_t* scales =
-        reinterpret_cast<const uint16_t*>(blob + (GATEUP ? f.off_w13_scales : f.off_w2_scales)) +
-        (int64_t)(nt * (kPBN / kTileRows) + wr * 4) * G * kTileRows + 4 * kq;
-    const int64_t tsc = (int64_t)G * kTileBytes, tss = (int64_t)G * kTileRows;
-
-    // staging by LDS DMA: wave w fills slots [w*512, w*512 + 512) of the tile, 64 per
-    // instruction; lane l of instruction j fills slot s = w*512 + 64 j + l
-    // rows are gathered tokens for gate/up (offsets from x, below 4 GiB by the host
-    // check) and consecutive sorted positions for down (offsets from the tile's first row)
-    const uint16_t* act_tile = GATEUP ? act : act + (int64_t)(row0 + mt * kPBM) * K;
-    uint32_t soff[8];
+    // ---- this lane's DMA sources for the tile (group 0; group g adds g * stride)
+    // Activations: instruction j of wavefront w fills slots s = 64 (4 w + j) + lane,
+    // i.e. chunk (s % 16) ^ (t % 16) of token t = s / 16.  Rows are gathered tokens
+    // for gate/up (byte offsets from x, below 4 GiB by the host check) and
+    // consecutive sorted positions for down (offsets from the tile's first row);
+    // padding tokens read the tile's first row and their outputs are dropped.
+    const uint8_t* act_tile = reinterpret_cast<const uint8_t*>(GATEUP ? act : act + (int64_t)(row0 + mt * kPBM) * K);
+    const i32x4_t rs_x = raw_rsrc(act_tile);
+    uint32_t xoff[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int slot = wave * 512 + 64 * j + lane;
-      const int t = slot >> 4, kc = (slot & 15) ^ (t & 15);
-      int row = 0;  // padding tokens read row 0 of the tile (a real row); their outputs are dropped
+    for (int j = 0; j < 4; ++j) {
+      const int sl = (wave * 4 + j) * 64 + lane;
+      const int t = sl >> 4, kc = (sl & 15) ^ (t & 15);
+      int row;
       if (GATEUP) row = s_row[t] >= 0 ? s_row[t] : s_row[0];
       else row = s_row[t] >= 0 ? t : 0;
-      soff[j] = ((uint32_t)row * (uint32_t)K + 8u * (uint32_t)kc) * 2u;  // byte offset of the chunk in group 0
+      xoff[j] = ((uint32_t)row * (uint32_t)K + 8u * (uint32_t)kc) * 2u;
     }
-    // per-token group sums of this lane's four token columns
-    int xrow[4];
+    // Weights: instruction j of wavefront w fills packed tile 2 w + j.  A last row
+    // tile past N reads the final packed tile in place of the missing ones (those
+    // rows are computed but not stored).
+    const int last_tile = N / kTileRows - 1;
+    const i32x4_t rs_w = raw_rsrc(blob + (GATEUP ? f.off_w13_codes : f.off_w2_codes));
+    uint32_t woff[2];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) xrow[b] = s_row[wt * 64 + b * 16 + col];
-
-    auto stage = [&](int buf, int g) {
-      const uint8_t* base = reinterpret_cast<const uint8_t*>(act_tile) + (int64_t)g * kGroup * 2;
+    for (int j = 0; j < 2; ++j)
+      woff[j] = (uint32_t)min(nt * kPTiles + 2 * wave + j, last_tile) * (uint32_t)(G * kTileBytes) + 16u * lane;
+    // Scales (wavefront 0, two 4-byte instructions): word p = 64 j + lane holds rows
+    // 2 (p % 8), + 1 of tile p / 8.  Group sums (wavefront 1, two instructions):
+    // slot p = 64 j + lane holds token 64 j + 16 (p % 4) + (p % 64) / 4.
+    const i32x4_t rs_a = raw_rsrc(wave == 0 ? (const void*)(blob + (GATEUP ? f.off_w13_scales : f.off_w2_scales))
+                                            : (const void*)asum);
+    uint32_t aoff[2] = {0u, 0u};
+    uint32_t astep = 0;  // bytes per group
+    if (wave == 0) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(base + soff[j]),
-                                         &sx[buf][wave * 512 + 64 * j], 16, 0, 0);
-    };
-    auto load_sums = [&](float (&xs)[4], int g) {
+      for (int j = 0; j < 2; ++j) {
+        const int p = 64 * j + lane;
+        aoff[j] = ((uint32_t)min(nt * kPTiles + (p >> 3), last_tile) * (uint32_t)(G * kTileRows) + 2u * (p & 7)) * 2u;
+      }
+      astep = kTileRows * 2;
+    } else if (wave == 1) {
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int r = xrow[b];
-        float v = 0.f;
-        if (r >= 0) v = GATEUP ? asum[(int64_t)r * G + g] : asum[(int64_t)r * GH + 2 * g] + asum[(int64_t)r * GH + 2 * g + 1];
-        xs[b] = -24.f * v;
+      for (int j = 0; j < 2; ++j) {
+        const int t = 64 * j + 16 * (lane & 3) + (lane >> 2);
+        const int r = s_row[t] >= 0 ? s_row[t] : s_row[0];
+        aoff[j] = (uint32_t)r * (uint32_t)(GATEUP ? G : GH) * 4u;
+      }
+      astep = 4;
+    }
+    auto issue_aux = [&](int g) {  // scales (wave 0) or group sums (wave 1) of group g
+      if (wave == 0) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) buf_dma4(rs_a, aoff[j], (uint32_t)g * astep, lds_addr(&s_sc[g & 3][128 * j]));
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) buf_dma4(rs_a, aoff[j], (uint32_t)g * astep, lds_addr(&s_xs[g & 3][64 * j]));
       }
     };
-    auto load_w = [&](u32x4_t (&cw)[4], u32x2_t (&sw)[4], int g) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        cw[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(codes + t * tsc + (int64_t)g * kTileBytes));
-        sw[t] = *reinterpret_cast<const u32x2_t*>(scales + t * tss + g * kTileRows);
+    // Part `part` (0..3) of batch k: one activation instruction, a weight
+    // instruction on parts 0 and 2, the scales / group sums on part 1.
+    auto issue_part = [&](int k, int part) {
+      PrefillStage& S = st[k % kStages];
+      buf_dma16(rs_x, xoff[part], (uint32_t)k * (kGroup * 2), lds_addr(&S.x[(wave * 4 + part) * 64]));
+      if ((part & 1) == 0)
+        buf_dma16(rs_w, woff[part >> 1], (uint32_t)k * kTileBytes, lds_addr(&S.w[(wave * 2 + (part >> 1)) * 64]));
+      if (part == 1) {
+        if (wave == 0 && k + 2 < G) issue_aux(k + 2);
+        if (wave == 1 && k + 1 < G) issue_aux(k + 1);
       }
     };
+    auto bf16_at = [](uint16_t b) { return __uint_as_float((uint32_t)b << 16); };
+    // DMA instructions of this wavefront in batch k (6, plus two for the scales /
+    // group sums it carries)
+    auto batch_has_aux = [&](int k) { return (wave == 0 && k + 2 < G) || (wave == 1 && k + 1 < G); };
 
-    f32x4_t tot[4][4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) tot[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    f32x4_t acc[4][4];
+    float e_next = 1.f;  // scale chain of row `tid` (threads 0 .. 255): e of the newest group seen
+    f32x4_t rn[4];       // this lane's ratios for the next group
+    f32x4_t xsn;         // this lane's group sums for the next group
 
-    u32x4_t cw[4], cwn[4];
-    u32x2_t sw[4], swn[4];
-    float xs[4], xsn[4];
-    load_w(cw, sw, 0);
-    load_sums(xs, 0);
-    stage(0, 0);
+    // prologue: scales of groups 0, 1 and the group sums of group 0, then batches 0, 1
+    if (wave == 0) {
+      issue_aux(0);
+      if (G > 1) issue_aux(1);
+    } else if (wave == 1) {
+      issue_aux(0);
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    for (int g = 0; g < G; ++g) {
-      const int buf = g & 1;
-      if (g + 1 < G) {
-        load_w(cwn, swn, g + 1);
-        load_sums(xsn, g + 1);
-        stage(buf ^ 1, g + 1);
+    if (tid < kPBN) {
+      const float s0 = bf16_at(s_sc[0][tid]);
+      const float e0 = s0 != 0.f ? s0 : 1.f;
+      float out;
+      if (G > 1) {
+        const float s1 = bf16_at(s_sc[1][tid]);
+        e_next = s1 != 0.f ? s1 : e0;
+        out = e0 * __builtin_amdgcn_rcpf(e_next);
+      } else {
+        e_next = e0;
+        out = 16.f * e0;
       }
-      f32x4_t acc[4][4];
+      s_ratio[1][tid] = out;
+    }
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+    for (int part = 0; part < 4; ++part) issue_part(0, part);
+    if (G > 1) {
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int part = 0; part < 4; ++part) issue_part(1, part);
+    }
+
+    for (int g = 0; g < G; ++g) {
+      // batch g has landed (batch g + 1 may still be in flight); everyone is done with stage g - 1
+      if (g + 1 < G) {
+        if (batch_has_aux(g + 1)) stage_wait_barrier<8>(); else stage_wait_barrier<6>();
+      } else {
+        stage_wait_barrier<0>();
+      }
+      // Row tid's ratio two groups ahead (16 e_last once that is past the end).
+      if (tid < kPBN && g + 2 <= G) {
+        float out;
+        if (g + 2 < G) {
+          const float sn = bf16_at(s_sc[(g + 2) & 3][tid]);
+          const float en = sn != 0.f ? sn : e_next;
+          out = e_next * __builtin_amdgcn_rcpf(en);
+          e_next = en;
+        } else {
+          out = 16.f * e_next;
+        }
+        s_ratio[g & 1][tid] = out;
+      }
+
+      const PrefillStage& S = st[g % kStages];
+      // acc = acc * (e_{g-1} / e_g) - 1.5 sum_k x   (acc = -1.5 sum_k x for g = 0)
+      if (g == 0) {
+        const f32x4_t xs = *reinterpret_cast<const f32x4_t*>(&s_xs[0][64 * wt + 4 * col]);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const float c = -1.5f * xs[b];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) acc[t][b] = f32x4_t{c, c, c, c};
+        }
+      } else {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const float c = -1.5f * xsn[b];
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[t][b][q] = fmaf(acc[t][b][q], rn[t][q], c);
+        }
+      }
+      // the next group's ratios (written at the top of g - 1) and group sums (batch g)
+      if (g + 1 < G) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) rn[t] = *reinterpret_cast<const f32x4_t*>(&s_ratio[(g + 1) & 1][64 * wr + 16 * t + 4 * kq]);
+        xsn = *reinterpret_cast<const f32x4_t*>(&s_xs[(g + 1) & 3][64 * wt + 4 * col]);
+      }
+
+      u32x4_t cw[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) cw[t] = S.w[(wr * 4 + t) * 64 + lane];
+      const u32x4_t* xrow = &S.x[(wt * 64 + col) * 16];  // token block b adds 256 slots
+      u32x4_t xb[4], xn[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) xb[b] = xrow[b * 256 + (kq ^ col)];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        if (i < 3) {
+#pragma unroll
+          for (int b = 0; b < 4; ++b) xn[b] = xrow[b * 256 + ((4 * (i + 1) + kq) ^ col)];
+        }
+        if (g + 2 < G) issue_part(g + 2, i);  // spread the DMA issue over the K steps
         bf16x8_t wa[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) wa[t] = as_bf16x8(decode_word_biased(cw[t][i], kMask, kOne));
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int tok = wt * 64 + b * 16 + col;
-          const u32x4_t xb = sx[buf][tok * 16 + ((4 * i + kq) ^ (tok & 15))];
+        for (int b = 0; b < 4; ++b)
 #pragma unroll
-          for (int t = 0; t < 4; ++t) acc[t][b] = mfma16x16x32(wa[t], as_bf16x8(xb), acc[t][b]);
+          for (int t = 0; t < 4; ++t) acc[t][b] = mfma16x16x32(wa[t], as_bf16x8(xb[b]), acc[t][b]);
+        if (i < 3) {
+#pragma unroll
+          for (int b = 0; b < 4; ++b) xb[b] = xn[b];
         }
       }
+    }
+    // 16 e_last (written at the top of G - 2, or in the prologue) is visible since the last barrier
+    {
+      const float* mult = &s_ratio[G & 1][64 * wr];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const float s4[4] = {__uint_as_float(sw[t][0] << 16), __uint_as_float(sw[t][0] & 0xFFFF0000u),
-                             __uint_as_float(sw[t][1] << 16), __uint_as_float(sw[t][1] & 0xFFFF0000u)};
+        const f32x4_t m = *reinterpret_cast<const f32x4_t*>(&mult[16 * t + 4 * kq]);
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) tot[t][b][q] = fmaf(s4[q], fmaf(16.f, acc[t][b][q], xs[b]), tot[t][b][q]);
+          for (int q = 0; q < 4; ++q) acc[t][b][q] *= m[q];
       }
-      if (g + 1 < G) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          cw[t] = cwn[t];
-          sw[t] = swn[t];
-        }
-#pragma unroll
-        for (int b = 0; b < 4; ++b) xs[b] = xsn[b];
-      }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the next group's tile has landed in LDS
-      __syncthreads();                                   // and every wavefront is done with `buf`
     }
 
     if (GATEUP) {
-      // tiles (0,1) and (2,3) are gate/up pairs: h columns nt*64 + wr*32 + 16p + 4kq + q
-      float hs[4] = {0.f, 0.f, 0.f, 0.f};
+      // tiles (0,1) and (2,3) of the wavefront are gate/up pairs: h columns nt*128 + wr*32 + 16p + 4kq + q
+      float hs[4];
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
+        hs[b] = 0.f;
         const int r = wt * 64 + b * 16 + col;
         const int pos = row0 + mt * kPBM + r;
         const bool ok = mt * kPBM + r < n_e;
@@ -242,17 +414,17 @@ __global__ __launch_bounds__(256) void k_prefill(
           uint32_t hv[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            hv[q] = f32_to_bf16_bits(silu_f32(tot[2 * p][b][q]) * tot[2 * p + 1][b][q]);
+            hv[q] = f32_to_bf16_bits(silu_fast(acc[2 * p][b][q]) * acc[2 * p + 1][b][q]);
             hs[b] += __uint_as_float(hv[q] << 16);
           }
           if (ok) {
-            const int hcol = nt * 64 + wr * 32 + 16 * p + 4 * kq;
+            const int hcol = nt * 128 + wr * 32 + 16 * p + 4 * kq;
             u32x2_t o = {hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16)};
             *reinterpret_cast<u32x2_t*>(hout + (int64_t)pos * f.I + hcol) = o;
           }
         }
       }
-      // per-token sum of this block's 64 h columns: lanes kq = 0..3, then the two row halves
+      // per-token sum of this block's 128 h columns (one group of h): lanes kq, then the four row quarters
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         hs[b] += __shfl_xor(hs[b], 16);
@@ -262,7 +434,7 @@ __global__ __launch_bounds__(256) void k_prefill(
       __syncthreads();
       if (tid < kPBM) {
         const int r = mt * kPBM + tid;
-        if (r < n_e) hsum_out[(int64_t)(row0 + r) * GH + nt] = s_hs[0][tid] + s_hs[1][tid];
+        if (r < n_e) hsum_out[(int64_t)(row0 + r) * GH + nt] = (s_hs[0][tid] + s_hs[1][tid]) + (s_hs[2][tid] + s_hs[3][tid]);
       }
     } else {
 #pragma unroll
@@ -273,7 +445,7 @@ __global__ __launch_bounds__(256) void k_prefill(
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             const int n = nt * kPBN + wr * 64 + t * 16 + 4 * kq;
-            *reinterpret_cast<f32x4_t*>(yout + (int64_t)pos * f.d + n) = tot[t][b];
+            if (n < N) *reinterpret_cast<f32x4_t*>(yout + (int64_t)pos * f.d + n) = acc[t][b];
           }
         }
       }
@@ -288,7 +460,7 @@ static int prefill_grid(Kern kern, int slot) {
     int dev = 0, cus = 0, per_cu = 0;
     (void)hipGetDevice(&dev);
     (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, 0);
+    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kPThreads, 0);
     cached[slot] = std::max(1, cus) * std::max(1, per_cu);
   }
   return cached[slot];
@@ -296,13 +468,14 @@ static int prefill_grid(Kern kern, int slot) {
 
 int64_t prefill_extra_bytes(int T, int d, int I, int k) {
   const int64_t P = (int64_t)T * k;
-  return (int64_t)T * (d / kGroup) * 4 + P * ((2 * I) / kPBN) * 4 + 512;
+  return (int64_t)T * (d / kGroup) * 4 + P * (I / kGroup) * 4 + 512;
 }
 
 int launch_prefill(const FfnDev& f, uint16_t* h, float* y, float* xsum, float* hsum, hipStream_t s) {
-  // gate/up gathers token rows by 32-bit byte offsets from x
-  if ((int64_t)f.T * f.d * 2 >= (int64_t(1) << 32)) {
-    set_error("moe_w4a16_grouped_ffn: prefill needs T * d * 2 < 4 GiB (T=%d d=%d)", f.T, f.d);
+  // the kernels address x, h and the group sums with 32-bit byte offsets
+  if ((int64_t)f.T * f.d * 2 >= (int64_t(1) << 32) || f.P * f.I * 2 >= (int64_t(1) << 32)) {
+    set_error("moe_w4a16_grouped_ffn: prefill needs T * d * 2 and T * k * I * 2 below 4 GiB (T=%d d=%d I=%d k=%d)", f.T,
+              f.d, f.I, f.k);
     return MOE_ERR_UNSUPPORTED_SHAPE;
   }
   hipLaunchKernelGGL(k_group_sums, dim3((unsigned)ceil_div(f.T, 4)), dim3(256), 0, s, f.x, f.T, f.d, xsum);
@@ -310,20 +483,20 @@ int launch_prefill(const FfnDev& f, uint16_t* h, float* y, float* xsum, float* h
   if (rc) return rc;
   // upper bound of tiles: sum over experts of ceil(n_e / 128) <= P / 128 + U
   const int64_t mt_bound = f.P / kPBM + f.umax;
-  const int64_t tiles_gu = mt_bound * ((2 * f.I) / kPBN);
-  const int64_t tiles_dn = mt_bound * (f.d / kPBN);
+  const int64_t tiles_gu = mt_bound * ceil_div(2 * f.I, kPBN);
+  const int64_t tiles_dn = mt_bound * ceil_div(f.d, kPBN);
   auto kgu = k_prefill<true>;
   auto kdn = k_prefill<false>;
   const int64_t grid_gu = std::min<int64_t>(prefill_grid(kgu, 0), tiles_gu);
   const int64_t grid_dn = std::min<int64_t>(prefill_grid(kdn, 1), tiles_dn);
   timing_begin(K_GATEUP_PREFILL, s);
-  hipLaunchKernelGGL(kgu, dim3((unsigned)grid_gu), dim3(256), 0, s, f, f.x, (const float*)xsum, h, hsum,
+  hipLaunchKernelGGL(kgu, dim3((unsigned)grid_gu), dim3(kPThreads), 0, s, f, f.x, (const float*)xsum, h, hsum,
                      (float*)nullptr);
   timing_end(K_GATEUP_PREFILL, s);
   rc = check_launch("grouped gate/up (prefill)");
   if (rc) return rc;
   timing_begin(K_DOWN_PREFILL, s);
-  hipLaunchKernelGGL(kdn, dim3((unsigned)grid_dn), dim3(256), 0, s, f, (const uint16_t*)h, (const float*)hsum,
+  hipLaunchKernelGGL(kdn, dim3((unsigned)grid_dn), dim3(kPThreads), 0, s, f, (const uint16_t*)h, (const float*)hsum,
                      (uint16_t*)nullptr, (float*)nullptr, y);
   timing_end(K_DOWN_PREFILL, s);
   return check_launch("grouped down (prefill)");

@@ -3,7 +3,7 @@
 Workload: OLMoE-1B-7B-shaped decode, 16 MoE layers (d_model 2048, 64 experts,
 top-8, expert intermediate 1024, SwiGLU), int4 symmetric group-128 experts with
 bf16 scales, bf16 router and activations, all 64 experts of every layer
-resident in HBM (16 x 207.6 MB).  One step = route -> align -> grouped FFN
+resident in HBM (16 x 207.6 MB).  One step = route + align (one launch) -> grouped FFN
 (gate/up + SwiGLU, down, combine) for each of the 16 layers on fresh
 activations, T tokens per step (headline T = 16).
 
@@ -75,6 +75,7 @@ class Decoder:
         self.T_max = T_max
         self.route = moe.alloc_route(T_max, s.E, s.k, device)
         self.align = moe.alloc_align(T_max, s.k, s.E, device)
+        self.counter = moe.alloc_counter(device)
         need = max(moe.ffn_workspace_bytes(t, s.d, s.I, s.E, s.k) for t in range(1, T_max + 1))
         self.ws = torch.empty(need, dtype=torch.uint8, device=device)
         self.out = [torch.empty((T_max, s.d), dtype=torch.bfloat16, device=device) for _ in range(wl.layers)]
@@ -86,8 +87,7 @@ class Decoder:
         r = moe.RouteOut(self.route.logits[:T], self.route.ids[:T], self.route.weights[:T])
         a = moe.AlignOut(self.align.offsets, self.align.sorted_pairs[:T * s.k], self.align.pair_pos[:T * s.k],
                          self.align.active, None, 0)
-        moe.moe_route_into(x, wr, s.k, r)
-        moe.moe_align_into(r.ids, s.E, a)
+        moe.moe_route_align_into(x, wr, s.k, r, a, self.counter)
         moe.moe_w4a16_grouped_ffn_into(x, r, a, bank, s.I, self.out[l][:T], self.ws)
         return a
 

@@ -156,6 +156,35 @@ def test_align_edges():
     check_align_gpu(skew, 64, 64)
 
 
+@pytest.mark.parametrize("T,E,k", [(1, 64, 8), (16, 64, 8), (128, 64, 8), (16, 8, 2), (7, 1024, 16), (129, 64, 8)])
+def test_route_align_fused_equals_separate(T, E, k):
+    """moe_route_align (one launch up to 128 tokens, the separate calls above) gives
+    bit-identical routing and permutation; three calls in a row reuse the counter."""
+    say(f"route_align T={T} E={E} k={k}")
+    d = 2048 if E <= 64 else 512
+    x = synth.normal_bf16((T, d), 1.0, seed=77 + T).to(DEV)
+    wr = synth.normal_bf16((E, d), 0.02, seed=78 + E).to(DEV)
+    r0 = moe.moe_route(x, wr, k)
+    a0 = moe.moe_align(r0.ids, E, block_m=128)
+    counter = moe.alloc_counter(DEV)
+    for rep in range(3):
+        r1 = moe.alloc_route(T, E, k, DEV)
+        a1 = moe.alloc_align(T, k, E, DEV, block_m=128)
+        moe.moe_route_align_into(x, wr, k, r1, a1, counter)
+        torch.cuda.synchronize()
+        assert torch.equal(r1.logits, r0.logits)
+        assert torch.equal(r1.ids, r0.ids)
+        assert torch.equal(r1.weights, r0.weights)
+        for name in ("offsets", "sorted_pairs", "pair_pos", "tile_offsets"):
+            assert torch.equal(getattr(a1, name), getattr(a0, name)), name
+        U = int(a0.active[0])
+        assert torch.equal(a1.active[:4 + 4 * U], a0.active[:4 + 4 * U])
+        assert int(counter[0]) == 0
+    # and against the oracle's selection
+    _, ids, _ = oroute.route(bits(x.cpu()), bits(wr.cpu()), k)
+    assert np.array_equal(r0.ids.cpu().numpy(), ids)
+
+
 # ------------------------------------------------------------------ whole layer
 
 def run_layer(x, wr, bank, I, k, mode=moe.MODE_AUTO):

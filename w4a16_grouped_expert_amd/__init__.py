@@ -6,8 +6,8 @@ library has to be built in-tree first (``w4a16_grouped_expert_amd._build.build``
 there is no fallback implementation.
 """
 from .api import (MODE_AUTO, active_experts, MODE_DECODE, MODE_PREFILL, AlignOut, MoELayer, RouteOut, SlotCache,  # noqa: F401
-                  alloc_align, alloc_route, alloc_workspace, expert_layout, ffn_workspace_bytes,
-                  moe_align, moe_align_into, moe_route, moe_route_into, moe_w4a16_grouped_ffn,
+                  alloc_align, alloc_counter, alloc_route, alloc_workspace, expert_layout, ffn_workspace_bytes,
+                  moe_align, moe_align_into, moe_route, moe_route_align_into, moe_route_into, moe_w4a16_grouped_ffn,
                   moe_w4a16_grouped_ffn_into, pack_experts, pack_w4_g128, timing_enable, timing_read,
                   timing_reset)
 from ._lib import LIB_PATH, MoeError, lib  # noqa: F401

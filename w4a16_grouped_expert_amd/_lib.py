@@ -53,6 +53,8 @@ SIGNATURES = {
     "pack_w4_g128": (c_int, [c_vp, c_int, c_int, c_int, c_int, c_vp, c_i64, c_vp, c_i64, c_vp]),
     "moe_route": (c_int, [c_vp, c_vp, c_int, c_int, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp]),
     "moe_align": (c_int, [c_vp, c_int, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "moe_route_align": (c_int, [c_vp, c_vp, c_int, c_int, c_int, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                c_vp, c_vp, c_vp, c_vp, c_vp]),
     "moe_ffn_workspace_bytes": (c_i64, [c_int, c_int, c_int, c_int, c_int, c_int]),
     "moe_w4a16_grouped_ffn": (c_int, [ctypes.POINTER(FfnArgs), c_vp]),
     "moe_slot_cache_create": (c_int, [c_int, c_int, c_i64, c_vp, c_vp, ctypes.POINTER(c_vp)]),

@@ -148,6 +148,26 @@ def moe_align(ids, E, block_m=0, stream=None) -> AlignOut:
     return moe_align_into(ids, E, alloc_align(T, k, E, ids.device, block_m), stream)
 
 
+def alloc_counter(device) -> torch.Tensor:
+    """A zeroed device counter for moe_route_align (each call leaves it zero)."""
+    return torch.zeros(4, dtype=torch.int32, device=device)
+
+
+def moe_route_align_into(x, w_router, k, route: RouteOut, al: AlignOut, counter: torch.Tensor, renormalize=True,
+                         stream=None):
+    """moe_route + moe_align in one launch for T <= 128 (bit-identical outputs)."""
+    _need(x, torch.bfloat16, "x")
+    _need(w_router, torch.bfloat16, "w_router")
+    _need(counter, torch.int32, "counter")
+    T, d = x.shape
+    E = w_router.shape[0]
+    check("moe_route_align", lib().moe_route_align(
+        _ptr(x), _ptr(w_router), T, d, E, k, int(bool(renormalize)), al.block_m, _ptr(route.logits),
+        _ptr(route.ids), _ptr(route.weights), _ptr(al.offsets), _ptr(al.sorted_pairs), _ptr(al.pair_pos),
+        _ptr(al.active), _ptr(al.tile_offsets), _ptr(counter), _stream(stream)))
+    return route, al
+
+
 # ---------------------------------------------------------------- grouped FFN
 
 def ffn_workspace_bytes(T, d, I, E, k, mode=MODE_AUTO) -> int:
@@ -211,6 +231,7 @@ class MoELayer:
         self.T_max = T_max
         self.route = alloc_route(T_max, self.E, k, dev)
         self.align = alloc_align(T_max, k, self.E, dev)
+        self.counter = alloc_counter(dev)
         self.out = torch.empty((T_max, self.d), dtype=torch.bfloat16, device=dev)
         need = max(ffn_workspace_bytes(t, self.d, I, self.E, k, mode) for t in range(1, T_max + 1))
         self.ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
@@ -226,8 +247,7 @@ class MoELayer:
         if T > self.T_max:
             raise ValueError(f"T={T} exceeds T_max={self.T_max}")
         r, a = self.views(T)
-        moe_route_into(x, self.w_router, self.k, r, self.renormalize, stream)
-        moe_align_into(r.ids, self.E, a, stream)
+        moe_route_align_into(x, self.w_router, self.k, r, a, self.counter, self.renormalize, stream)
         o = self.out[:T] if out is None else out
         ws_need = ffn_workspace_bytes(T, self.d, self.I, self.E, self.k, self.mode)
         moe_w4a16_grouped_ffn_into(x, r, a, self.bank, self.I, o, self.ws[:max(ws_need, 256)], self.mode, True,

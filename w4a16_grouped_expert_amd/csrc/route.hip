@@ -9,7 +9,7 @@
 // Two launch shapes: one 1024-thread block per token for small T (latency), and
 // blocks of TB tokens x all experts for large T (router weights reused across
 // the TB tokens).
-#include "common.hpp"
+#include "align_block.hpp"
 
 namespace moe {
 
@@ -150,15 +150,17 @@ __global__ __launch_bounds__(1024) void k_route_token(const uint16_t* __restrict
   }
   __syncthreads();
   const float lmax = s_sel_v[0];
+  // the same sums, in the same order, as topk_wave
   if (tid < 64) {
     float part = 0.f;
     if (renormalize) {
-      if (tid < k) part = expf(s_sel_v[tid] - lmax);
+      if (tid == 0)
+        for (int j = 0; j < k; ++j) part += expf(s_sel_v[j] - lmax);
     } else {
       for (int e = tid; e < E; e += 64) part += expf(s_logit[e] - lmax);
-    }
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+      for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+    }
     if (tid == 0) s_den = part;
   }
   __syncthreads();
@@ -166,6 +168,104 @@ __global__ __launch_bounds__(1024) void k_route_token(const uint16_t* __restrict
     ids[(int64_t)t * k + tid] = s_sel_i[tid];
     weights[(int64_t)t * k + tid] = expf(s_sel_v[tid] - lmax) / s_den;
   }
+}
+
+// Decode-sized steps, routing and alignment in one launch.  Every workgroup
+// computes 16 logits, one per wavefront (lane l takes the 16-byte chunks l,
+// l + 64, ... of d; the float64 partial sums meet in a butterfly), releases them
+// with device-coherent stores and counts itself done on a counter in device
+// memory once they have completed.  The workgroup that counts last reads
+// everyone's logits with device-coherent loads into LDS, runs the top-k of
+// every token (one wavefront per token) and the alignment (align_block), and puts
+// the counter back to zero for the next call.
+constexpr int kRouteAlignMaxT = 128;
+constexpr int kRouteAlignMaxLogits = 16384;  // T * E staged in LDS by the last workgroup
+
+__global__ __launch_bounds__(kAlignThreads) void k_route_align(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int T, int d, int E, int k, int renormalize,
+    int block_m, int id_bits, float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ weights,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_pos,
+    int32_t* __restrict__ active, int32_t* __restrict__ tile_offsets, int32_t* __restrict__ counter) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int e = blockIdx.x * kAlignWaves + wave, t = blockIdx.y;
+  if (e < E) {
+    const int nch = d / 8;
+    const uint16_t* xr = x + (int64_t)t * d;
+    const uint16_t* wrow = wr + (int64_t)e * d;
+    double acc = 0.0;
+    constexpr int kB = 4;
+    for (int c0 = 0; c0 < nch; c0 += 64 * kB) {
+      u32x4_t xq[kB], wq[kB];
+#pragma unroll
+      for (int c = 0; c < kB; ++c) {
+        const int ch = c0 + lane + 64 * c;
+        xq[c] = ch < nch ? *reinterpret_cast<const u32x4_t*>(xr + 8 * ch) : u32x4_t{0u, 0u, 0u, 0u};
+        wq[c] = ch < nch ? *reinterpret_cast<const u32x4_t*>(wrow + 8 * ch) : u32x4_t{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int c = 0; c < kB; ++c)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          acc = fma(bf16_to_f64(xq[c][m] & 0xFFFFu), bf16_to_f64(wq[c][m] & 0xFFFFu), acc);
+          acc = fma(bf16_to_f64(xq[c][m] >> 16), bf16_to_f64(wq[c][m] >> 16), acc);
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    // device-coherent store (no L2 write-back of everything else needed)
+    if (lane == 0) __hip_atomic_store(logits + (int64_t)t * E + e, (float)acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __shared__ int s_last;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wavefront's logit has reached device scope
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             (int)(gridDim.x * gridDim.y) - 1;
+  __syncthreads();
+  if (!s_last) return;
+  // every other workgroup's logits are complete at device scope: one coherent read
+  // of all T * E of them into LDS
+  __shared__ float s_lg[kRouteAlignMaxLogits];
+  for (int i = threadIdx.x; i < T * E; i += kAlignThreads)
+    s_lg[i] = __hip_atomic_load(logits + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  // top-k by rank: each (token, expert) logit counts the logits of its token that
+  // beat it (value desc, index asc); the k with rank < k write themselves
+  __shared__ float s_sel_v[kRouteAlignMaxT][MOE_MAX_TOPK];
+  __shared__ int s_sel_i[kRouteAlignMaxT][MOE_MAX_TOPK];
+  for (int i = threadIdx.x; i < T * E; i += kAlignThreads) {
+    const int tt = i / E, ee = i - tt * E;
+    const float v = s_lg[i];
+    const float* row = s_lg + tt * E;
+    int rank = 0;
+    for (int o = 0; o < E; ++o) rank += better(row[o], o, v, ee) ? 1 : 0;
+    if (rank < k) {
+      s_sel_v[tt][rank] = v;
+      s_sel_i[tt][rank] = ee;
+    }
+  }
+  __syncthreads();
+  // weights, with the sums of topk_wave in the same order
+  for (int tt = wave; tt < T; tt += kAlignWaves) {
+    const float lmax = s_sel_v[tt][0];
+    float den = 0.f;
+    if (renormalize) {
+      for (int j = 0; j < k; ++j) den += expf(s_sel_v[tt][j] - lmax);
+    } else {
+      float part = 0.f;
+      for (int ee = lane; ee < E; ee += 64) part += expf(s_lg[tt * E + ee] - lmax);
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+      den = part;
+    }
+    if (lane < k) {
+      ids[(int64_t)tt * k + lane] = s_sel_i[tt][lane];
+      weights[(int64_t)tt * k + lane] = expf(s_sel_v[tt][lane] - lmax) / den;
+    }
+  }
+  __syncthreads();
+  align_block(ids, T * k, E, block_m, id_bits, offsets, sorted_pairs, pair_pos, active, tile_offsets);
+  if (threadIdx.x == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int TB>
@@ -281,4 +381,38 @@ extern "C" int moe_route(const uint16_t* x, const uint16_t* w_router, int T, int
   }
   timing_end(K_ROUTE, s);
   return check_launch("moe_route");
+}
+
+extern "C" int moe_route_align(const uint16_t* x, const uint16_t* w_router, int T, int d, int E, int k,
+                               int renormalize, int block_m, float* logits, int32_t* topk_ids, float* topk_weights,
+                               int32_t* expert_offsets, int32_t* sorted_pairs, int32_t* pair_pos,
+                               int32_t* active_experts, int32_t* tile_offsets, int32_t* counter, void* stream) {
+  clear_error();
+  MOE_CHECK_ARG(T >= 0 && d > 0 && E > 0 && k > 0 && block_m >= 0, MOE_ERR_INVALID_ARG,
+                "moe_route_align: bad sizes T=%d d=%d E=%d k=%d block_m=%d", T, d, E, k, block_m);
+  if (T == 0 || T > kRouteAlignMaxT || (int64_t)T * E > kRouteAlignMaxLogits) {
+    // nothing to route, or a step too large for one launch: the two separate calls
+    int rc = moe_route(x, w_router, T, d, E, k, renormalize, logits, topk_ids, topk_weights, stream);
+    if (rc) return rc;
+    return moe_align(topk_ids, T, k, E, block_m, expert_offsets, sorted_pairs, pair_pos, active_experts,
+                     tile_offsets, stream);
+  }
+  MOE_CHECK_ARG(E <= MOE_MAX_EXPERTS && k <= MOE_MAX_TOPK && k <= E && d % 8 == 0, MOE_ERR_UNSUPPORTED_SHAPE,
+                "moe_route_align: unsupported E=%d k=%d d=%d (E <= 1024, k <= min(E,16), d %% 8 == 0)", E, k, d);
+  MOE_CHECK_ARG(x && w_router && logits && topk_ids && topk_weights && expert_offsets && sorted_pairs && pair_pos &&
+                    active_experts && counter,
+                MOE_ERR_INVALID_ARG, "moe_route_align: null pointer");
+  MOE_CHECK_ARG(block_m == 0 || tile_offsets, MOE_ERR_INVALID_ARG, "moe_route_align: block_m > 0 needs tile_offsets");
+  MOE_CHECK_ARG(((uintptr_t)x % 16) == 0 && ((uintptr_t)w_router % 16) == 0 && ((uintptr_t)active_experts % 16) == 0,
+                MOE_ERR_INVALID_ARG, "moe_route_align: x, w_router and active_experts must be 16-byte aligned");
+  int bits = 0;
+  while ((1 << bits) < E) ++bits;
+  hipStream_t s = (hipStream_t)stream;
+  timing_begin(K_ROUTE, s);
+  hipLaunchKernelGGL(k_route_align, dim3((unsigned)ceil_div(E, kAlignWaves), (unsigned)T), dim3(kAlignThreads), 0, s,
+                     x, w_router, T, d, E, k, renormalize, block_m, bits, logits, topk_ids, topk_weights,
+                     expert_offsets, sorted_pairs, pair_pos, active_experts, block_m > 0 ? tile_offsets : nullptr,
+                     counter);
+  timing_end(K_ROUTE, s);
+  return check_launch("moe_route_align");
 }

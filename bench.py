@@ -9,8 +9,11 @@ activations, T tokens per step (headline T = 16).
 
 Prints one JSON line: MoE-layer tokens/s (T * layers / step time), the
 achieved algorithmic HBM GB/s, the roofline of the dominant kernel (grouped
-gate/up) timed with HIP events on its own stream, and the CPU oracle timed on a
-bounded sample of the same workload.
+gate/up) timed with HIP events on its own stream (its measured HBM traffic comes
+from the committed rocprofv3 counter summary under profiles/ when that was taken
+on the current kernel sources), a batched-prefill layer (T = 4096) with the MFMA
+roofline of its grouped gate/up kernel, and the CPU oracle timed on a bounded
+sample of the decode workload.
 """
 import argparse
 import json
@@ -25,6 +28,10 @@ if ROOT not in sys.path:
 
 METRIC = "MoE-layer tokens/s + achieved HBM GB/s (W4A16, OLMoE shape, T=1..4096)"
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "gateup_decode_olmoe_t16_hbm_counters.txt")
+COUNTED_SOURCES = ["w4a16_grouped_expert_amd/csrc/ffn_decode.hip", "w4a16_grouped_expert_amd/csrc/ffn_common.hpp",
+                   "w4a16_grouped_expert_amd/csrc/common.hpp"]
 
 
 def parse():
@@ -37,6 +44,7 @@ def parse():
     p.add_argument("--x-sets", type=int, default=8, help="distinct activation sets cycled over steps")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU-oracle baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--prefill-tokens", type=int, default=4096, help="tokens of the prefill measurement (0: skip)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain device copy of known size (for HBM counter calibration)")
     return p.parse_args()
@@ -186,6 +194,74 @@ def run_decode(dec, T, steps, warmup, x_sets):
     return res
 
 
+def measured_traffic():
+    """HBM bytes per launch of the decode gate/up kernel from the committed rocprofv3
+    counter summary, if it was taken on the kernel sources as they are now."""
+    import hashlib
+    try:
+        kv = {}
+        for line in open(COUNTERS_FILE):
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+        h = hashlib.sha256()
+        for f in COUNTED_SOURCES:
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        if kv.get("source_sha256") != h.hexdigest():
+            return None
+        return int(float(kv["traffic_bytes_per_launch"]))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def run_prefill(T, reps=5, warmup=2):
+    """One OLMoE-shaped layer at T tokens (batched prefill, uniform router): eager
+    forward passes with HIP events around each kernel; MFMA roofline of the grouped
+    gate/up kernel from its algorithmic flops (2 * T * k * d * 2I per launch)."""
+    import torch
+    import synth
+    import w4a16_grouped_expert_amd as moe
+    wl = synth.OLMOE_PREFILL
+    s = wl.shape
+    w13, w2 = synth.expert_weights(wl, 0, device="cuda")
+    bank, _ = moe.pack_experts(w13, w2)
+    del w13, w2
+    wr = synth.router_weight(wl, 0, device="cpu").cuda()
+    x = synth.activations(wl, T, 0, device="cuda")
+    layer = moe.MoELayer(wr, bank, s.I, s.k, T)
+    for _ in range(warmup):
+        layer.forward(x)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    moe.timing_reset()
+    moe.timing_enable(True)
+    t0.record()
+    for _ in range(reps):
+        layer.forward(x)
+    t1.record()
+    torch.cuda.synchronize()
+    moe.timing_enable(False)
+    ms = t0.elapsed_time(t1) / reps
+    kern = {}
+    for kname in ("route", "align", "gateup_prefill", "down_prefill", "combine"):
+        tot, n = moe.timing_read(kname)
+        if n:
+            kern[kname] = round(1e3 * tot / n, 3)
+    P = T * s.k
+    fl_gu, fl_dn = 2.0 * P * s.d * 2 * s.I, 2.0 * P * s.I * s.d
+    gu = fl_gu / (kern["gateup_prefill"] * 1e-6) / 1e12
+    dn = fl_dn / (kern["down_prefill"] * 1e-6) / 1e12
+    del layer, bank
+    torch.cuda.empty_cache()
+    return {"workload": f"olmoe_prefill: 1 MoE layer, d=2048, E=64, top-8, I=1024, W4 g128, T={T} tokens, "
+                        "uniform router (about T*8/64 tokens per expert)",
+            "tokens_per_s": round(T / (ms * 1e-3), 1), "ms_per_layer": round(ms, 4), "kernels_us": kern,
+            "down_tflops": round(dn, 1),
+            "roofline": {"bound": "mfma", "kernel": "k_prefill (gate/up)", "achieved": round(gu, 1),
+                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(gu / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "flops_per_launch": fl_gu, "avg_us": kern["gateup_prefill"]}}
+
+
 def cpu_baseline(wl, T, budget_s):
     """The CPU oracle on a bounded sample of the same workload: one OLMoE-shaped
     layer at T tokens (route, align, per-pair SwiGLU FFN in float64, combine),
@@ -260,9 +336,9 @@ def main():
             sweep[f"T={T}"]["gateup_gbps"] = r["gateup_bytes_per_launch"] / (kt * 1e-6) / 1e9
     kern = head["kernels"]["gateup_decode"]
     achieved = head["gateup_bytes_per_launch"] / (kern["avg_us"] * 1e-6) / 1e9
-    roofline = {"bound": "hbm", "kernel": "k_gateup_decode", "achieved": round(achieved, 1),
+    roofline = {"bound": "hbm", "kernel": "k_decode_persist (grouped gate/up)", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": None, "avg_us": round(kern["avg_us"], 3),
+                "traffic": measured_traffic(), "avg_us": round(kern["avg_us"], 3),
                 "bytes_per_launch": int(head["gateup_bytes_per_launch"])}
     out = {
         "metric": METRIC,
@@ -290,6 +366,10 @@ def main():
         "kernels_us": {k: round(v["avg_us"], 3) for k, v in head["kernels"].items()},
         "decode_sweep": sweep,
     }
+    del dec
+    torch.cuda.empty_cache()
+    if args.prefill_tokens > 0:
+        out["prefill"] = run_prefill(args.prefill_tokens)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.tokens, args.cpu_seconds)
     print(json.dumps(out))

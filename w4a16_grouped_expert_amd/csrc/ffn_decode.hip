@@ -51,7 +51,7 @@ struct GroupBuf {
   u32x4_t x[4];   // activation fragments, one per 32-wide K step
 };
 
-template <int RT, int NG, bool GATEUP, bool DENSE>
+template <int RT, int NG, bool GATEUP, bool DENSE, bool RING>
 __global__ __launch_bounds__(256) void k_decode_persist(FfnDev f, const uint16_t* __restrict__ hin,
                                                         uint16_t* __restrict__ hout, float* __restrict__ y,
                                                         int ksplit) {
@@ -169,13 +169,30 @@ __global__ __launch_bounds__(256) void k_decode_persist(FfnDev f, const uint16_t
       }
     };
 
-    GroupBuf<RT> buf[2];
-    for (int gc = g0; gc < g1; gc += NG) {
-      load(buf[0], gc);
+    if (RING) {
+      // ring of NG buffers: the loads of group g + NG - 1 are issued before group g
+      // is computed, so NG - 1 groups are in flight behind the one being multiplied
+      // (few tokens: little compute per group to hide the memory latency behind)
+      GroupBuf<RT> buf[NG];
 #pragma unroll
-      for (int j = 0; j < NG; ++j) {
-        if (j + 1 < NG) load(buf[(j + 1) & 1], gc + j + 1);
-        compute(buf[j & 1], (gc + j < g1) ? 1.f : 0.f);
+      for (int j = 0; j < NG - 1; ++j) load(buf[j], g0 + j);
+      for (int gc = g0; gc < g1; gc += NG) {
+#pragma unroll
+        for (int j = 0; j < NG; ++j) {
+          load(buf[(j + NG - 1) % NG], gc + j + NG - 1);
+          compute(buf[j], (gc + j < g1) ? 1.f : 0.f);
+        }
+      }
+    } else {
+      // two buffers, restarted every NG groups
+      GroupBuf<RT> buf[2];
+      for (int gc = g0; gc < g1; gc += NG) {
+        load(buf[0], gc);
+#pragma unroll
+        for (int j = 0; j < NG; ++j) {
+          if (j + 1 < NG) load(buf[(j + 1) & 1], gc + j + 1);
+          compute(buf[j & 1], (gc + j < g1) ? 1.f : 0.f);
+        }
       }
     }
 
@@ -382,7 +399,7 @@ __global__ __launch_bounds__(256) void k_ffn_decode(FfnDev f, const uint16_t* __
 }
 
 constexpr int kGateUpRT = 2, kDownRT = 4;
-constexpr int kPersistRT = 4, kPersistNG = 8;
+constexpr int kPersistRT = 4, kPersistNG = 8, kRingNG = 4;
 
 int decode_down_gpw(int I, int ksplit) {
   const int G = I / kGroup;
@@ -424,12 +441,17 @@ static void launch_nb(const FfnDev& f, uint16_t* h, float* y, int ksplit, hipStr
 int launch_decode(const FfnDev& f, uint16_t* h, float* y, int ksplit, int nb, hipStream_t s) {
   const int64_t umax = f.umax;
   if (f.T <= 16) {
-    auto kgu = k_decode_persist<kPersistRT, kPersistNG, true, true>;
-    auto kdn = k_decode_persist<kPersistRT, kPersistNG, false, false>;
+    // up to 4 tokens: a 4-deep ring of group loads; more tokens: double buffering
+    // (more compute per group covers the latency, and it keeps 3 waves per SIMD)
+    const bool ring = f.T <= 4;
+    auto kgu = ring ? k_decode_persist<kPersistRT, kRingNG, true, true, true>
+                    : k_decode_persist<kPersistRT, kPersistNG, true, true, false>;
+    auto kdn = ring ? k_decode_persist<kPersistRT, kRingNG, false, false, true>
+                    : k_decode_persist<kPersistRT, kPersistNG, false, false, false>;
     const int64_t items_gu = umax * (2 * f.I / (kTileRows * kPersistRT));
     const int64_t items_dn = umax * (f.d / (kTileRows * kPersistRT)) * ksplit;
-    const int64_t grid_gu = std::min<int64_t>(persistent_grid(kgu, 0), ceil_div(items_gu, 4));
-    const int64_t grid_dn = std::min<int64_t>(persistent_grid(kdn, 1), ceil_div(items_dn, 4));
+    const int64_t grid_gu = std::min<int64_t>(persistent_grid(kgu, ring ? 2 : 0), ceil_div(items_gu, 4));
+    const int64_t grid_dn = std::min<int64_t>(persistent_grid(kdn, ring ? 3 : 1), ceil_div(items_dn, 4));
     timing_begin(K_GATEUP_DECODE, s);
     hipLaunchKernelGGL(kgu, dim3((unsigned)grid_gu), dim3(256), 0, s, f, (const uint16_t*)nullptr, h, (float*)nullptr, 1);
     timing_end(K_GATEUP_DECODE, s);

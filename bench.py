@@ -45,6 +45,10 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU-oracle baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--prefill-tokens", type=int, default=4096, help="tokens of the prefill measurement (0: skip)")
+    p.add_argument("--prefill-sweep", default="512", help="extra prefill T values")
+    p.add_argument("--no-large", action="store_true", help="skip the large-expert shape")
+    p.add_argument("--no-slot-cache", action="store_true", help="skip the 16-slot cache workload")
+    p.add_argument("--slot-steps", type=int, default=24, help="timed steps of the slot-cache workload")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain device copy of known size (for HBM counter calibration)")
     return p.parse_args()
@@ -262,6 +266,134 @@ def run_prefill(T, reps=5, warmup=2):
                          "flops_per_launch": fl_gu, "avg_us": kern["gateup_prefill"]}}
 
 
+def run_large(Ts, reps=10, warmup=3):
+    """Large-expert shape (d=4096, E=8, top-2, I=14336, 4 layers, all resident): per T
+    the 4-layer step timed with HIP events; HBM fraction on algorithmic bytes (distinct
+    experts x blob + router + activations) and MFMA fraction on flops."""
+    import torch
+    import synth
+    import w4a16_grouped_expert_amd as moe
+    wl = synth.LARGE
+    s = wl.shape
+    layers = []
+    for l in range(wl.layers):
+        w13, w2 = synth.expert_weights(wl, l, device="cuda")
+        bank, lay = moe.pack_experts(w13, w2)
+        del w13, w2
+        wr = synth.router_weight(wl, l, device="cpu").cuda()
+        layers.append(moe.MoELayer(wr, bank, s.I, s.k, max(Ts)))
+    torch.cuda.empty_cache()
+    blob = lay["blob_bytes"]
+    res = {}
+    for T in Ts:
+        xs = [synth.activations(wl, T, l, device="cuda") for l in range(wl.layers)]
+        for _ in range(warmup):
+            for L, x in zip(layers, xs):
+                L.forward(x)
+        torch.cuda.synchronize()
+        U = [int(L.align.active[0].item()) for L in layers]
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            for L, x in zip(layers, xs):
+                L.forward(x)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / reps
+        by = sum(U) * blob + wl.layers * (s.E * s.d * 2 + 2 * T * s.d * 2)
+        fl = wl.layers * T * (s.k * 6 * s.d * s.I + 2 * s.d * s.E)
+        res[f"T={T}"] = {"tokens_per_s": round(T * wl.layers / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
+                         "hbm_gbps": round(by / (ms * 1e-3) / 1e9, 1),
+                         "hbm_frac": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                         "mfma_frac": round(fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "mean_distinct_experts": sum(U) / len(U)}
+    del layers
+    torch.cuda.empty_cache()
+    return {"workload": "large_expert: 4 MoE layers, d=4096, E=8, top-2, I=14336, W4 g128 experts resident; "
+                        "whole-step time (route + align + grouped FFN + combine) per T", **res}
+
+
+def run_slot_cache(steps, warmup=8, T=16, S=16):
+    """16-slot expert cache (OLMoE shape, 16 layers, Zipf(1.2) popularity with AR(1)
+    step locality): experts in pinned host memory, S device slots per layer, misses
+    copied by hipMemcpyAsync on a side stream before each FFN round."""
+    import torch
+    import synth
+    import w4a16_grouped_expert_amd as moe
+    wl = synth.OLMOE_SLOT
+    s = wl.shape
+    layers = []
+    for l in range(wl.layers):
+        w13, w2 = synth.expert_weights(wl, l, device="cuda")
+        bank, lay = moe.pack_experts(w13, w2)
+        del w13, w2
+        B = lay["blob_bytes"]
+        store = torch.empty((s.E, B), dtype=torch.uint8, pin_memory=True)
+        store.copy_(bank)
+        del bank
+        slots = torch.zeros((S, B), dtype=torch.uint8, device="cuda")
+        wr = synth.router_weight(wl, l).cuda()
+        layers.append({"wr": wr, "store": store, "slots": slots, "cache": moe.SlotCache(s.E, S, B, store, slots),
+                       "table": torch.full((s.E,), -1, dtype=torch.int32, device="cuda")})
+    torch.cuda.empty_cache()
+    route = moe.alloc_route(T, s.E, s.k, "cuda")
+    al = moe.alloc_align(T, s.k, s.E, "cuda")
+    counter = moe.alloc_counter("cuda")
+    ws = moe.alloc_workspace(T, s.d, s.I, s.E, s.k, moe.MODE_DECODE)
+    out = torch.empty((T, s.d), dtype=torch.bfloat16, device="cuda")
+    main = torch.cuda.current_stream()
+    copy = torch.cuda.Stream()
+    done, ffn_done = torch.cuda.Event(), torch.cuda.Event()
+    ffn_done.record(main)
+    seqs = [[x.cuda() for x in synth.ar1_activation_sequence(wl, T, l, warmup + steps, device="cpu")]
+            for l in range(wl.layers)]
+
+    def step(st):
+        rounds = misses = 0
+        for l, L in enumerate(layers):
+            x = seqs[l][st]
+            moe.moe_route_align_into(x, L["wr"], s.k, route, al, counter)
+            pending = {w[0] for w in moe.active_experts(al)}  # the one D2H sync per layer
+            while pending:
+                got, nh, nm = L["cache"].load(pending, L["table"], copy, ffn_done, done)
+                main.wait_event(done)
+                pending -= got
+                moe.moe_w4a16_grouped_ffn_into(x, route, al, L["slots"], s.I, out, ws, moe.MODE_DECODE,
+                                               not pending, L["table"])
+                ffn_done.record(main)
+                rounds += 1
+                misses += nm
+        return rounds, misses
+
+    for st in range(warmup):
+        step(st)
+    torch.cuda.synchronize()
+    h0 = [L["cache"].state()[1:] for L in layers]
+    t0 = time.perf_counter()
+    rounds = misses = 0
+    for st in range(warmup, warmup + steps):
+        r, m = step(st)
+        rounds += r
+        misses += m
+    torch.cuda.synchronize()
+    sec = time.perf_counter() - t0
+    h1 = [L["cache"].state()[1:] for L in layers]
+    hits = sum(b[0] - a[0] for a, b in zip(h0, h1))
+    miss = sum(b[1] - a[1] for a, b in zip(h0, h1))
+    for L in layers:
+        L["cache"].close()
+    res = {"workload": f"olmoe_slot16: 16 MoE layers, d=2048, E=64, top-8, I=1024, W4 g128; 64 experts per layer in "
+                       f"pinned host memory, {S} device slots per layer, Zipf(1.2) popularity, AR(1) locality, T={T}",
+           "tokens_per_s": round(steps * T * wl.layers / sec, 1), "ms_per_step": round(1e3 * sec / steps, 3),
+           "hit_rate": round(hits / max(1, hits + miss), 4), "misses_per_step": round(miss / steps, 2),
+           "rounds_per_layer": round(rounds / (steps * wl.layers), 3),
+           "h2d_gbps": round(miss * B / sec / 1e9, 2),
+           "timing": "wall clock over the timed steps (host round trip per layer for the needed set included)"}
+    del layers
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(wl, T, budget_s):
     """The CPU oracle on a bounded sample of the same workload: one OLMoE-shaped
     layer at T tokens (route, align, per-pair SwiGLU FFN in float64, combine),
@@ -370,6 +502,17 @@ def main():
     torch.cuda.empty_cache()
     if args.prefill_tokens > 0:
         out["prefill"] = run_prefill(args.prefill_tokens)
+        extra = {}
+        for T in [int(t) for t in args.prefill_sweep.split(",") if t]:
+            r = run_prefill(T)
+            extra[f"T={T}"] = {k: r[k] for k in ("tokens_per_s", "ms_per_layer", "kernels_us")}
+            extra[f"T={T}"]["gateup_mfma_frac"] = r["roofline"]["frac"]
+        if extra:
+            out["prefill_sweep"] = extra
+    if not args.no_large:
+        out["large_expert"] = run_large(synth.LARGE.tokens)
+    if not args.no_slot_cache:
+        out["slot_cache"] = run_slot_cache(args.slot_steps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.tokens, args.cpu_seconds)
     print(json.dumps(out))

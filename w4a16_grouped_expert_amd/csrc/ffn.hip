@@ -18,21 +18,40 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, in
   const int64_t t = blockIdx.x / nchunks;
   const int n = ((blockIdx.x % nchunks) * 256 + threadIdx.x) * 4;
   if (n >= d) return;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
-    const int64_t pos = pair_pos[t * k + j];
-    if (pos < 0) continue;  // pair dropped by moe_align (expert id out of range)
-    const float wj = w[t * k + j];
-    f32x4_t v = *reinterpret_cast<const f32x4_t*>(y + pos * d + n);
-    for (int s = 1; s < ksplit; ++s) {
-      const f32x4_t p = *reinterpret_cast<const f32x4_t*>(y + ((int64_t)s * P + pos) * d + n);
-      v[0] += p[0];
-      v[1] += p[1];
-      v[2] += p[2];
-      v[3] += p[3];
-    }
+  // every position and weight first, then every row slice: two dependent round
+  // trips per thread instead of two per routed slot
+  int64_t pos[MOE_MAX_TOPK];
+  float wj[MOE_MAX_TOPK];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[r] = fmaf(wj, v[r], acc[r]);
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+    pos[j] = j < k ? pair_pos[t * k + j] : -1;  // -1: pair dropped by moe_align (expert id out of range)
+    wj[j] = j < k ? w[t * k + j] : 0.f;
+  }
+  f32x4_t v[MOE_MAX_TOPK];
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j)
+    v[j] = pos[j] >= 0 ? *reinterpret_cast<const f32x4_t*>(y + pos[j] * d + n) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int s = 1; s < ksplit; ++s) {
+    f32x4_t p[MOE_MAX_TOPK];
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j)
+      p[j] = pos[j] >= 0 ? *reinterpret_cast<const f32x4_t*>(y + ((int64_t)s * P + pos[j]) * d + n)
+                         : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+      v[j][0] += p[j][0];
+      v[j][1] += p[j][1];
+      v[j][2] += p[j][2];
+      v[j][3] += p[j][3];
+    }
+  }
+  // the k routed outputs in slot order, fp32, one bf16 rounding
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+    if (pos[j] < 0) continue;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = fmaf(wj[j], v[j][r], acc[r]);
   }
   u32x2_t o = {f32_to_bf16_bits(acc[0]) | (f32_to_bf16_bits(acc[1]) << 16),
                f32_to_bf16_bits(acc[2]) | (f32_to_bf16_bits(acc[3]) << 16)};

@@ -67,6 +67,11 @@ __global__ __launch_bounds__(256) void k_decode_persist(FfnDev f, const uint16_t
   const int U = f.active[0];
   const int gs_per = (G + ksplit - 1) / ksplit;
 
+  // the first item's record is in flight while the routing table is staged
+  const i32x4_t* work = reinterpret_cast<const i32x4_t*>(f.active + 4);
+  int item = worker;
+  i32x4_t next_w = work[min(item / per_u, f.umax - 1)];
+
   // DENSE: the step's routing table (token -> its k experts) staged once in LDS
   __shared__ int s_ids[16][MOE_MAX_TOPK];
   if (DENSE) {
@@ -83,10 +88,6 @@ __global__ __launch_bounds__(256) void k_decode_persist(FfnDev f, const uint16_t
   const __amdgpu_buffer_rsrc_t xres =
       GATEUP ? __builtin_amdgcn_make_buffer_rsrc((void*)f.x, (short)0, (int)(f.T * f.d * 2), kBufferRsrcWord3)
              : __builtin_amdgcn_make_buffer_rsrc((void*)hin, (short)0, (int)(f.P * f.I * 2), kBufferRsrcWord3);
-  const i32x4_t* work = reinterpret_cast<const i32x4_t*>(f.active + 4);
-
-  int item = worker;
-  i32x4_t next_w = work[min(item / per_u, f.umax - 1)];
   for (; item < n_items; item += n_workers) {
     const int u = item / per_u;
     const int rem = item % per_u;
@@ -216,6 +217,163 @@ __global__ __launch_bounds__(256) void k_decode_persist(FfnDev f, const uint16_t
           const int n = kTileRows * (RT * stripe + r) + 4 * kq;
           *reinterpret_cast<f32x4_t*>(yout + (int64_t)out_row * f.d + n) = tot[r];
         }
+      }
+    }
+  }
+}
+
+// Grouped gate/up + SwiGLU for steps of at most 16 tokens, the activations shared
+// through LDS.  The 16 MFMA columns are the step's tokens (rows past T read as
+// zeros), the same for every expert, so a workgroup of 8 wavefronts stages the
+// whole activation block once, already in B-fragment order (fragment (g, i) of
+// lane l at (4g + i) * 64 + l: one conflict-free 16-byte LDS read per lane), with
+// the per-token group sums sum_k x_k that the biased decode needs, formed by the
+// same all-ones MFMA as elsewhere.  After that the only global reads are the
+// packed weights and their scales: each wavefront is a worker over (expert,
+// stripe of RT = 2 tiles = 16 gate rows + the matching 16 up rows) items with a
+// ring of NB group loads, so twice as many independent weight streams as 4-tile
+// stripes, which the HBM serves at a higher rate.  The first item's weight loads
+// are issued before the staging, whose latency they hide.
+template <int RT, int NB, int MAXG>
+__global__ __launch_bounds__(512, 4) void k_gateup_dense(FfnDev f, uint16_t* __restrict__ hout) {
+  constexpr int kWaves = 8;
+  const int G = f.d / kGroup;
+  const int n_stripes = 2 * f.I / (kTileRows * RT);
+  const int n_items = f.umax * n_stripes;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = lane_id();
+  const int col = lane & 15, kq = lane >> 4;
+  const int worker = blockIdx.x * kWaves + wave, n_workers = gridDim.x * kWaves;
+  const i32x4_t* work = reinterpret_cast<const i32x4_t*>(f.active + 4);
+  const int U = f.active[0];
+  const int64_t tile_stride_c = (int64_t)G * kTileBytes;
+  const int64_t tile_stride_s = (int64_t)G * kTileRows;
+
+  struct Buf {
+    u32x4_t c[RT];
+    u32x2_t s[RT];
+  };
+  Buf buf[NB];
+  const uint8_t* codes = nullptr;
+  const uint16_t* scales = nullptr;
+  // past the item's last group the loads repeat group G - 1 and the group's
+  // weight is 0, so no load sits under a branch and the wait counts stay exact
+  auto load = [&](Buf& b, int g) {
+    const int gl = min(g, G - 1);
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      b.c[r] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4_t*>(codes + r * tile_stride_c + (int64_t)gl * kTileBytes));
+      b.s[r] = *reinterpret_cast<const u32x2_t*>(scales + r * tile_stride_s + gl * kTileRows);
+    }
+  };
+  // Item setup: its record, its weight pointers and the loads of its first NB - 1
+  // groups.  Returns the expert (-1: no item left for this worker).
+  int item = worker, row0 = 0;
+  i32x4_t w4 = work[min(item / n_stripes, f.umax - 1)];
+  auto start_item = [&]() -> int {
+    for (; item < n_items; item += n_workers) {
+      const i32x4_t cur = w4;
+      w4 = work[min((item + n_workers) / n_stripes, f.umax - 1)];  // next record, in flight now
+      if (item / n_stripes >= U) break;  // items are visited in increasing u: nothing active remains
+      const uint8_t* blob = f.blob(cur[0]);
+      if (!blob) continue;
+      const int stripe = item % n_stripes;
+      codes = blob + f.off_w13_codes + (int64_t)(RT * stripe) * G * kTileBytes + 16 * lane;
+      scales = reinterpret_cast<const uint16_t*>(blob + f.off_w13_scales) + (int64_t)(RT * stripe) * G * kTileRows +
+               4 * kq;
+#pragma unroll
+      for (int j = 0; j < NB - 1; ++j) load(buf[j], j);
+      row0 = cur[1];
+      return cur[0];
+    }
+    item = n_items;
+    return -1;
+  };
+  int e = start_item();
+
+  __shared__ u32x4_t s_x[MAXG * 4 * 64];
+  __shared__ float s_xs[MAXG * 16];
+  __shared__ int s_ids[16][MOE_MAX_TOPK];
+  {
+    const u32x4_t ones_w = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    const bf16x8_t ones = as_bf16x8(ones_w);
+    const __amdgpu_buffer_rsrc_t xres =
+        __builtin_amdgcn_make_buffer_rsrc((void*)f.x, (short)0, (int)(f.T * f.d * 2), kBufferRsrcWord3);
+    const uint32_t xoff = (uint32_t)(col * f.d + 8 * kq) * 2u;
+    for (int g = wave; g < G; g += kWaves) {
+      u32x4_t xv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        xv[i] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xres, xoff + (uint32_t)(g * kGroup + 32 * i) * 2u, 0, 0));
+      f32x4_t as = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s_x[(4 * g + i) * 64 + lane] = xv[i];
+        as = mfma16x16x32(ones, as_bf16x8(xv[i]), as);
+      }
+      if (lane < 16) s_xs[g * 16 + lane] = as[0];  // C column = lane, every row the same sum
+    }
+    for (int i = threadIdx.x; i < 16 * MOE_MAX_TOPK; i += kWaves * 64) {
+      const int t = i / MOE_MAX_TOPK, j = i % MOE_MAX_TOPK;
+      s_ids[t][j] = (j < f.k && t < f.T) ? f.topk_ids[t * f.k + j] : -1;
+    }
+  }
+  __syncthreads();
+  const uint32_t kMask = vgpr_const(0x00780078u), kOne = vgpr_const(0x3F803F80u);
+
+  while (e >= 0) {
+    const int stripe = item % n_stripes;
+    bool routed = false;
+    for (int j = 0; j < f.k; ++j) routed |= (s_ids[col][j] == e);
+    const uint32_t colmask = (uint32_t)__ballot(routed) & 0xFFFFu;
+    const int out_row = row0 + __popc(colmask & ((1u << col) - 1u));
+    const int cur_stripe = stripe;
+
+    f32x4_t tot[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) tot[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](const Buf& b, int g) {
+      const int gl = min(g, G - 1);
+      const float gv = g < G ? 1.f : 0.f;
+      const float xs = -24.f * s_xs[gl * 16 + col];
+      f32x4_t acc[RT];
+#pragma unroll
+      for (int r = 0; r < RT; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x8_t xv = as_bf16x8(s_x[(4 * gl + i) * 64 + lane]);
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+          acc[r] = mfma16x16x32(as_bf16x8(decode_word_biased(b.c[r][i], kMask, kOne)), xv, acc[r]);
+      }
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        const float s4[4] = {__uint_as_float(b.s[r][0] << 16), __uint_as_float(b.s[r][0] & 0xFFFF0000u),
+                             __uint_as_float(b.s[r][1] << 16), __uint_as_float(b.s[r][1] & 0xFFFF0000u)};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) tot[r][q] = fmaf(gv * s4[q], fmaf(16.f, acc[r][q], xs), tot[r][q]);
+      }
+    };
+    for (int gc = 0; gc < G; gc += NB) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        load(buf[(j + NB - 1) % NB], gc + j + NB - 1);
+        compute(buf[j], gc + j);
+      }
+    }
+    // the next item's first loads go out before this item's stores
+    item += n_workers;
+    e = start_item();
+#pragma unroll
+    for (int p = 0; p < RT / 2; ++p) {
+      uint32_t hv[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) hv[q] = f32_to_bf16_bits(silu_f32(tot[2 * p][q]) * tot[2 * p + 1][q]);
+      if (routed) {
+        const int hcol = kTileRows * ((RT / 2) * cur_stripe + p) + 4 * kq;
+        u32x2_t o = {hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16)};
+        *reinterpret_cast<u32x2_t*>(hout + (int64_t)out_row * f.I + hcol) = o;
       }
     }
   }
@@ -399,7 +557,8 @@ __global__ __launch_bounds__(256) void k_ffn_decode(FfnDev f, const uint16_t* __
 }
 
 constexpr int kGateUpRT = 2, kDownRT = 4;
-constexpr int kPersistRT = 4, kPersistNG = 8, kRingNG = 4;
+constexpr int kPersistRT = 4, kPersistNG = 8, kRingRT = 2, kRingNG = 4;
+constexpr int kDenseRT = 2, kDenseNB = 4;  // LDS-activation gate/up: tiles per stripe, ring depth
 
 int decode_down_gpw(int I, int ksplit) {
   const int G = I / kGroup;
@@ -407,15 +566,15 @@ int decode_down_gpw(int I, int ksplit) {
   return (gs_per + 3) / 4 <= 2 ? 2 : 4;
 }
 
-// Resident 256-thread blocks per CU for a kernel, times the CU count (cached).
+// Resident blocks per CU for a kernel, times the CU count (cached per slot).
 template <typename Kern>
-static int persistent_grid(Kern kern, int slot) {
+static int persistent_grid(Kern kern, int slot, int threads = 256) {
   static int cached[8] = {0};
   if (!cached[slot]) {
     int dev = 0, cus = 0, per_cu = 0;
     (void)hipGetDevice(&dev);
     (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, 0);
+    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, 0);
     cached[slot] = std::max(1, cus) * std::max(1, per_cu);
   }
   return cached[slot];
@@ -441,19 +600,32 @@ static void launch_nb(const FfnDev& f, uint16_t* h, float* y, int ksplit, hipStr
 int launch_decode(const FfnDev& f, uint16_t* h, float* y, int ksplit, int nb, hipStream_t s) {
   const int64_t umax = f.umax;
   if (f.T <= 16) {
-    // up to 4 tokens: a 4-deep ring of group loads; more tokens: double buffering
-    // (more compute per group covers the latency, and it keeps 3 waves per SIMD)
+    // gate/up: activations in LDS when they fit (d <= 4096), else read per group;
+    // down: up to 4 tokens a 4-deep ring of group loads over 2-tile stripes (twice
+    // the weight streams), more tokens double buffering over 4-tile stripes (more
+    // compute per group covers the latency, and it keeps 3 waves per SIMD)
     const bool ring = f.T <= 4;
-    auto kgu = ring ? k_decode_persist<kPersistRT, kRingNG, true, true, true>
-                    : k_decode_persist<kPersistRT, kPersistNG, true, true, false>;
-    auto kdn = ring ? k_decode_persist<kPersistRT, kRingNG, false, false, true>
+    auto kdn = ring ? k_decode_persist<kRingRT, kRingNG, false, false, true>
                     : k_decode_persist<kPersistRT, kPersistNG, false, false, false>;
-    const int64_t items_gu = umax * (2 * f.I / (kTileRows * kPersistRT));
-    const int64_t items_dn = umax * (f.d / (kTileRows * kPersistRT)) * ksplit;
-    const int64_t grid_gu = std::min<int64_t>(persistent_grid(kgu, ring ? 2 : 0), ceil_div(items_gu, 4));
+    const int64_t items_dn = umax * (f.d / (kTileRows * (ring ? kRingRT : kPersistRT))) * ksplit;
     const int64_t grid_dn = std::min<int64_t>(persistent_grid(kdn, ring ? 3 : 1), ceil_div(items_dn, 4));
     timing_begin(K_GATEUP_DECODE, s);
-    hipLaunchKernelGGL(kgu, dim3((unsigned)grid_gu), dim3(256), 0, s, f, (const uint16_t*)nullptr, h, (float*)nullptr, 1);
+    if (f.d <= 32 * kGroup) {
+      const int G = f.d / kGroup;
+      // d <= 2048: 2 workgroups per CU and 4 wavefronts per SIMD; d <= 4096: 1 (LDS)
+      auto kgu = G <= 16 ? k_gateup_dense<kDenseRT, kDenseNB, 16> : k_gateup_dense<kDenseRT, kDenseNB, 32>;
+      const int slot = G <= 16 ? 4 : 5;
+      const int64_t items_gu = umax * (2 * f.I / (kTileRows * kDenseRT));
+      const int64_t grid_gu = std::min<int64_t>(persistent_grid(kgu, slot, 512), ceil_div(items_gu, 8));
+      hipLaunchKernelGGL(kgu, dim3((unsigned)grid_gu), dim3(512), 0, s, f, h);
+    } else {
+      auto kgu = ring ? k_decode_persist<kPersistRT, kRingNG, true, true, true>
+                      : k_decode_persist<kPersistRT, kPersistNG, true, true, false>;
+      const int64_t items_gu = umax * (2 * f.I / (kTileRows * kPersistRT));
+      const int64_t grid_gu = std::min<int64_t>(persistent_grid(kgu, ring ? 2 : 0), ceil_div(items_gu, 4));
+      hipLaunchKernelGGL(kgu, dim3((unsigned)grid_gu), dim3(256), 0, s, f, (const uint16_t*)nullptr, h,
+                         (float*)nullptr, 1);
+    }
     timing_end(K_GATEUP_DECODE, s);
     timing_begin(K_DOWN_DECODE, s);
     hipLaunchKernelGGL(kdn, dim3((unsigned)grid_dn), dim3(256), 0, s, f, (const uint16_t*)h, (uint16_t*)nullptr, y, ksplit);

@@ -21,6 +21,21 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
+// Number of the token's E logits (row, in LDS) that beat (v, e): 16 broadcast
+// reads are issued before their compares, so the LDS latency is paid once per 16.
+__device__ __forceinline__ int rank_in_row(const float* row, int E, float v, int e) {
+  int rank = 0, o = 0;
+  for (; o + 16 <= E; o += 16) {
+    float r[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) r[u] = row[o + u];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) rank += better(r[u], o + u, v, e) ? 1 : 0;
+  }
+  for (; o < E; ++o) rank += better(row[o], o, v, e) ? 1 : 0;
+  return rank;
+}
+
 // Top-k of one token's E logits (in LDS) by one wavefront: lane l owns experts
 // l, l+64, ...; k rounds of a wave-wide (value desc, index asc) argmax.
 __device__ __forceinline__ void topk_wave(const float* __restrict__ lg, int E, int k, int renormalize, int t,
@@ -141,8 +156,7 @@ __global__ __launch_bounds__(1024) void k_route_token(const uint16_t* __restrict
   for (int e = tid; e < E; e += 1024) {
     const float v = s_logit[e];
     logits[(int64_t)t * E + e] = v;
-    int rank = 0;
-    for (int o = 0; o < E; ++o) rank += better(s_logit[o], o, v, e) ? 1 : 0;
+    const int rank = rank_in_row(s_logit, E, v, e);
     if (rank < k) {
       s_sel_v[rank] = v;
       s_sel_i[rank] = e;
@@ -236,21 +250,22 @@ __global__ __launch_bounds__(kAlignThreads) void k_route_align(
   for (int i = threadIdx.x; i < T * E; i += kAlignThreads) {
     const int tt = i / E, ee = i - tt * E;
     const float v = s_lg[i];
-    const float* row = s_lg + tt * E;
-    int rank = 0;
-    for (int o = 0; o < E; ++o) rank += better(row[o], o, v, ee) ? 1 : 0;
+    const int rank = rank_in_row(s_lg + tt * E, E, v, ee);
     if (rank < k) {
       s_sel_v[tt][rank] = v;
       s_sel_i[tt][rank] = ee;
     }
   }
   __syncthreads();
-  // weights, with the sums of topk_wave in the same order
+  // weights, with the sums of topk_wave in the same order; lane j < k holds the
+  // exponential of selection j, the renormalising sum runs over j in order
+  __shared__ int32_t s_ids[kRouteAlignMaxT * MOE_MAX_TOPK];
   for (int tt = wave; tt < T; tt += kAlignWaves) {
     const float lmax = s_sel_v[tt][0];
+    const float ex = lane < k ? expf(s_sel_v[tt][lane] - lmax) : 0.f;
     float den = 0.f;
     if (renormalize) {
-      for (int j = 0; j < k; ++j) den += expf(s_sel_v[tt][j] - lmax);
+      for (int j = 0; j < k; ++j) den += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
     } else {
       float part = 0.f;
       for (int ee = lane; ee < E; ee += 64) part += expf(s_lg[tt * E + ee] - lmax);
@@ -259,12 +274,14 @@ __global__ __launch_bounds__(kAlignThreads) void k_route_align(
       den = part;
     }
     if (lane < k) {
-      ids[(int64_t)tt * k + lane] = s_sel_i[tt][lane];
-      weights[(int64_t)tt * k + lane] = expf(s_sel_v[tt][lane] - lmax) / den;
+      const int id = s_sel_i[tt][lane];
+      s_ids[tt * k + lane] = id;
+      ids[(int64_t)tt * k + lane] = id;
+      weights[(int64_t)tt * k + lane] = ex / den;
     }
   }
   __syncthreads();
-  align_block(ids, T * k, E, block_m, id_bits, offsets, sorted_pairs, pair_pos, active, tile_offsets);
+  align_block(s_ids, T * k, E, block_m, id_bits, offsets, sorted_pairs, pair_pos, active, tile_offsets);
   if (threadIdx.x == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 

@@ -128,22 +128,23 @@ int moe_align(const int32_t* topk_ids, int T, int k, int E, int block_m,
 
 /*
  * moe_route_align -- moe_route followed by moe_align, in one launch for steps of
- * at most 128 tokens with T * E <= 16384 (the decode case); other steps (and
- * T == 0) run the two calls above.  Outputs are bit-identical to moe_route +
- * moe_align.
+ * at most 128 tokens (the decode case); other steps (and T == 0) run the two
+ * calls above.  Outputs are bit-identical to moe_route + moe_align.
  *
  *  Arguments: those of moe_route and moe_align, plus
- *  counter  one int32 in device memory, owned by the caller: it must hold 0
- *           before the first call and every call leaves it at 0.  Calls that share
- *           a counter must not overlap (same stream, or otherwise ordered).
+ *  counters  MOE_ROUTE_ALIGN_COUNTERS int32 in device memory, owned by the
+ *            caller: they must hold 0 before the first call and every call leaves
+ *            them at 0.  Calls that share counters must not overlap (same stream,
+ *            or otherwise ordered).
  *  Limits and errors: those of moe_route and moe_align; x, w_router and
  *  active_experts 16-byte aligned.
  */
+#define MOE_ROUTE_ALIGN_COUNTERS 256
 int moe_route_align(const uint16_t* x, const uint16_t* w_router, int T, int d, int E, int k,
                     int renormalize, int block_m, float* logits, int32_t* topk_ids,
                     float* topk_weights, int32_t* expert_offsets, int32_t* sorted_pairs,
                     int32_t* pair_pos, int32_t* active_experts, int32_t* tile_offsets,
-                    int32_t* counter, void* stream);
+                    int32_t* counters, void* stream);
 
 /*
  * moe_w4a16_grouped_ffn -- the fused grouped expert pass (ExactMoE, Abstract:

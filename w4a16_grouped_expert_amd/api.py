@@ -148,9 +148,12 @@ def moe_align(ids, E, block_m=0, stream=None) -> AlignOut:
     return moe_align_into(ids, E, alloc_align(T, k, E, ids.device, block_m), stream)
 
 
+ROUTE_ALIGN_COUNTERS = 256  # MOE_ROUTE_ALIGN_COUNTERS in w4a16_moe.h
+
+
 def alloc_counter(device) -> torch.Tensor:
-    """A zeroed device counter for moe_route_align (each call leaves it zero)."""
-    return torch.zeros(4, dtype=torch.int32, device=device)
+    """Zeroed device counters for moe_route_align (each call leaves them zero)."""
+    return torch.zeros(ROUTE_ALIGN_COUNTERS, dtype=torch.int32, device=device)
 
 
 def moe_route_align_into(x, w_router, k, route: RouteOut, al: AlignOut, counter: torch.Tensor, renormalize=True,
@@ -159,6 +162,8 @@ def moe_route_align_into(x, w_router, k, route: RouteOut, al: AlignOut, counter:
     _need(x, torch.bfloat16, "x")
     _need(w_router, torch.bfloat16, "w_router")
     _need(counter, torch.int32, "counter")
+    if counter.numel() < ROUTE_ALIGN_COUNTERS:
+        raise ValueError(f"moe_route_align needs {ROUTE_ALIGN_COUNTERS} counters, got {counter.numel()}")
     T, d = x.shape
     E = w_router.shape[0]
     check("moe_route_align", lib().moe_route_align(

@@ -3,7 +3,7 @@
 // Expert Counts: ExactMoE for Memory-Efficient W4A16 Inference", Abstract).  A
 // stable counting sort in one 1024-thread workgroup:
 //
-//  1. histogram of expert ids (LDS atomics; the counts do not depend on order);
+//  1. expert counts;
 //  2. one block-wide scan gives the offsets, the compacted work list of active
 //     experts ({id, first position, count} each) and the per-expert tile counts;
 //  3. placement, 1024 pairs per pass in pair order: inside a wavefront the lanes
@@ -11,6 +11,7 @@
 //     rank is a popcount of the lower lanes; the per-wave counts are exchanged in
 //     LDS so each wavefront adds the counts of the earlier wavefronts of the pass
 //     and of the earlier passes.  Every pair lands at the unique stable position.
+// With at most 1024 pairs the per-wavefront counts of step 3 also give step 1.
 //
 // Shared by moe_align (its own kernel) and moe_route_align (the last workgroup of
 // the router kernel).
@@ -23,54 +24,60 @@ namespace moe {
 constexpr int kAlignThreads = 1024;
 constexpr int kAlignWaves = kAlignThreads / 64;
 
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(v, off);
-    if (lane >= off) v += o;
-  }
+// Inclusive prefix sum over the 64 lanes of a wavefront with DPP moves: shifts by
+// 1, 2, 4, 8 inside each 16-lane row (lanes with no source in the row add 0), then
+// row 0's total is broadcast into row 1 and row 2's into row 3, and the total of
+// rows 0-1 into rows 2-3.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
   return v;
 }
 
-// The whole permutation, run by one workgroup of kAlignThreads threads.
-__device__ __forceinline__ void align_block(const int32_t* __restrict__ ids, int P, int E, int block_m, int id_bits,
-                                            int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
-                                            int32_t* __restrict__ pair_pos, int32_t* __restrict__ active,
-                                            int32_t* __restrict__ tile_offsets) {
-  __shared__ int s_count[MOE_MAX_EXPERTS];
-  __shared__ int s_off[MOE_MAX_EXPERTS];
-  __shared__ uint16_t s_wcnt[kAlignWaves][MOE_MAX_EXPERTS];
+// Pairs of one wavefront that carry the same expert: ballots over the id bits
+// leave the mask of lanes with this lane's expert; the lane's rank is the number
+// of such lanes below it.
+struct LaneGroup {
+  int rank, cnt;
+};
+__device__ __forceinline__ LaneGroup lane_group(int e, bool valid, int id_bits, int lane) {
+  uint64_t m = __ballot(valid);
+  for (int b = 0; b < id_bits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t bb = __ballot(valid && bit);
+    m &= bit ? bb : ~bb;
+  }
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  return LaneGroup{(int)__popcll(m & lt_mask), (int)__popcll(m)};
+}
+
+// Block-wide scan over the experts (one per thread, E <= kAlignThreads) of the
+// pair counts: offsets, the compacted work list of active experts and the
+// per-expert tile counts.  Every thread must call it (it synchronises when E > 64).
+__device__ __forceinline__ void align_scan(int c, int E, int block_m, int tid, int lane, int wave,
+                                           int32_t* __restrict__ s_off, int32_t* __restrict__ offsets,
+                                           int32_t* __restrict__ active, int32_t* __restrict__ tile_offsets) {
   __shared__ int s_tot[3][kAlignWaves];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int e = tid; e < E; e += kAlignThreads) {
-    s_count[e] = 0;
-#pragma unroll
-    for (int w = 0; w < kAlignWaves; ++w) s_wcnt[w][e] = 0;
-  }
-  __syncthreads();
-  for (int p = tid; p < P; p += kAlignThreads) {
-    const int e = ids[p];
-    if (e >= 0 && e < E) atomicAdd(&s_count[e], 1);
-  }
-  __syncthreads();
-
-  // block scan over experts (E <= 1024: one expert per thread)
-  const int c = tid < E ? s_count[tid] : 0;
   const int a = c > 0 ? 1 : 0;
   const int tl = (block_m > 0) ? (c + block_m - 1) / block_m : 0;
-  int ic = wave_incl_scan(c, lane), ia = wave_incl_scan(a, lane), it = wave_incl_scan(tl, lane);
-  if (lane == 63) {
-    s_tot[0][wave] = ic;
-    s_tot[1][wave] = ia;
-    s_tot[2][wave] = it;
-  }
-  __syncthreads();
+  const int ic = wave_incl_scan(c), ia = wave_incl_scan(a), it = wave_incl_scan(tl);
   int bc = 0, ba = 0, bt = 0;
-  for (int w = 0; w < wave; ++w) {
-    bc += s_tot[0][w];
-    ba += s_tot[1][w];
-    bt += s_tot[2][w];
+  if (E > 64) {
+    if (lane == 63) {
+      s_tot[0][wave] = ic;
+      s_tot[1][wave] = ia;
+      s_tot[2][wave] = it;
+    }
+    __syncthreads();
+    for (int w = 0; w < wave; ++w) {
+      bc += s_tot[0][w];
+      ba += s_tot[1][w];
+      bt += s_tot[2][w];
+    }
   }
   const int ex_c = bc + ic - c, ex_a = ba + ia - a, ex_t = bt + it - tl;
   if (tid < E) {
@@ -89,37 +96,83 @@ __device__ __forceinline__ void align_block(const int32_t* __restrict__ ids, int
     *reinterpret_cast<i32x4_t*>(active) = head;
     if (tile_offsets) tile_offsets[E] = ex_t + tl;
   }
+}
+
+// The whole permutation, run by one workgroup of kAlignThreads threads.
+// Up to kAlignThreads pairs: one pass.  Every wavefront groups its pairs by
+// expert (lane_group) and its group leaders record the per-wavefront counts; the
+// expert totals are sums of those, and a pair's position is its expert's offset
+// plus the counts of its expert in the earlier wavefronts plus its rank.
+// More pairs: the counts come from LDS atomics first, then passes of
+// kAlignThreads pairs in pair order, each adding the counts of the earlier passes.
+__device__ __forceinline__ void align_block(const int32_t* __restrict__ ids, int P, int E, int block_m, int id_bits,
+                                            int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
+                                            int32_t* __restrict__ pair_pos, int32_t* __restrict__ active,
+                                            int32_t* __restrict__ tile_offsets) {
+  __shared__ int s_count[MOE_MAX_EXPERTS];
+  __shared__ int s_off[MOE_MAX_EXPERTS];
+  __shared__ uint16_t s_wcnt[kAlignWaves][MOE_MAX_EXPERTS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < kAlignWaves * E; i += kAlignThreads) s_wcnt[i / E][i % E] = 0;
+  if (P <= kAlignThreads) {
+    __syncthreads();
+    const int p = tid;
+    const int e_in = p < P ? ids[p] : 0;
+    const bool valid = p < P && e_in >= 0 && e_in < E;  // out-of-range ids are dropped
+    const int e = valid ? e_in : 0;
+    if (p < P && !valid) pair_pos[p] = -1;
+    const LaneGroup lg = lane_group(e, valid, id_bits, lane);
+    if (valid && lg.rank == 0) s_wcnt[wave][e] = (uint16_t)lg.cnt;
+    __syncthreads();
+    int c = 0;
+    if (tid < E) {
+#pragma unroll
+      for (int w = 0; w < kAlignWaves; ++w) c += s_wcnt[w][tid];
+    }
+    align_scan(c, E, block_m, tid, lane, wave, s_off, offsets, active, tile_offsets);
+    __syncthreads();
+    if (valid) {
+      int before = 0;
+      for (int w = 0; w < wave; ++w) before += s_wcnt[w][e];
+      const int q = s_off[e] + before + lg.rank;
+      sorted_pairs[q] = p;
+      pair_pos[p] = q;
+    }
+    return;
+  }
+
+  for (int e = tid; e < E; e += kAlignThreads) s_count[e] = 0;
+  __syncthreads();
+  for (int p = tid; p < P; p += kAlignThreads) {
+    const int e = ids[p];
+    if (e >= 0 && e < E) atomicAdd(&s_count[e], 1);
+  }
+  __syncthreads();
+  align_scan(tid < E ? s_count[tid] : 0, E, block_m, tid, lane, wave, s_off, offsets, active, tile_offsets);
   __syncthreads();
   for (int e = tid; e < E; e += kAlignThreads) s_count[e] = 0;  // now: pairs placed so far
   __syncthreads();
 
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int base = 0; base < P; base += kAlignThreads) {
     const int p = base + tid;
     const int e_in = p < P ? ids[p] : 0;
     const bool valid = p < P && e_in >= 0 && e_in < E;   // out-of-range ids are dropped
     const int e = valid ? e_in : 0;
     if (p < P && !valid) pair_pos[p] = -1;
-    uint64_t m = __ballot(valid);
-    for (int b = 0; b < id_bits; ++b) {
-      const bool bit = (e >> b) & 1;
-      const uint64_t bb = __ballot(valid && bit);
-      m &= bit ? bb : ~bb;
-    }
-    const int rank = __popcll(m & lt_mask);
-    const int cnt = __popcll(m);
-    if (valid && rank == 0) s_wcnt[wave][e] = (uint16_t)cnt;
+    const LaneGroup lg = lane_group(e, valid, id_bits, lane);
+    if (valid && lg.rank == 0) s_wcnt[wave][e] = (uint16_t)lg.cnt;
     __syncthreads();
     if (valid) {
       int before = s_count[e];
       for (int w = 0; w < wave; ++w) before += s_wcnt[w][e];
-      const int q = s_off[e] + before + rank;
+      const int q = s_off[e] + before + lg.rank;
       sorted_pairs[q] = p;
       pair_pos[p] = q;
     }
     __syncthreads();
-    if (valid && rank == 0) {
-      atomicAdd(&s_count[e], cnt);
+    if (valid && lg.rank == 0) {
+      atomicAdd(&s_count[e], lg.cnt);
       s_wcnt[wave][e] = 0;
     }
     __syncthreads();

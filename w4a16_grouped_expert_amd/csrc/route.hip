@@ -185,22 +185,23 @@ __global__ __launch_bounds__(1024) void k_route_token(const uint16_t* __restrict
 }
 
 // Decode-sized steps, routing and alignment in one launch.  Every workgroup
-// computes 16 logits, one per wavefront (lane l takes the 16-byte chunks l,
-// l + 64, ... of d; the float64 partial sums meet in a butterfly), releases them
-// with device-coherent stores and counts itself done on a counter in device
-// memory once they have completed.  The workgroup that counts last reads
-// everyone's logits with device-coherent loads into LDS, runs the top-k of
-// every token (one wavefront per token) and the alignment (align_block), and puts
-// the counter back to zero for the next call.
+// computes 16 logits of one token, one per wavefront (lane l takes the 16-byte
+// chunks l, l + 64, ... of d; the float64 partial sums meet in a butterfly),
+// releases them with device-coherent stores and counts itself done on its
+// token's counter once they have completed.  The workgroup that completes a
+// token reads that token's logits with device-coherent loads and runs its top-k
+// and weights (tokens in parallel, on as many CUs), releases the ids the same
+// way and counts the token done; the workgroup that completes the last token
+// reads every id and runs the alignment (align_block).  Each counter is put back
+// to zero by the workgroup that saw it complete.
 constexpr int kRouteAlignMaxT = 128;
-constexpr int kRouteAlignMaxLogits = 16384;  // T * E staged in LDS by the last workgroup
 
 __global__ __launch_bounds__(kAlignThreads) void k_route_align(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int T, int d, int E, int k, int renormalize,
     int block_m, int id_bits, float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ weights,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_pos,
-    int32_t* __restrict__ active, int32_t* __restrict__ tile_offsets, int32_t* __restrict__ counter) {
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
+    int32_t* __restrict__ active, int32_t* __restrict__ tile_offsets, int32_t* __restrict__ counters) {
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int e = blockIdx.x * kAlignWaves + wave, t = blockIdx.y;
   if (e < E) {
     const int nch = d / 8;
@@ -232,57 +233,70 @@ __global__ __launch_bounds__(kAlignThreads) void k_route_align(
   __shared__ int s_last;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wavefront's logit has reached device scope
   __syncthreads();
-  if (threadIdx.x == 0)
-    s_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-             (int)(gridDim.x * gridDim.y) - 1;
+  if (tid == 0) {
+    s_last = __hip_atomic_fetch_add(counters + 1 + t, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             (int)gridDim.x - 1;
+    if (s_last) __hip_atomic_store(counters + 1 + t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   __syncthreads();
   if (!s_last) return;
-  // every other workgroup's logits are complete at device scope: one coherent read
-  // of all T * E of them into LDS
-  __shared__ float s_lg[kRouteAlignMaxLogits];
-  for (int i = threadIdx.x; i < T * E; i += kAlignThreads)
-    s_lg[i] = __hip_atomic_load(logits + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // this token's logits are complete at device scope: top-k by rank (each expert
+  // counts the logits that beat it, value desc, index asc) and weights, with the
+  // sums of topk_wave in the same order
+  __shared__ float s_lg[MOE_MAX_EXPERTS];
+  __shared__ float s_sel_v[MOE_MAX_TOPK];
+  __shared__ int s_sel_i[MOE_MAX_TOPK];
+  __shared__ int32_t s_ids[kRouteAlignMaxT * MOE_MAX_TOPK];
+  for (int i = tid; i < E; i += kAlignThreads)
+    s_lg[i] = __hip_atomic_load(logits + (int64_t)t * E + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  // top-k by rank: each (token, expert) logit counts the logits of its token that
-  // beat it (value desc, index asc); the k with rank < k write themselves
-  __shared__ float s_sel_v[kRouteAlignMaxT][MOE_MAX_TOPK];
-  __shared__ int s_sel_i[kRouteAlignMaxT][MOE_MAX_TOPK];
-  for (int i = threadIdx.x; i < T * E; i += kAlignThreads) {
-    const int tt = i / E, ee = i - tt * E;
+  for (int i = tid; i < E; i += kAlignThreads) {
     const float v = s_lg[i];
-    const int rank = rank_in_row(s_lg + tt * E, E, v, ee);
+    const int rank = rank_in_row(s_lg, E, v, i);
     if (rank < k) {
-      s_sel_v[tt][rank] = v;
-      s_sel_i[tt][rank] = ee;
+      s_sel_v[rank] = v;
+      s_sel_i[rank] = i;
     }
   }
   __syncthreads();
-  // weights, with the sums of topk_wave in the same order; lane j < k holds the
-  // exponential of selection j, the renormalising sum runs over j in order
-  __shared__ int32_t s_ids[kRouteAlignMaxT * MOE_MAX_TOPK];
-  for (int tt = wave; tt < T; tt += kAlignWaves) {
-    const float lmax = s_sel_v[tt][0];
-    const float ex = lane < k ? expf(s_sel_v[tt][lane] - lmax) : 0.f;
+  if (wave == 0) {
+    // lane j < k holds the exponential of selection j; the renormalising sum runs
+    // over j in order
+    const float lmax = s_sel_v[0];
+    const float ex = lane < k ? expf(s_sel_v[lane] - lmax) : 0.f;
     float den = 0.f;
     if (renormalize) {
       for (int j = 0; j < k; ++j) den += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
     } else {
       float part = 0.f;
-      for (int ee = lane; ee < E; ee += 64) part += expf(s_lg[tt * E + ee] - lmax);
+      for (int i = lane; i < E; i += 64) part += expf(s_lg[i] - lmax);
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
       den = part;
     }
     if (lane < k) {
-      const int id = s_sel_i[tt][lane];
-      s_ids[tt * k + lane] = id;
-      ids[(int64_t)tt * k + lane] = id;
-      weights[(int64_t)tt * k + lane] = ex / den;
+      const int id = s_sel_i[lane];
+      s_ids[lane] = id;  // used when this is the only token
+      __hip_atomic_store(ids + (int64_t)t * k + lane, id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      weights[(int64_t)t * k + lane] = ex / den;
     }
+  }
+  if (T > 1) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this token's ids have reached device scope
+    __syncthreads();
+    if (tid == 0) {
+      s_last = __hip_atomic_fetch_add(counters, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == T - 1;
+      if (s_last) __hip_atomic_store(counters, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    // every token's ids are complete at device scope
+    for (int i = tid; i < T * k; i += kAlignThreads)
+      s_ids[i] = __hip_atomic_load(ids + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
   align_block(s_ids, T * k, E, block_m, id_bits, offsets, sorted_pairs, pair_pos, active, tile_offsets);
-  if (threadIdx.x == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int TB>
@@ -403,11 +417,11 @@ extern "C" int moe_route(const uint16_t* x, const uint16_t* w_router, int T, int
 extern "C" int moe_route_align(const uint16_t* x, const uint16_t* w_router, int T, int d, int E, int k,
                                int renormalize, int block_m, float* logits, int32_t* topk_ids, float* topk_weights,
                                int32_t* expert_offsets, int32_t* sorted_pairs, int32_t* pair_pos,
-                               int32_t* active_experts, int32_t* tile_offsets, int32_t* counter, void* stream) {
+                               int32_t* active_experts, int32_t* tile_offsets, int32_t* counters, void* stream) {
   clear_error();
   MOE_CHECK_ARG(T >= 0 && d > 0 && E > 0 && k > 0 && block_m >= 0, MOE_ERR_INVALID_ARG,
                 "moe_route_align: bad sizes T=%d d=%d E=%d k=%d block_m=%d", T, d, E, k, block_m);
-  if (T == 0 || T > kRouteAlignMaxT || (int64_t)T * E > kRouteAlignMaxLogits) {
+  if (T == 0 || T > kRouteAlignMaxT) {
     // nothing to route, or a step too large for one launch: the two separate calls
     int rc = moe_route(x, w_router, T, d, E, k, renormalize, logits, topk_ids, topk_weights, stream);
     if (rc) return rc;
@@ -417,7 +431,7 @@ extern "C" int moe_route_align(const uint16_t* x, const uint16_t* w_router, int 
   MOE_CHECK_ARG(E <= MOE_MAX_EXPERTS && k <= MOE_MAX_TOPK && k <= E && d % 8 == 0, MOE_ERR_UNSUPPORTED_SHAPE,
                 "moe_route_align: unsupported E=%d k=%d d=%d (E <= 1024, k <= min(E,16), d %% 8 == 0)", E, k, d);
   MOE_CHECK_ARG(x && w_router && logits && topk_ids && topk_weights && expert_offsets && sorted_pairs && pair_pos &&
-                    active_experts && counter,
+                    active_experts && counters,
                 MOE_ERR_INVALID_ARG, "moe_route_align: null pointer");
   MOE_CHECK_ARG(block_m == 0 || tile_offsets, MOE_ERR_INVALID_ARG, "moe_route_align: block_m > 0 needs tile_offsets");
   MOE_CHECK_ARG(((uintptr_t)x % 16) == 0 && ((uintptr_t)w_router % 16) == 0 && ((uintptr_t)active_experts % 16) == 0,
@@ -429,7 +443,7 @@ extern "C" int moe_route_align(const uint16_t* x, const uint16_t* w_router, int 
   hipLaunchKernelGGL(k_route_align, dim3((unsigned)ceil_div(E, kAlignWaves), (unsigned)T), dim3(kAlignThreads), 0, s,
                      x, w_router, T, d, E, k, renormalize, block_m, bits, logits, topk_ids, topk_weights,
                      expert_offsets, sorted_pairs, pair_pos, active_experts, block_m > 0 ? tile_offsets : nullptr,
-                     counter);
+                     counters);
   timing_end(K_ROUTE, s);
   return check_launch("moe_route_align");
 }

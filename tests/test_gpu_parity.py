@@ -316,3 +316,31 @@ def test_slot_table_subsets_equal_resident():
     moe.moe_w4a16_grouped_ffn_into(x, r, a, bank, s.I, out, ws, moe.MODE_DECODE, True, other)
     torch.cuda.synchronize()
     assert torch.equal(out, ref)
+
+
+@pytest.mark.parametrize("T", [1, 16])
+def test_per_expert_calls_equal_fused(T):
+    # the ablation's sequential variant: one grouped-FFN call per active expert (slot
+    # table keeping only that expert), combine on the last call; same kernels, so the
+    # output equals the fused call bit for bit (OLMoE shape, decode path)
+    say(f"per-expert calls vs fused T={T}")
+    wl = synth.OLMOE_DECODE
+    s = wl.shape
+    w13, w2 = synth.expert_weights(wl, 2, device=DEV)
+    bank, _ = moe.pack_experts(w13, w2)
+    del w13, w2
+    wr = synth.router_weight(wl, 2).to(DEV)
+    x = synth.activations(wl, T, 2).to(DEV)
+    ref, r, a = run_layer(x, wr, bank, s.I, s.k)
+    ws = moe.alloc_workspace(T, s.d, s.I, s.E, s.k)
+    out = torch.empty_like(ref)
+    act = a.active.cpu()
+    experts = act[4::4][:int(act[0])].tolist()
+    assert len(experts) == len(set(r.ids.cpu().numpy().ravel().tolist()))
+    for i, e in enumerate(experts):
+        only = torch.full((s.E,), -1, dtype=torch.int32, device=DEV)
+        only[e] = e
+        moe.moe_w4a16_grouped_ffn_into(x, r, a, bank, s.I, out, ws, combine=(i == len(experts) - 1),
+                                       slot_of_expert=only)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)

@@ -49,6 +49,7 @@ def parse():
     p.add_argument("--no-large", action="store_true", help="skip the large-expert shape")
     p.add_argument("--no-slot-cache", action="store_true", help="skip the 16-slot cache workload")
     p.add_argument("--no-ablation", action="store_true", help="skip the fused vs per-expert ablation")
+    p.add_argument("--no-bf16", action="store_true", help="skip the BF16-expert comparison")
     p.add_argument("--slot-steps", type=int, default=24, help="timed steps of the slot-cache workload")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain device copy of known size (for HBM counter calibration)")
@@ -67,29 +68,34 @@ def copy_calibration():
 
 
 class Decoder:
-    """16 resident W4A16 MoE layers with shared per-step buffers."""
+    """16 resident MoE layers with shared per-step buffers: four-bit experts, or
+    (bf16=True) the same experts unquantised for the W4 versus BF16 comparison."""
 
-    def __init__(self, wl, T_max, device):
+    def __init__(self, wl, T_max, device, bf16=False):
         import torch
         import synth
         import w4a16_grouped_expert_amd as moe
         self.moe, self.torch = moe, torch
         s = wl.shape
-        self.wl, self.s = wl, s
+        self.wl, self.s, self.bf16 = wl, s, bf16
         self.layers = []
         for l in range(wl.layers):
             w13, w2 = synth.expert_weights(wl, l, device=device)
-            bank, lay = moe.pack_experts(w13, w2)
+            if bf16:
+                bank = moe.pack_bf16_experts(w13, w2)
+            else:
+                bank, lay = moe.pack_experts(w13, w2)
             del w13, w2
             wr = synth.router_weight(wl, l, device="cpu").to(device)
             self.layers.append((wr, bank))
         torch.cuda.synchronize()
-        self.blob_bytes = lay["blob_bytes"]
+        self.blob_bytes = moe.bf16_expert_bytes(s.d, s.I) if bf16 else lay["blob_bytes"]
         self.T_max = T_max
         self.route = moe.alloc_route(T_max, s.E, s.k, device)
         self.align = moe.alloc_align(T_max, s.k, s.E, device)
         self.counter = moe.alloc_counter(device)
-        need = max(moe.ffn_workspace_bytes(t, s.d, s.I, s.E, s.k) for t in range(1, T_max + 1))
+        need = max(max(moe.ffn_workspace_bytes(t, s.d, s.I, s.E, s.k), moe.ffn_workspace_bytes(t, s.d, s.I, s.E, s.k, moe.MODE_DECODE))
+                   for t in range(1, T_max + 1))
         self.ws = torch.empty(need, dtype=torch.uint8, device=device)
         self.out = [torch.empty((T_max, s.d), dtype=torch.bfloat16, device=device) for _ in range(wl.layers)]
 
@@ -101,7 +107,10 @@ class Decoder:
         a = moe.AlignOut(self.align.offsets, self.align.sorted_pairs[:T * s.k], self.align.pair_pos[:T * s.k],
                          self.align.active, None, 0)
         moe.moe_route_align_into(x, wr, s.k, r, a, self.counter)
-        moe.moe_w4a16_grouped_ffn_into(x, r, a, bank, s.I, self.out[l][:T], self.ws)
+        if self.bf16:
+            moe.moe_bf16_grouped_ffn_into(x, r, a, bank, s.I, self.out[l][:T], self.ws)
+        else:
+            moe.moe_w4a16_grouped_ffn_into(x, r, a, bank, s.I, self.out[l][:T], self.ws)
         return a
 
     def step(self, xs):
@@ -199,6 +208,29 @@ def run_ablation(dec, T, steps, x_sets=4):
             "sequential_tokens_per_s": round(T * wl.layers / (seq_g * 1e-3), 1)}
 
 
+def run_bf16_compare(Ts, steps, warmup, x_sets, w4_tokens_per_s):
+    """The same 16-layer decode with the experts unquantised (BF16 blobs, 3.88x the
+    bytes of the four-bit ones): tokens/s and HBM rate from HIP-graph replays,
+    and the four-bit speedup at each T."""
+    import torch
+    import synth
+    wl = synth.OLMOE_DECODE
+    dec = Decoder(wl, max(Ts), "cuda", bf16=True)
+    res = {}
+    for T in Ts:
+        r = run_decode(dec, T, steps, warmup, x_sets, timed_kernels=("gateup_bf16", "down_bf16", "combine", "route"))
+        s = dec.s
+        layer_bytes = r["mean_distinct_experts"] * dec.blob_bytes + s.E * s.d * 2 + 2 * T * s.d * 2
+        res[f"T={T}"] = {"tokens_per_s": round(r["tokens_per_s"], 1), "ms_per_step": round(r["ms_per_step"], 4),
+                         "hbm_gbps": round(layer_bytes * wl.layers / (r["ms_per_step"] * 1e-3) / 1e9, 1),
+                         "kernels_us": {k: round(v["avg_us"], 3) for k, v in r["kernels"].items()},
+                         "w4_speedup": round(w4_tokens_per_s[T] / r["tokens_per_s"], 3)}
+    del dec
+    torch.cuda.empty_cache()
+    return {"workload": "olmoe_decode with BF16 experts (12.58 MB each, row-major, same route/align/combine)",
+            "pages_w4_over_bf16": round(31.923 / 21.662, 3), "bytes_ratio": 3.879, **res}
+
+
 def expert_section_bytes(d, I):
     codes13, scales13 = 2 * I * d // 2, 2 * I * (d // 128) * 2
     codes2, scales2 = d * I // 2, d * (I // 128) * 2
@@ -225,7 +257,8 @@ def capture_graphs(dec, xs_sets):
     return graphs
 
 
-def run_decode(dec, T, steps, warmup, x_sets):
+def run_decode(dec, T, steps, warmup, x_sets, timed_kernels=("gateup_decode", "down_decode", "combine", "route",
+                                                              "align")):
     """Time K steps replayed from HIP graphs (value), then K eager steps with the
     dominant kernels bracketed by HIP events on their stream (roofline)."""
     import torch
@@ -260,7 +293,7 @@ def run_decode(dec, T, steps, warmup, x_sets):
     moe.timing_enable(False)
     ms_eager = t0.elapsed_time(t1) / steps
     res = {"T": T, "ms_per_step": ms, "ms_per_step_eager": ms_eager, "kernels": {}}
-    for kname in ("gateup_decode", "down_decode", "combine", "route", "align"):
+    for kname in timed_kernels:
         tot, n = moe.timing_read(kname)
         if n:
             res["kernels"][kname] = {"avg_us": 1e3 * tot / n, "launches": n}
@@ -590,6 +623,10 @@ def main():
             **{f"T={T}": run_ablation(dec, T, max(4, args.steps // 5)) for T in (args.tokens, 1)}}
     del dec
     torch.cuda.empty_cache()
+    if not args.no_bf16:
+        w4 = {args.tokens: head["tokens_per_s"]}
+        w4.update({int(k[2:]): v["tokens_per_s"] for k, v in sweep.items()})
+        out["bf16_experts"] = run_bf16_compare(sorted(w4), args.steps, args.warmup, args.x_sets, w4)
     if args.prefill_tokens > 0:
         out["prefill"] = run_prefill(args.prefill_tokens)
         extra = {}

@@ -180,6 +180,30 @@ int64_t moe_ffn_workspace_bytes(int T, int d, int I, int E, int k, int mode);
 int moe_w4a16_grouped_ffn(const moe_ffn_args* args, void* stream);
 
 /*
+ * BF16 experts: the same grouped pass over unquantised experts, the BF16 side of
+ * the page's four-bit versus BF16 decode comparison (ExactMoE, Abstract: W4A16
+ * experts against the BF16 model).
+ *
+ * moe_bf16_expert_bytes: bytes of one BF16 expert blob, 6 * d * I: W13 [2I][d]
+ *   (gate rows 0..I-1, then up rows) followed by W2 [d][I], bf16 row-major.
+ *   -1 for non-positive sizes.
+ * moe_bf16_pack: copy E experts' w13 [E][2I][d] and w2 [E][d][I] (device bf16,
+ *   contiguous) into a bank of blobs at bank_stride bytes (device-to-device
+ *   copies on `stream`).  Errors: MOE_ERR_INVALID_ARG (sizes, NULL, stride below
+ *   the blob size), MOE_ERR_HIP (copy could not be enqueued).
+ * moe_bf16_grouped_ffn: gate/up + SwiGLU, down and combine as
+ *   moe_w4a16_grouped_ffn, with `bank` holding BF16 blobs (256-byte aligned,
+ *   stride >= moe_bf16_expert_bytes and a multiple of 256) and slot_of_expert /
+ *   combine as there.  `mode` is ignored.  The workspace must hold
+ *   moe_ffn_workspace_bytes(T, d, I, E, k, MOE_MODE_DECODE) bytes.  Limits: those
+ *   of moe_w4a16_grouped_ffn, and T * d and T * k * I below 2^30.
+ */
+int64_t moe_bf16_expert_bytes(int d, int I);
+int moe_bf16_pack(const uint16_t* w13, const uint16_t* w2, int E, int d, int I, uint8_t* bank,
+                  int64_t bank_stride, void* stream);
+int moe_bf16_grouped_ffn(const moe_ffn_args* args, void* stream);
+
+/*
  * Expert slot cache (ExactMoE, Abstract: quantised experts in pinned host
  * memory, executed from a configurable GPU-resident slot cache).
  *
@@ -219,7 +243,8 @@ int moe_slot_cache_state(const moe_slot_cache* cache, int32_t* slot_expert,
  * hipEvents on its own stream.  moe_timing_read synchronises on the recorded
  * events and returns the summed duration and launch count since the last reset.
  * Kernel ids: 0 = gate/up (decode), 1 = down (decode), 2 = gate/up (prefill),
- * 3 = down (prefill), 4 = combine, 5 = route logits, 6 = align.
+ * 3 = down (prefill), 4 = combine, 5 = route logits, 6 = align, 7 = gate/up
+ * (BF16 experts), 8 = down (BF16 experts).
  */
 int moe_timing_enable(int on);
 int moe_timing_reset(void);

@@ -44,6 +44,21 @@ class DequantBank:
         return self._cache[e]
 
 
+class Bf16Bank:
+    """Unquantised experts: the bf16 master weights themselves, as float64 (the
+    BF16 side of the page's four-bit versus BF16 comparison).  Same interface as
+    DequantBank."""
+
+    def __init__(self, w13_bits, w2_bits):
+        self._w13, self._w2 = w13_bits, w2_bits
+        self._cache = {}
+
+    def get(self, e):
+        if e not in self._cache:
+            self._cache[e] = (bf16.to_f64(self._w13(e)), bf16.to_f64(self._w2(e)))
+        return self._cache[e]
+
+
 def expert_ffn(w13, w2, X):
     """SwiGLU expert on rows of X [n, d] with dequantised w13 [2I, d], w2 [d, I] -> [n, d]."""
     I = w13.shape[0] // 2

@@ -44,6 +44,28 @@ def test_single_expert_is_textbook_swiglu_mlp():
         assert np.allclose(res["out"][t], y, rtol=1e-12, atol=1e-14)
 
 
+def test_bf16_bank_single_expert_is_textbook_swiglu_mlp():
+    # unquantised experts: the weights are the bf16 values themselves
+    d, I = 128, 128
+    w13 = rand_bits((2 * I, d), 0.05, 30)
+    w2 = rand_bits((d, I), 0.05, 31)
+    bank = ffn.Bf16Bank(lambda e: w13, lambda e: w2)
+    xb = rand_bits((2, d), 1.0, 32)
+    res = ffn.moe_layer(xb, rand_bits((1, d), 0.02, 33), bank, k=1)
+    W13, W2, x = bf16.to_f64(w13), bf16.to_f64(w2), bf16.to_f64(xb)
+    for t in range(2):
+        h = []
+        for i in range(I):
+            g = sum(float(W13[i, c]) * x[t, c] for c in range(d))
+            u = sum(float(W13[I + i, c]) * x[t, c] for c in range(d))
+            h.append(g / (1.0 + math.exp(-g)) * u)
+        y = [sum(float(W2[n, i]) * h[i] for i in range(I)) for n in range(d)]
+        assert np.allclose(res["out"][t], y, rtol=1e-12, atol=1e-14)
+    # and it differs from the four-bit layer on the same weights (quantisation is not a no-op)
+    q = ffn.moe_layer(xb, rand_bits((1, d), 0.02, 33), ffn.DequantBank(lambda e: w13, lambda e: w2), k=1)
+    assert not np.allclose(q["out"], res["out"], rtol=1e-3, atol=0)
+
+
 def test_layer_equals_dense_masked_formulation():
     T, d, E, k, I = 16, 256, 8, 2, 512          # the tiny workload's shape
     w13, w2, bank = make_bank(E, d, I, 20)

@@ -57,6 +57,9 @@ SIGNATURES = {
                                 c_vp, c_vp, c_vp, c_vp, c_vp]),
     "moe_ffn_workspace_bytes": (c_i64, [c_int, c_int, c_int, c_int, c_int, c_int]),
     "moe_w4a16_grouped_ffn": (c_int, [ctypes.POINTER(FfnArgs), c_vp]),
+    "moe_bf16_expert_bytes": (c_i64, [c_int, c_int]),
+    "moe_bf16_pack": (c_int, [c_vp, c_vp, c_int, c_int, c_int, c_vp, c_i64, c_vp]),
+    "moe_bf16_grouped_ffn": (c_int, [ctypes.POINTER(FfnArgs), c_vp]),
     "moe_slot_cache_create": (c_int, [c_int, c_int, c_i64, c_vp, c_vp, ctypes.POINTER(c_vp)]),
     "moe_slot_cache_destroy": (c_int, [c_vp]),
     "slot_cache_load": (c_int, [c_vp, c_u64p, c_u64p, c_vp, c_i32p, c_i32p, c_vp, c_vp, c_vp]),

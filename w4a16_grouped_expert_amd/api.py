@@ -213,6 +213,61 @@ def moe_w4a16_grouped_ffn_into(x, route: RouteOut, al: AlignOut, bank: torch.Ten
     return out
 
 
+def bf16_expert_bytes(d: int, I: int) -> int:
+    return int(lib().moe_bf16_expert_bytes(d, I))
+
+
+def pack_bf16_experts(w13: torch.Tensor, w2: torch.Tensor, bank: Optional[torch.Tensor] = None, stream=None):
+    """BF16 expert bank: w13 [E, 2I, d], w2 [E, d, I] (bf16, GPU) copied into blobs
+    (uint8 [E, stride], stride = bf16 blob bytes rounded up to 256)."""
+    _need(w13, torch.bfloat16, "w13")
+    _need(w2, torch.bfloat16, "w2")
+    E, twoI, d = w13.shape
+    I = twoI // 2
+    stride = (bf16_expert_bytes(d, I) + 255) // 256 * 256
+    if bank is None:
+        bank = torch.empty((E, stride), dtype=torch.uint8, device=w13.device)
+    check("moe_bf16_pack", lib().moe_bf16_pack(_ptr(w13.contiguous()), _ptr(w2.contiguous()), E, d, I, _ptr(bank),
+                                               bank.stride(0), _stream(stream)))
+    return bank
+
+
+def moe_bf16_grouped_ffn_into(x, route: RouteOut, al: AlignOut, bank: torch.Tensor, I: int, out: torch.Tensor,
+                              workspace: torch.Tensor, combine=True, slot_of_expert: Optional[torch.Tensor] = None,
+                              stream=None):
+    """The grouped pass over BF16 expert blobs (pack_bf16_experts); workspace sized
+    with mode=MODE_DECODE."""
+    _need(x, torch.bfloat16, "x")
+    _need(bank, torch.uint8, "bank")
+    _need(workspace, torch.uint8, "workspace")
+    if combine:
+        _need(out, torch.bfloat16, "out")
+    if slot_of_expert is not None:
+        _need(slot_of_expert, torch.int32, "slot_of_expert")
+    T, d = x.shape
+    a = _lib.FfnArgs()
+    a.x, a.T, a.d, a.I, a.E, a.k = x.data_ptr(), T, d, I, route.logits.shape[1], route.ids.shape[1]
+    a.topk_ids, a.topk_weights = route.ids.data_ptr(), route.weights.data_ptr()
+    a.expert_offsets, a.sorted_pairs = al.offsets.data_ptr(), al.sorted_pairs.data_ptr()
+    a.pair_pos, a.active_experts = al.pair_pos.data_ptr(), al.active.data_ptr()
+    a.tile_offsets = al.tile_offsets.data_ptr() if al.tile_offsets is not None else None
+    a.bank, a.bank_stride = bank.data_ptr(), bank.stride(0)
+    a.slot_of_expert = slot_of_expert.data_ptr() if slot_of_expert is not None else None
+    a.mode, a.combine = MODE_DECODE, int(bool(combine))
+    a.out = out.data_ptr() if out is not None else None
+    a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
+    check("moe_bf16_grouped_ffn", lib().moe_bf16_grouped_ffn(ctypes.byref(a), _stream(stream)))
+    return out
+
+
+def moe_bf16_grouped_ffn(x, route, al, bank, I, stream=None):
+    T, d = x.shape
+    E, k = route.logits.shape[1], route.ids.shape[1]
+    out = torch.empty((T, d), dtype=torch.bfloat16, device=x.device)
+    ws = alloc_workspace(T, d, I, E, k, MODE_DECODE, x.device)
+    return moe_bf16_grouped_ffn_into(x, route, al, bank, I, out, ws, True, stream=stream)
+
+
 def moe_w4a16_grouped_ffn(x, route, al, bank, I, mode=MODE_AUTO, slot_of_expert=None, stream=None):
     T, d = x.shape
     E, k = route.logits.shape[1], route.ids.shape[1]
@@ -319,6 +374,7 @@ class SlotCache:
 # ---------------------------------------------------------------- timing
 
 KERNELS = {"gateup_decode": 0, "down_decode": 1, "gateup_prefill": 2, "down_prefill": 3, "combine": 4,
+           "gateup_bf16": 7, "down_bf16": 8,
            "route": 5, "align": 6}
 
 

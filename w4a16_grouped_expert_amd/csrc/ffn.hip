@@ -96,6 +96,27 @@ static WsLayout ws_layout(int T, int d, int I, int E, int k, int mode) {
   return L;
 }
 
+FfnWorkspace ffn_workspace(int T, int d, int I, int E, int k, int mode, void* ws) {
+  const WsLayout L = ws_layout(T, d, I, E, k, mode);
+  uint8_t* b = static_cast<uint8_t*>(ws);
+  FfnWorkspace w;
+  w.h = reinterpret_cast<uint16_t*>(b + L.h_off);
+  w.y = reinterpret_cast<float*>(b + L.y_off);
+  w.xsum = reinterpret_cast<float*>(b + L.xsum_off);
+  w.hsum = reinterpret_cast<float*>(b + L.hsum_off);
+  w.ksplit = down_ksplit(T, d, I, E, k, mode);
+  return w;
+}
+
+int launch_combine(const FfnDev& f, const float* y, int ksplit, const float* weights, uint16_t* out, hipStream_t s) {
+  const int nchunks = (int)ceil_div(f.d, 1024);
+  timing_begin(K_COMBINE, s);
+  hipLaunchKernelGGL(k_combine, dim3((unsigned)(f.T * (int64_t)nchunks)), dim3(256), 0, s, y, ksplit, f.P, f.d, f.k,
+                     f.pair_pos, weights, out, nchunks);
+  timing_end(K_COMBINE, s);
+  return check_launch("combine");
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -162,26 +183,15 @@ extern "C" int moe_w4a16_grouped_ffn(const moe_ffn_args* a, void* stream) {
   f.off_w2_codes = lay.w2_codes;
   f.off_w2_scales = lay.w2_scales;
 
-  uint8_t* ws = static_cast<uint8_t*>(a->workspace);
-  uint16_t* h = reinterpret_cast<uint16_t*>(ws + L.h_off);
-  float* y = reinterpret_cast<float*>(ws + L.y_off);
+  const FfnWorkspace w = ffn_workspace(a->T, a->d, a->I, a->E, a->k, mode, a->workspace);
   hipStream_t s = (hipStream_t)stream;
-  const int ks = down_ksplit(a->T, a->d, a->I, a->E, a->k, mode);
   if (mode == MOE_MODE_DECODE) {
     const double per_expert = (double)a->T * a->k / a->E;
-    rc = launch_decode(f, h, y, ks, per_expert <= 8.0 ? 1 : 2, s);
+    rc = launch_decode(f, w.h, w.y, w.ksplit, per_expert <= 8.0 ? 1 : 2, s);
   } else {
-    rc = launch_prefill(f, h, y, reinterpret_cast<float*>(ws + L.xsum_off), reinterpret_cast<float*>(ws + L.hsum_off),
-                        s);
+    rc = launch_prefill(f, w.h, w.y, w.xsum, w.hsum, s);
   }
   if (rc) return rc;
-  if (a->combine) {
-    const int nchunks = (int)ceil_div(a->d, 1024);
-    timing_begin(K_COMBINE, s);
-    hipLaunchKernelGGL(k_combine, dim3((unsigned)(a->T * (int64_t)nchunks)), dim3(256), 0, s, y, ks, f.P, a->d,
-                       a->k, a->pair_pos, a->topk_weights, a->out, nchunks);
-    timing_end(K_COMBINE, s);
-    rc = check_launch("combine");
-  }
+  if (a->combine) rc = launch_combine(f, w.y, w.ksplit, a->topk_weights, a->out, s);
   return rc;
 }

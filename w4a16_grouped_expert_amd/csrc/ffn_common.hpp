@@ -30,6 +30,18 @@ struct FfnDev {
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
 
+// Workspace of one call: h [T*k][I] bf16, y [ksplit][T*k][d] fp32, and for the
+// prefill variant the group sums of x and h.
+struct FfnWorkspace {
+  uint16_t* h;
+  float* y;
+  float* xsum;
+  float* hsum;
+  int ksplit;
+};
+FfnWorkspace ffn_workspace(int T, int d, int I, int E, int k, int mode, void* ws);
+int launch_combine(const FfnDev& f, const float* y, int ksplit, const float* weights, uint16_t* out, hipStream_t s);
+
 int launch_decode(const FfnDev& f, uint16_t* h, float* y, int ksplit, int nb, hipStream_t s);
 int launch_prefill(const FfnDev& f, uint16_t* h, float* y, float* xsum, float* hsum, hipStream_t s);
 int64_t prefill_extra_bytes(int T, int d, int I, int k);

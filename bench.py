@@ -429,16 +429,19 @@ def run_large(Ts, reps=10, warmup=3):
                         "whole-step time (route + align + grouped FFN + combine) per T", **res}
 
 
-def run_slot_cache(steps, warmup=8, T=16, S=16):
-    """16-slot expert cache (OLMoE shape, 16 layers, Zipf(1.2) popularity with AR(1)
+def run_slot_cache(steps, warmup=8, T=16, variants=((16, False), (16, True), (64, False))):
+    """Expert slot cache (OLMoE shape, 16 layers, Zipf(1.2) popularity with AR(1)
     step locality): experts in pinned host memory, S device slots per layer, misses
-    copied by hipMemcpyAsync on a side stream before each FFN round."""
+    copied by hipMemcpyAsync on a side stream before each FFN round.  Variants
+    (S, prefetch): with prefetch, while layer l runs, the experts layer l+1 needed
+    at the previous step are copied into its slots (the copy stream stays busy
+    through the route / read-back / compute phases)."""
     import torch
     import synth
     import w4a16_grouped_expert_amd as moe
     wl = synth.OLMOE_SLOT
     s = wl.shape
-    layers = []
+    stores = []
     for l in range(wl.layers):
         w13, w2 = synth.expert_weights(wl, l, device="cuda")
         bank, lay = moe.pack_experts(w13, w2)
@@ -447,65 +450,97 @@ def run_slot_cache(steps, warmup=8, T=16, S=16):
         store = torch.empty((s.E, B), dtype=torch.uint8, pin_memory=True)
         store.copy_(bank)
         del bank
-        slots = torch.zeros((S, B), dtype=torch.uint8, device="cuda")
-        wr = synth.router_weight(wl, l).cuda()
-        layers.append({"wr": wr, "store": store, "slots": slots, "cache": moe.SlotCache(s.E, S, B, store, slots),
-                       "table": torch.full((s.E,), -1, dtype=torch.int32, device="cuda")})
+        stores.append((store, synth.router_weight(wl, l).cuda()))
     torch.cuda.empty_cache()
     route = moe.alloc_route(T, s.E, s.k, "cuda")
     al = moe.alloc_align(T, s.k, s.E, "cuda")
     counter = moe.alloc_counter("cuda")
     ws = moe.alloc_workspace(T, s.d, s.I, s.E, s.k, moe.MODE_DECODE)
     out = torch.empty((T, s.d), dtype=torch.bfloat16, device="cuda")
-    main = torch.cuda.current_stream()
-    copy = torch.cuda.Stream()
-    done, ffn_done = torch.cuda.Event(), torch.cuda.Event()
-    ffn_done.record(main)
     seqs = [[x.cuda() for x in synth.ar1_activation_sequence(wl, T, l, warmup + steps, device="cpu")]
             for l in range(wl.layers)]
+    main = torch.cuda.current_stream()
+    copy = torch.cuda.Stream()
 
-    def step(st):
-        rounds = misses = 0
-        for l, L in enumerate(layers):
-            x = seqs[l][st]
-            moe.moe_route_align_into(x, L["wr"], s.k, route, al, counter)
-            pending = {w[0] for w in moe.active_experts(al)}  # the one D2H sync per layer
-            while pending:
-                got, nh, nm = L["cache"].load(pending, L["table"], copy, ffn_done, done)
-                main.wait_event(done)
-                pending -= got
-                moe.moe_w4a16_grouped_ffn_into(x, route, al, L["slots"], s.I, out, ws, moe.MODE_DECODE,
-                                               not pending, L["table"])
-                ffn_done.record(main)
-                rounds += 1
-                misses += nm
-        return rounds, misses
+    def one(S, prefetch):
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        layers = []
+        for store, wr in stores:
+            slots = torch.zeros((S, B), dtype=torch.uint8, device="cuda")
+            layers.append({"wr": wr, "slots": slots, "cache": moe.SlotCache(s.E, S, B, store, slots),
+                           "table": torch.full((s.E,), -1, dtype=torch.int32, device="cuda"),
+                           "ffn_done": torch.cuda.Event(), "prev": set()})
+        done = torch.cuda.Event()
+        for L in layers:
+            L["ffn_done"].record(main)
+        L_ = len(layers)
 
-    for st in range(warmup):
-        step(st)
-    torch.cuda.synchronize()
-    h0 = [L["cache"].state()[1:] for L in layers]
-    t0 = time.perf_counter()
-    rounds = misses = 0
-    for st in range(warmup, warmup + steps):
-        r, m = step(st)
-        rounds += r
-        misses += m
-    torch.cuda.synchronize()
-    sec = time.perf_counter() - t0
-    h1 = [L["cache"].state()[1:] for L in layers]
-    hits = sum(b[0] - a[0] for a, b in zip(h0, h1))
-    miss = sum(b[1] - a[1] for a, b in zip(h0, h1))
-    for L in layers:
-        L["cache"].close()
-    res = {"workload": f"olmoe_slot16: 16 MoE layers, d=2048, E=64, top-8, I=1024, W4 g128; 64 experts per layer in "
-                       f"pinned host memory, {S} device slots per layer, Zipf(1.2) popularity, AR(1) locality, T={T}",
-           "tokens_per_s": round(steps * T * wl.layers / sec, 1), "ms_per_step": round(1e3 * sec / steps, 3),
-           "hit_rate": round(hits / max(1, hits + miss), 4), "misses_per_step": round(miss / steps, 2),
-           "rounds_per_layer": round(rounds / (steps * wl.layers), 3),
-           "h2d_gbps": round(miss * B / sec / 1e9, 2),
+        def step(st):
+            rounds = misses = pref = floor = 0
+            for l, L in enumerate(layers):
+                x = seqs[l][st]
+                moe.moe_route_align_into(x, L["wr"], s.k, route, al, counter)
+                need = {w[0] for w in moe.active_experts(al)}  # the one D2H sync per layer
+                floor += max(0, len(need) - S)  # copies no policy avoids: the rounds cycle the needed set
+                pending = set(need)
+                first = True
+                while pending:
+                    got, nh, nm = L["cache"].load(pending, L["table"], copy, L["ffn_done"], done)
+                    if first and prefetch:
+                        nxt = layers[(l + 1) % L_]
+                        if nxt["prev"]:
+                            pref += nxt["cache"].prefetch(nxt["prev"], S, copy, nxt["ffn_done"])
+                    first = False
+                    main.wait_event(done)
+                    pending -= got
+                    moe.moe_w4a16_grouped_ffn_into(x, route, al, L["slots"], s.I, out, ws, moe.MODE_DECODE,
+                                                   not pending, L["table"])
+                    L["ffn_done"].record(main)
+                    rounds += 1
+                    misses += nm
+                L["prev"] = need
+            return rounds, misses, pref, floor
+
+        for st in range(warmup):
+            step(st)
+        torch.cuda.synchronize()
+        h0 = [L["cache"].state()[1:] for L in layers]
+        t0 = time.perf_counter()
+        rounds = misses = pref = floor = 0
+        for st in range(warmup, warmup + steps):
+            r, m, p, fl = step(st)
+            rounds += r
+            misses += m
+            pref += p
+            floor += fl
+        torch.cuda.synchronize()
+        sec = time.perf_counter() - t0
+        h1 = [L["cache"].state()[1:] for L in layers]
+        hits = sum(b[0] - a[0] for a, b in zip(h0, h1))
+        miss = sum(b[1] - a[1] for a, b in zip(h0, h1))
+        peak = torch.cuda.max_memory_allocated() - base
+        for L in layers:
+            L["cache"].close()
+        del layers
+        torch.cuda.empty_cache()
+        return {"tokens_per_s": round(steps * T * wl.layers / sec, 1), "ms_per_step": round(1e3 * sec / steps, 3),
+                "hit_rate": round(hits / max(1, hits + miss), 4), "misses_per_step": round(miss / steps, 2),
+                "miss_floor_per_step": round(floor / steps, 2),
+                "prefetches_per_step": round(pref / steps, 2),
+                "rounds_per_layer": round(rounds / (steps * wl.layers), 3),
+                "h2d_gbps": round((miss + pref) * B / sec / 1e9, 2),
+                "slot_bytes_per_layer": S * B, "slot_bytes_total": S * B * wl.layers,
+                "peak_device_bytes_during_run": int(peak)}
+
+    res = {"workload": f"olmoe_slot: 16 MoE layers, d=2048, E=64, top-8, I=1024, W4 g128; 64 experts per layer in "
+                       f"pinned host memory, S device slots per layer, Zipf(1.2) popularity, AR(1) locality, T={T}",
+           "resident_bytes_all_experts": s.E * B * wl.layers,
            "timing": "wall clock over the timed steps (host round trip per layer for the needed set included)"}
-    del layers
+    for S, pf in variants:
+        res[f"S={S}" + (" prefetch" if pf else "")] = one(S, pf)
+    del stores
     torch.cuda.empty_cache()
     return res
 

@@ -234,6 +234,21 @@ int moe_slot_cache_destroy(moe_slot_cache* cache);
 int slot_cache_load(moe_slot_cache* cache, const uint64_t* pending_mask, uint64_t* round_mask,
                     int32_t* slot_table_dev, int32_t* n_hits, int32_t* n_misses,
                     void* copy_stream, void* wait_event, void* done_event);
+/* slot_cache_prefetch: copy experts expected to be needed soon (host bitmask
+ *   `predicted`, ceil(E/64) words) ahead of their round, so that the copies
+ *   overlap other work (the next-layer prefetch: issued while an earlier layer
+ *   computes).  The predicted experts not resident, in ascending id and at most
+ *   max_copies of them, go into victim slots chosen among the slots not holding a
+ *   predicted expert (empty slots first, then least recently used, ties to the
+ *   lower slot); they are then resident and count as hits when a round needs
+ *   them.  Copies are enqueued on copy_stream after wait_event (may be NULL; pass
+ *   an event recorded after the last kernel that read this cache's slots); the
+ *   next slot_cache_load on the same copy stream is ordered after them.
+ *   n_copies (host out, may be NULL).  Errors: MOE_ERR_INVALID_ARG, MOE_ERR_HIP
+ *   (a copy could not be enqueued; its slot is then marked empty).
+ */
+int slot_cache_prefetch(moe_slot_cache* cache, const uint64_t* predicted_mask, int max_copies,
+                        int32_t* n_copies, void* copy_stream, void* wait_event);
 /* Current slot contents ([S] expert id or -1) and cumulative hit / miss counts. */
 int moe_slot_cache_state(const moe_slot_cache* cache, int32_t* slot_expert,
                          int64_t* hits, int64_t* misses);

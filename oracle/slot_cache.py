@@ -15,6 +15,13 @@ reading taken:
   increases by one per round);
 * later rounds of the same step may evict experts of earlier rounds (their
   work is finished).
+
+Prefetch (the next-layer overlap: experts a layer is expected to need are copied
+while an earlier layer computes), the reading taken: the predicted experts not
+resident, in ascending id and at most max_copies of them, go into victim slots
+chosen among the slots not holding a predicted expert, by the same order (empty,
+then least recently used, ties to the lower slot); the prefetched slots get a new
+timestamp, like a round.
 """
 
 
@@ -56,3 +63,17 @@ class LRUSlotCache:
             rounds.append((subset, hits, copies))
             pending -= set(subset)
         return rounds
+
+    def prefetch(self, predicted, max_copies):
+        """Prefetch -> copies[(expert, slot)]."""
+        res = self.resident()
+        predicted = sorted(set(predicted))
+        want = [e for e in predicted if e not in res]
+        keep = {res[e] for e in predicted if e in res}
+        victims = sorted((s for s in range(self.S) if s not in keep), key=lambda s: (self.slot_stamp[s], s))
+        copies = list(zip(want[:max(0, max_copies)], victims))
+        self.clock += 1
+        for e, s in copies:
+            self.slot_expert[s] = e
+            self.slot_stamp[s] = self.clock
+        return copies

@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def run_slot_steps(wl, S, steps, T, seed_layer=0):
+def run_slot_steps(wl, S, steps, T, seed_layer=0, prefetch=False):
     s = wl.shape
     w13, w2 = synth.expert_weights(wl, seed_layer, device=DEV)
     wr = synth.router_weight(wl, seed_layer).to(DEV)
@@ -36,11 +36,17 @@ def run_slot_steps(wl, S, steps, T, seed_layer=0):
     ws = moe.alloc_workspace(T, s.d, s.I, s.E, s.k, moe.MODE_DECODE)
     xs = synth.ar1_activation_sequence(wl, T, seed_layer, steps, device="cpu")
     n_rounds = []
+    prev = set()
     for st in range(steps):
         x = xs[st].to(DEV)
+        if prefetch and prev:
+            # the previous step's experts, copied ahead of this step's rounds
+            n = cache.prefetch(prev, S, copy, ffn_done)
+            assert n == len(sim.prefetch(prev, S)), st
         r = moe.moe_route(x, wr, s.k)
         a = moe.moe_align(r.ids, s.E)
         need = {w[0] for w in moe.active_experts(a)}
+        prev = need
         expect = sim.step(need)
         pending = set(need)
         out = torch.empty((T, s.d), dtype=torch.bfloat16, device=DEV)
@@ -77,6 +83,13 @@ def test_slot_cache_olmoe_zipf_16_slots():
     n_rounds, hits, misses = run_slot_steps(synth.OLMOE_SLOT, 16, 6, 16)
     say(f"  rounds {n_rounds} hits {hits} misses {misses}")
     assert hits > 0 and misses > 0
+
+
+def test_slot_cache_prefetch_olmoe_zipf_16_slots():
+    say("slot cache prefetch olmoe zipf S=16")
+    n_rounds, hits, misses = run_slot_steps(synth.OLMOE_SLOT, 16, 6, 16, prefetch=True)
+    say(f"  rounds {n_rounds} hits {hits} misses {misses}")
+    assert hits > 0
 
 
 def test_slot_cache_injected_copy_failure(monkeypatch):

@@ -131,6 +131,24 @@ def test_lru_hand_traced():
     assert c.step({2}) == [([2], [2], [])]
 
 
+def test_prefetch_hand_traced():
+    c = LRUSlotCache(num_experts=8, num_slots=3)
+    c.step({5, 1})                                   # slots [1, 5, -], stamps [1, 1, -1]
+    # predicted {1, 2, 7}: 1 resident (its slot kept); 2, 7 go to the empty slot 2,
+    # then to slot 1 (expert 5, least recent among the rest)
+    assert c.prefetch({1, 2, 7}, 3) == [(2, 2), (7, 1)]
+    assert c.slot_expert == [1, 7, 2]
+    assert c.step({1, 2, 7}) == [([1, 2, 7], [1, 2, 7], [])]   # all hits now
+    d = LRUSlotCache(num_experts=8, num_slots=3)
+    d.step({5, 1})
+    assert d.prefetch({2, 7}, 1) == [(2, 2)]         # at most max_copies, ascending id
+    assert d.prefetch({7}, 0) == []
+    e = LRUSlotCache(num_experts=4, num_slots=2)
+    e.step({0, 1})
+    assert e.prefetch({0, 1, 2}, 5) == []            # every slot holds a predicted expert
+    assert e.slot_expert == [0, 1]
+
+
 def test_lru_never_evicts_a_hit_and_covers_all_needed():
     rng = np.random.default_rng(5)
     c = LRUSlotCache(num_experts=64, num_slots=16)

@@ -364,6 +364,19 @@ class SlotCache:
         got = {e for e in range(self.E) if (rm[e >> 6] >> (e & 63)) & 1}
         return got, nh.value, nm.value
 
+    def prefetch(self, predicted: set, max_copies: int, copy_stream, wait_event=None) -> int:
+        """Copy predicted experts ahead of their round; returns the number of copies."""
+        if wait_event is not None and wait_event.cuda_event == 0:
+            wait_event.record(torch.cuda.current_stream())
+        pm = (ctypes.c_uint64 * self.words)()
+        for e in predicted:
+            pm[e >> 6] |= 1 << (e & 63)
+        n = ctypes.c_int32()
+        check("slot_cache_prefetch", lib().slot_cache_prefetch(
+            self._h, pm, int(max_copies), ctypes.byref(n), ctypes.c_void_p(copy_stream.cuda_stream),
+            ctypes.c_void_p(wait_event.cuda_event) if wait_event is not None else None))
+        return n.value
+
     def state(self):
         se = (ctypes.c_int32 * self.S)()
         h, m = ctypes.c_int64(), ctypes.c_int64()

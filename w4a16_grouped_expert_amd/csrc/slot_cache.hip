@@ -19,7 +19,7 @@ struct moe_slot_cache {
   std::vector<int> slot_expert;    // [S] expert in slot or -1
   std::vector<int64_t> slot_stamp; // [S] last round that used the slot, -1 if never
   std::vector<int> expert_slot;    // [E] slot of expert or -1
-  int64_t clock = 0, hits = 0, misses = 0;
+  int64_t clock = 0, hits = 0, misses = 0, prefetches = 0;
   // ring of pinned staging tables for the per-round expert->slot map
   static constexpr int kRing = 8;
   int32_t* tables = nullptr;       // [kRing][E], pinned
@@ -167,6 +167,62 @@ extern "C" int slot_cache_load(moe_slot_cache* c, const uint64_t* pending_mask, 
   c->table_used[slot_idx] = true;
   if (n_hits) *n_hits = (int32_t)hits.size();
   if (n_misses) *n_misses = (int32_t)loaded.size();
+  return MOE_OK;
+}
+
+extern "C" int slot_cache_prefetch(moe_slot_cache* c, const uint64_t* predicted_mask, int max_copies,
+                                   int32_t* n_copies, void* copy_stream, void* wait_event) {
+  clear_error();
+  MOE_CHECK_ARG(c && predicted_mask && max_copies >= 0, MOE_ERR_INVALID_ARG, "slot_cache_prefetch: bad argument");
+  hipStream_t s = (hipStream_t)copy_stream;
+  const int E = c->E, S = c->S;
+  std::vector<int> want;
+  std::vector<char> keep(S, 0);
+  for (int e = 0; e < E; ++e) {
+    if (!((predicted_mask[e >> 6] >> (e & 63)) & 1ull)) continue;
+    if (c->expert_slot[e] >= 0)
+      keep[c->expert_slot[e]] = 1;
+    else
+      want.push_back(e);
+  }
+  std::vector<int> victims;
+  for (int sl = 0; sl < S; ++sl)
+    if (!keep[sl]) victims.push_back(sl);
+  std::stable_sort(victims.begin(), victims.end(),
+                   [&](int a, int b) { return c->slot_stamp[a] < c->slot_stamp[b]; });
+  const int n = std::min<int>(std::min<int>((int)want.size(), (int)victims.size()), max_copies);
+  if (n > 0 && wait_event && hipStreamWaitEvent(s, (hipEvent_t)wait_event, 0) != hipSuccess) {
+    set_error("slot_cache_prefetch: hipStreamWaitEvent failed");
+    return MOE_ERR_HIP;
+  }
+  c->clock += 1;
+  int done = 0;
+  for (int i = 0; i < n; ++i) {
+    const int e = want[i], sl = victims[i];
+    const int old = c->slot_expert[sl];
+    if (old >= 0) c->expert_slot[old] = -1;
+    c->slot_expert[sl] = -1;
+    c->slot_stamp[sl] = -1;
+    hipError_t err = hipSuccess;
+    if (c->fail_after == 0) {
+      err = hipErrorInvalidValue;
+    } else {
+      if (c->fail_after > 0) --c->fail_after;
+      err = hipMemcpyAsync(c->device_slots + (int64_t)sl * c->blob_bytes, c->host_store + (int64_t)e * c->blob_bytes,
+                           c->blob_bytes, hipMemcpyHostToDevice, s);
+    }
+    if (err != hipSuccess) {
+      set_error("slot_cache_prefetch: H2D copy of expert %d into slot %d failed: %s", e, sl, hipGetErrorString(err));
+      if (n_copies) *n_copies = done;
+      return MOE_ERR_HIP;
+    }
+    c->slot_expert[sl] = e;
+    c->expert_slot[e] = sl;
+    c->slot_stamp[sl] = c->clock;
+    ++done;
+  }
+  c->prefetches += done;
+  if (n_copies) *n_copies = done;
   return MOE_OK;
 }
 

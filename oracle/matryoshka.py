@@ -22,13 +22,15 @@ routing scores.  The abstract fixes none of the details; the readings taken:
   two-bit).
 
 Storage (this repository's layout m1): the h and l bits are kept in two separate
-planes, so a two-bit expert reads half of the code bytes.  A weight W[N, K] is cut
-into the 16 x 128 tiles of layout v1 (same tile order, same gate/up row
-interleave, same bf16 scale array); each plane tile is 512 bytes, lane L = 0..63
-owns the 8 bytes at offset 8 * L: little-endian 32-bit words j = 0, 1, word j
-holding K steps i = 2j and 2j + 1 of row L % 16, columns 32 i + 8 (L // 16) + m
-(m = 0..7) of the tile.  Inside word j, element (i, m) with t = i - 2j has pair
-index p = 4t + m // 2 and its 2-bit field starts at bit (5 + 2p + 16 (m % 2)) mod 32,
+planes, so a two-bit expert reads half of the code bytes.  A weight W[N, K] with
+N % 16 == 0 and K % 256 == 0 is cut into plane tiles of 16 rows x 256 columns (two
+quantisation groups), tile (nb, kb) at byte offset (nb * K/256 + kb) * 1024 of its
+plane, rows in the gate/up interleaved order of layout v1 and the same bf16 scale
+array; lane L = 0..63 owns the 16 bytes at offset 16 * L: little-endian 32-bit
+words j = 0..3, word j holding K steps i = 2j and 2j + 1 of row L % 16, columns
+32 i + 8 (L // 16) + m (m = 0..7) of the tile (steps 0-3 are the first group,
+4-7 the second).  Inside word j, element (i, m) with t = i - 2j has pair index
+p = 4t + m // 2 and its 2-bit field starts at bit (5 + 2p + 16 (m % 2)) mod 32,
 running upward and wrapping from bit 31 to bit 0; equivalently
 word = rotl32(u, 5), u = sum v << (2p + 16 (m % 2)).
 """
@@ -62,13 +64,17 @@ def dequant_floor(q, s):
 _PFIELD = np.array([[2 * (4 * t + m // 2) + 16 * (m % 2) for m in range(8)] for t in range(2)], dtype=np.uint32)
 
 
+PLANE_K = 256          # columns per plane tile (two groups)
+PLANE_TILE_BYTES = 1024
+
+
 def _plane_words(v):
-    """One plane (values 0..3, [N, K] in packed row order) -> uint32 words [N/16, K/128, 64, 2]."""
+    """One plane (values 0..3, [N, K] in packed row order) -> uint32 words [N/16, K/256, 64, 4]."""
     N, K = v.shape
-    # K index = kb*128 + 32*(2j + t) + 8*c + m ; row = nb*16 + r ; lane = 16*c + r
-    c7 = v.astype(np.uint32).reshape(N // 16, 16, K // 128, 2, 2, 4, 8)   # nb, r, kb, j, t, c, m
-    c7 = c7.transpose(0, 2, 5, 1, 3, 4, 6)                                # nb, kb, c, r, j, t, m
-    c7 = c7.reshape(N // 16, K // 128, 64, 2, 2, 8)                       # nb, kb, lane, j, t, m
+    # K index = kb*256 + 32*(2j + t) + 8*c + m ; row = nb*16 + r ; lane = 16*c + r
+    c7 = v.astype(np.uint32).reshape(N // 16, 16, K // PLANE_K, 4, 2, 4, 8)   # nb, r, kb, j, t, c, m
+    c7 = c7.transpose(0, 2, 5, 1, 3, 4, 6)                                    # nb, kb, c, r, j, t, m
+    c7 = c7.reshape(N // 16, K // PLANE_K, 64, 4, 2, 8)                       # nb, kb, lane, j, t, m
     u = np.bitwise_or.reduce(np.bitwise_or.reduce(c7 << _PFIELD, axis=-1), axis=-1).astype(np.uint32)
     return quant._rotl32(u, 5)
 
@@ -77,8 +83,8 @@ def pack_m1(q, s, gateup_interleave=False):
     """One matrix: q [N, K], s [N, K/128] -> (hi uint8 [N*K/4], lo uint8 [N*K/4], scales uint16)."""
     q = np.asarray(q)
     N, K = q.shape
-    if N % 16 or K % 128:
-        raise ValueError("N must be a multiple of 16 and K a multiple of 128")
+    if N % 16 or K % PLANE_K:
+        raise ValueError("N must be a multiple of 16 and K a multiple of 256")
     if gateup_interleave:
         order = quant.gateup_row_order(N)
         q, s = q[order], np.asarray(s)[order]
@@ -91,10 +97,10 @@ def pack_m1(q, s, gateup_interleave=False):
 
 def unpack_plane(plane, N, K, gateup_interleave=False):
     """Inverse of one plane of pack_m1: bytes -> values 0..3 [N, K] in source row order."""
-    words = np.asarray(plane, dtype=np.uint8).view("<u4").astype(np.uint32).reshape(N // 16, K // 128, 64, 2)
+    words = np.asarray(plane, dtype=np.uint8).view("<u4").astype(np.uint32).reshape(N // 16, K // PLANE_K, 64, 4)
     u = quant._rotr32(words, 5)
     v = (u[..., None, None] >> _PFIELD) & np.uint32(3)                   # nb, kb, lane, j, t, m
-    v = v.reshape(N // 16, K // 128, 4, 16, 2, 2, 8)                     # nb, kb, c, r, j, t, m
+    v = v.reshape(N // 16, K // PLANE_K, 4, 16, 4, 2, 8)                 # nb, kb, c, r, j, t, m
     v = v.transpose(0, 3, 1, 4, 5, 2, 6).reshape(N, K)                   # nb, r, kb, j, t, c, m
     if gateup_interleave:
         v = v[np.argsort(quant.gateup_row_order(N))]

@@ -64,7 +64,7 @@ def test_planes_match_hand_derived_golden_bytes():
 
 def test_plane_round_trip_and_nesting():
     rng = np.random.default_rng(3)
-    for N, K, inter in ((32, 256, False), (64, 128, True)):
+    for N, K, inter in ((32, 512, False), (64, 256, True)):
         q = rng.integers(-8, 8, size=(N, K)).astype(np.int8)
         s = np.ones((N, K // 128))
         hi, lo, _ = mat.pack_m1(q, s, gateup_interleave=inter)

@@ -50,6 +50,7 @@ def parse():
     p.add_argument("--no-slot-cache", action="store_true", help="skip the 16-slot cache workload")
     p.add_argument("--no-ablation", action="store_true", help="skip the fused vs per-expert ablation")
     p.add_argument("--no-bf16", action="store_true", help="skip the BF16-expert comparison")
+    p.add_argument("--no-mat", action="store_true", help="skip the nested two/four-bit comparison")
     p.add_argument("--slot-steps", type=int, default=24, help="timed steps of the slot-cache workload")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain device copy of known size (for HBM counter calibration)")
@@ -71,13 +72,13 @@ class Decoder:
     """16 resident MoE layers with shared per-step buffers: four-bit experts, or
     (bf16=True) the same experts unquantised for the W4 versus BF16 comparison."""
 
-    def __init__(self, wl, T_max, device, bf16=False):
+    def __init__(self, wl, T_max, device, bf16=False, mat=False):
         import torch
         import synth
         import w4a16_grouped_expert_amd as moe
         self.moe, self.torch = moe, torch
         s = wl.shape
-        self.wl, self.s, self.bf16 = wl, s, bf16
+        self.wl, self.s, self.bf16, self.mat, self.tau = wl, s, bf16, mat, 0.0
         self.layers = []
         for l in range(wl.layers):
             w13, w2 = synth.expert_weights(wl, l, device=device)
@@ -85,6 +86,8 @@ class Decoder:
                 bank = moe.pack_bf16_experts(w13, w2)
             else:
                 bank, lay = moe.pack_experts(w13, w2)
+                if mat:
+                    bank = moe.mat_from_w4(bank, s.d, s.I)
             del w13, w2
             wr = synth.router_weight(wl, l, device="cpu").to(device)
             self.layers.append((wr, bank))
@@ -109,6 +112,8 @@ class Decoder:
         moe.moe_route_align_into(x, wr, s.k, r, a, self.counter)
         if self.bf16:
             moe.moe_bf16_grouped_ffn_into(x, r, a, bank, s.I, self.out[l][:T], self.ws)
+        elif self.mat:
+            moe.moe_mat_grouped_ffn_into(x, r, a, bank, s.I, self.out[l][:T], self.ws, self.tau)
         else:
             moe.moe_w4a16_grouped_ffn_into(x, r, a, bank, s.I, self.out[l][:T], self.ws)
         return a
@@ -229,6 +234,46 @@ def run_bf16_compare(Ts, steps, warmup, x_sets, w4_tokens_per_s):
     torch.cuda.empty_cache()
     return {"workload": "olmoe_decode with BF16 experts (12.58 MB each, row-major, same route/align/combine)",
             "pages_w4_over_bf16": round(31.923 / 21.662, 3), "bytes_ratio": 3.879, **res}
+
+
+def run_mat_compare(Ts, taus, steps, warmup, x_sets, w4_tokens_per_s):
+    """Nested two/four-bit experts (layout m1): the same 16-layer decode with each
+    expert's precision from its routing weights (four bits when its largest weight
+    reaches tau); per T and tau the tokens/s from HIP graphs, the share of experts
+    at four bits and the weight bytes read, against the four-bit path."""
+    import torch
+    import synth
+    wl = synth.OLMOE_DECODE
+    s = wl.shape
+    dec = Decoder(wl, max(Ts), "cuda", mat=True)
+    res = {}
+    for T in Ts:
+        xs = [[synth.activations(wl, T, l, step=st, device="cuda") for l in range(wl.layers)] for st in range(x_sets)]
+        for tau in taus:
+            dec.tau = tau
+            r = run_decode(dec, T, steps, warmup, x_sets, timed_kernels=("gateup_mat", "down_mat", "combine", "route"))
+            # share of the step's experts at four bits (same decision as the kernels, from the routing weights)
+            n4 = n = 0
+            for xl in xs[:2]:
+                for l, x in enumerate(xl):
+                    a = dec.layer(l, x)
+                    U = int(a.active[0])
+                    act = a.active[4:4 + 4 * U].view(U, 4)[:, 0].long()
+                    wmax = torch.zeros(s.E, device="cuda").scatter_reduce(
+                        0, dec.route.ids[:T].reshape(-1).long(), dec.route.weights[:T].reshape(-1), "amax")
+                    n4 += int((wmax[act] >= tau).sum())
+                    n += U
+            frac4 = n4 / max(1, n)
+            res[f"T={T} tau={tau}"] = {
+                "tokens_per_s": round(r["tokens_per_s"], 1), "ms_per_step": round(r["ms_per_step"], 4),
+                "experts_at_four_bits": round(frac4, 3),
+                "kernels_us": {k: round(v["avg_us"], 3) for k, v in r["kernels"].items()},
+                "vs_w4": round(r["tokens_per_s"] / w4_tokens_per_s[T], 3)}
+    del dec
+    torch.cuda.empty_cache()
+    return {"workload": "olmoe_decode with nested two/four-bit experts (layout m1, same route/align/combine); "
+                        "four bits when an expert's largest routing weight in the step reaches tau, else two "
+                        "bits (high plane only, floor plus compensation)", **res}
 
 
 def expert_section_bytes(d, I):
@@ -658,10 +703,13 @@ def main():
             **{f"T={T}": run_ablation(dec, T, max(4, args.steps // 5)) for T in (args.tokens, 1)}}
     del dec
     torch.cuda.empty_cache()
+    w4 = {args.tokens: head["tokens_per_s"]}
+    w4.update({int(k[2:]): v["tokens_per_s"] for k, v in sweep.items()})
     if not args.no_bf16:
-        w4 = {args.tokens: head["tokens_per_s"]}
-        w4.update({int(k[2:]): v["tokens_per_s"] for k, v in sweep.items()})
         out["bf16_experts"] = run_bf16_compare(sorted(w4), args.steps, args.warmup, args.x_sets, w4)
+    if not args.no_mat:
+        out["nested_2_4_bit"] = run_mat_compare([t for t in (args.tokens, 1) if t in w4], (0.0, 0.14, 2.0),
+                                                args.steps, args.warmup, args.x_sets, w4)
     if args.prefill_tokens > 0:
         out["prefill"] = run_prefill(args.prefill_tokens)
         extra = {}

@@ -204,6 +204,43 @@ int moe_bf16_pack(const uint16_t* w13, const uint16_t* w2, int E, int d, int I, 
 int moe_bf16_grouped_ffn(const moe_ffn_args* args, void* stream);
 
 /*
+ * Nested two/four-bit experts (page "MatMoE: Dynamic Mixed-Precision
+ * Quantization for Efficient MoE Inference", arXiv abstract: one nested
+ * multi-precision representation, floor-and-compensation quantisation, each
+ * expert's bit-width from its routing scores), built on the four-bit codes of
+ * pack_w4_g128.
+ *
+ * Layout m1: each code c = q + 8 = 4h + l split into a high plane (h) and a low
+ * plane (l); plane tiles of 16 rows x 256 columns (two groups, 1024 bytes) at
+ * (row tile * K/256 + column tile) * 1024, rows in the gate/up interleaved order
+ * of layout v1, the bf16 scales of layout v1; lane L of a wavefront owns 16 bytes
+ * of each tile: 32-bit words j = 0..3 with K steps 2j, 2j+1 of row L % 16,
+ * columns 32 i + 8 (L / 16) + m; element m of K step 2j + t has its 2-bit field
+ * at bit (5 + 2 (4t + m/2) + 16 (m % 2)) mod 32.  Expert blob: w13 high plane |
+ * w13 low plane | w13 scales | w2 high | w2 low | w2 scales, each 256-byte
+ * aligned (moe_mat_layout_get; same blob size as layout v1).
+ *
+ * moe_mat_layout_get: section offsets and blob bytes for d, I (multiples of 256).
+ * moe_mat_from_w4: rewrite E four-bit blobs (layout v1, from pack_w4_g128) as
+ *   layout-m1 blobs (device to device on `stream`; same codes and scales).
+ * moe_mat_grouped_ffn: the grouped pass with a per-expert precision: an expert
+ *   runs at four bits, (4h + l - 8) * s = q * s, when the largest routing weight
+ *   among its pairs in this step is >= tau, else at two bits with the dropped
+ *   bits compensated by their mean, (4h + 1.5 - 8) * s, reading only the high
+ *   plane.  Arguments as moe_w4a16_grouped_ffn with `bank` holding layout-m1
+ *   blobs; `mode` ignored; workspace of moe_ffn_workspace_bytes(..., MOE_MODE_DECODE).
+ *   Limits: T <= 16, d <= 4096, d and I multiples of 256 (decode steps;
+ *   MOE_ERR_UNSUPPORTED_SHAPE otherwise), and those of moe_w4a16_grouped_ffn.
+ */
+typedef struct {
+  int64_t w13_hi, w13_lo, w13_scales, w2_hi, w2_lo, w2_scales, blob_bytes;
+} moe_mat_layout;
+int moe_mat_layout_get(int d, int I, moe_mat_layout* out);
+int moe_mat_from_w4(const uint8_t* w4_bank, int64_t w4_stride, int E, int d, int I, uint8_t* mat_bank,
+                    int64_t mat_stride, void* stream);
+int moe_mat_grouped_ffn(const moe_ffn_args* args, float tau, void* stream);
+
+/*
  * Expert slot cache (ExactMoE, Abstract: quantised experts in pinned host
  * memory, executed from a configurable GPU-resident slot cache).
  *
@@ -259,7 +296,8 @@ int moe_slot_cache_state(const moe_slot_cache* cache, int32_t* slot_expert,
  * events and returns the summed duration and launch count since the last reset.
  * Kernel ids: 0 = gate/up (decode), 1 = down (decode), 2 = gate/up (prefill),
  * 3 = down (prefill), 4 = combine, 5 = route logits, 6 = align, 7 = gate/up
- * (BF16 experts), 8 = down (BF16 experts).
+ * (BF16 experts), 8 = down (BF16 experts), 9 = gate/up (nested two/four-bit),
+ * 10 = down (nested two/four-bit).
  */
 int moe_timing_enable(int on);
 int moe_timing_reset(void);

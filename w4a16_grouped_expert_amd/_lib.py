@@ -32,6 +32,11 @@ class ExpertLayout(ctypes.Structure):
                 ("blob_bytes", c_i64)]
 
 
+class MatLayout(ctypes.Structure):
+    _fields_ = [("w13_hi", c_i64), ("w13_lo", c_i64), ("w13_scales", c_i64), ("w2_hi", c_i64), ("w2_lo", c_i64),
+                ("w2_scales", c_i64), ("blob_bytes", c_i64)]
+
+
 class FfnArgs(ctypes.Structure):
     _fields_ = [
         ("x", c_vp), ("T", c_int), ("d", c_int), ("I", c_int), ("E", c_int), ("k", c_int),
@@ -60,6 +65,9 @@ SIGNATURES = {
     "moe_bf16_expert_bytes": (c_i64, [c_int, c_int]),
     "moe_bf16_pack": (c_int, [c_vp, c_vp, c_int, c_int, c_int, c_vp, c_i64, c_vp]),
     "moe_bf16_grouped_ffn": (c_int, [ctypes.POINTER(FfnArgs), c_vp]),
+    "moe_mat_layout_get": (c_int, [c_int, c_int, ctypes.POINTER(MatLayout)]),
+    "moe_mat_from_w4": (c_int, [c_vp, c_i64, c_int, c_int, c_int, c_vp, c_i64, c_vp]),
+    "moe_mat_grouped_ffn": (c_int, [ctypes.POINTER(FfnArgs), ctypes.c_float, c_vp]),
     "moe_slot_cache_create": (c_int, [c_int, c_int, c_i64, c_vp, c_vp, ctypes.POINTER(c_vp)]),
     "moe_slot_cache_destroy": (c_int, [c_vp]),
     "slot_cache_load": (c_int, [c_vp, c_u64p, c_u64p, c_vp, c_i32p, c_i32p, c_vp, c_vp, c_vp]),

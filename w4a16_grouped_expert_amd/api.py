@@ -268,6 +268,49 @@ def moe_bf16_grouped_ffn(x, route, al, bank, I, stream=None):
     return moe_bf16_grouped_ffn_into(x, route, al, bank, I, out, ws, True, stream=stream)
 
 
+def mat_layout(d: int, I: int) -> dict:
+    lay = _lib.MatLayout()
+    check("moe_mat_layout_get", lib().moe_mat_layout_get(d, I, ctypes.byref(lay)))
+    return {f: getattr(lay, f) for f, _ in _lib.MatLayout._fields_}
+
+
+def mat_from_w4(w4_bank: torch.Tensor, d: int, I: int, stream=None) -> torch.Tensor:
+    """Nested two/four-bit bank (layout m1) from a four-bit bank (pack_experts)."""
+    _need(w4_bank, torch.uint8, "w4_bank")
+    E = w4_bank.shape[0]
+    stride = mat_layout(d, I)["blob_bytes"]
+    bank = torch.empty((E, stride), dtype=torch.uint8, device=w4_bank.device)
+    check("moe_mat_from_w4", lib().moe_mat_from_w4(_ptr(w4_bank), w4_bank.stride(0), E, d, I, _ptr(bank), stride,
+                                                   _stream(stream)))
+    return bank
+
+
+def moe_mat_grouped_ffn_into(x, route: RouteOut, al: AlignOut, bank: torch.Tensor, I: int, out: torch.Tensor,
+                             workspace: torch.Tensor, tau: float, combine=True,
+                             slot_of_expert: Optional[torch.Tensor] = None, stream=None):
+    """The grouped pass over nested two/four-bit blobs (mat_from_w4): an expert runs
+    at four bits when its largest routing weight in the step is >= tau, else at two."""
+    _need(x, torch.bfloat16, "x")
+    _need(bank, torch.uint8, "bank")
+    _need(workspace, torch.uint8, "workspace")
+    if combine:
+        _need(out, torch.bfloat16, "out")
+    T, d = x.shape
+    a = _lib.FfnArgs()
+    a.x, a.T, a.d, a.I, a.E, a.k = x.data_ptr(), T, d, I, route.logits.shape[1], route.ids.shape[1]
+    a.topk_ids, a.topk_weights = route.ids.data_ptr(), route.weights.data_ptr()
+    a.expert_offsets, a.sorted_pairs = al.offsets.data_ptr(), al.sorted_pairs.data_ptr()
+    a.pair_pos, a.active_experts = al.pair_pos.data_ptr(), al.active.data_ptr()
+    a.tile_offsets = al.tile_offsets.data_ptr() if al.tile_offsets is not None else None
+    a.bank, a.bank_stride = bank.data_ptr(), bank.stride(0)
+    a.slot_of_expert = slot_of_expert.data_ptr() if slot_of_expert is not None else None
+    a.mode, a.combine = MODE_DECODE, int(bool(combine))
+    a.out = out.data_ptr() if out is not None else None
+    a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
+    check("moe_mat_grouped_ffn", lib().moe_mat_grouped_ffn(ctypes.byref(a), float(tau), _stream(stream)))
+    return out
+
+
 def moe_w4a16_grouped_ffn(x, route, al, bank, I, mode=MODE_AUTO, slot_of_expert=None, stream=None):
     T, d = x.shape
     E, k = route.logits.shape[1], route.ids.shape[1]
@@ -387,7 +430,7 @@ class SlotCache:
 # ---------------------------------------------------------------- timing
 
 KERNELS = {"gateup_decode": 0, "down_decode": 1, "gateup_prefill": 2, "down_prefill": 3, "combine": 4,
-           "gateup_bf16": 7, "down_bf16": 8,
+           "gateup_bf16": 7, "down_bf16": 8, "gateup_mat": 9, "down_mat": 10,
            "route": 5, "align": 6}
 
 

@@ -30,7 +30,8 @@ int check_launch(const char* what);
 
 // Timing hooks (see moe_timing_*): bracket one launch of `kernel_id`.
 enum KernelId { K_GATEUP_DECODE = 0, K_DOWN_DECODE = 1, K_GATEUP_PREFILL = 2, K_DOWN_PREFILL = 3,
-                K_COMBINE = 4, K_ROUTE = 5, K_ALIGN = 6, K_GATEUP_BF16 = 7, K_DOWN_BF16 = 8, K_NUM = 9 };
+                K_COMBINE = 4, K_ROUTE = 5, K_ALIGN = 6, K_GATEUP_BF16 = 7, K_DOWN_BF16 = 8,
+                K_GATEUP_MAT = 9, K_DOWN_MAT = 10, K_NUM = 11 };
 void timing_begin(int kernel_id, hipStream_t s);
 void timing_end(int kernel_id, hipStream_t s);
 

@@ -170,6 +170,7 @@ extern "C" int moe_w4a16_grouped_ffn(const moe_ffn_args* a, void* stream) {
   f.P = (int64_t)a->T * a->k;
   f.umax = (int)std::min<int64_t>(a->E, f.P);
   f.topk_ids = a->topk_ids;
+  f.topk_weights = a->topk_weights;
   f.offsets = a->expert_offsets;
   f.sorted_pairs = a->sorted_pairs;
   f.pair_pos = a->pair_pos;

@@ -1,6 +1,8 @@
 // Device-side view of one grouped FFN call, shared by the decode and prefill kernels.
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace moe {
@@ -10,6 +12,7 @@ struct FfnDev {
   int T, d, I, E, k;
   int64_t P;          // T * k
   const int32_t* topk_ids;  // [T][k]
+  const float* topk_weights;  // [T][k]
   int umax;           // upper bound on active experts: min(E, P)
   const int32_t* offsets;
   const int32_t* sorted_pairs;

@@ -158,7 +158,7 @@ def test_align_edges():
 
 @pytest.mark.parametrize("T,E,k,renorm", [(1, 64, 8, True), (16, 64, 8, True), (16, 64, 8, False),
                                           (128, 64, 8, True), (16, 8, 2, True), (7, 1024, 16, True),
-                                          (2, 1024, 16, False), (129, 64, 8, True)])
+                                          (2, 1024, 16, False), (100, 64, 16, True), (129, 64, 8, True)])
 def test_route_align_fused_equals_separate(T, E, k, renorm):
     """moe_route_align (one launch up to 128 tokens, the separate calls above) gives
     bit-identical routing and permutation; three calls in a row reuse the counters."""

@@ -6,12 +6,13 @@
 //  1. expert counts;
 //  2. one block-wide scan gives the offsets, the compacted work list of active
 //     experts ({id, first position, count} each) and the per-expert tile counts;
-//  3. placement, 1024 pairs per pass in pair order: inside a wavefront the lanes
-//     that carry the same expert are found with ballots over the id bits, their
-//     rank is a popcount of the lower lanes; the per-wave counts are exchanged in
-//     LDS so each wavefront adds the counts of the earlier wavefronts of the pass
-//     and of the earlier passes.  Every pair lands at the unique stable position.
-// With at most 1024 pairs the per-wavefront counts of step 3 also give step 1.
+//  3. placement in pair order: inside a wavefront the lanes that carry the same
+//     expert are found with ballots over the id bits, their rank is a popcount of
+//     the lower lanes; the counts of the earlier wavefronts (and, for more than
+//     1024 pairs, of the wavefront's earlier pairs) come from LDS.  Every pair
+//     lands at the unique stable position.
+// With at most 1024 pairs the per-wavefront counts of step 3 also give step 1;
+// with more, each wavefront owns one contiguous chunk and counts it first.
 //
 // Shared by moe_align (its own kernel) and moe_route_align (the last workgroup of
 // the router kernel).
@@ -103,27 +104,28 @@ __device__ __forceinline__ void align_scan(int c, int E, int block_m, int tid, i
 // expert (lane_group) and its group leaders record the per-wavefront counts; the
 // expert totals are sums of those, and a pair's position is its expert's offset
 // plus the counts of its expert in the earlier wavefronts plus its rank.
-// More pairs: the counts come from LDS atomics first, then passes of
-// kAlignThreads pairs in pair order, each adding the counts of the earlier passes.
+// More pairs: each wavefront owns a contiguous chunk of the pairs (chunks in
+// pair order); it counts its chunk's experts, one block-wide pass turns the
+// counts into every (wavefront, expert) base position, and each wavefront places
+// its chunk 64 pairs at a time in order, advancing its own bases.
 __device__ __forceinline__ void align_block(const int32_t* __restrict__ ids, int P, int E, int block_m, int id_bits,
                                             int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
                                             int32_t* __restrict__ pair_pos, int32_t* __restrict__ active,
                                             int32_t* __restrict__ tile_offsets) {
-  __shared__ int s_count[MOE_MAX_EXPERTS];
   __shared__ int s_off[MOE_MAX_EXPERTS];
-  __shared__ uint16_t s_wcnt[kAlignWaves][MOE_MAX_EXPERTS];
+  __shared__ int s_wcnt[kAlignWaves][MOE_MAX_EXPERTS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int i = tid; i < kAlignWaves * E; i += kAlignThreads) s_wcnt[i / E][i % E] = 0;
+  __syncthreads();
   if (P <= kAlignThreads) {
-    __syncthreads();
     const int p = tid;
     const int e_in = p < P ? ids[p] : 0;
     const bool valid = p < P && e_in >= 0 && e_in < E;  // out-of-range ids are dropped
     const int e = valid ? e_in : 0;
     if (p < P && !valid) pair_pos[p] = -1;
     const LaneGroup lg = lane_group(e, valid, id_bits, lane);
-    if (valid && lg.rank == 0) s_wcnt[wave][e] = (uint16_t)lg.cnt;
+    if (valid && lg.rank == 0) s_wcnt[wave][e] = lg.cnt;
     __syncthreads();
     int c = 0;
     if (tid < E) {
@@ -142,40 +144,67 @@ __device__ __forceinline__ void align_block(const int32_t* __restrict__ ids, int
     return;
   }
 
-  for (int e = tid; e < E; e += kAlignThreads) s_count[e] = 0;
-  __syncthreads();
-  for (int p = tid; p < P; p += kAlignThreads) {
-    const int e = ids[p];
-    if (e >= 0 && e < E) atomicAdd(&s_count[e], 1);
+  // chunk of each wavefront: a multiple of 64 pairs, in pair order
+  const int chunk = (int)((((int64_t)P + kAlignWaves - 1) / kAlignWaves + 63) / 64 * 64);
+  const int c0 = min(P, wave * chunk), c1 = min(P, c0 + chunk);
+  constexpr int kU = 32;  // ids per lane loaded at once (2048 pairs per wavefront per batch)
+  for (int b = c0; b < c1; b += 64 * kU) {
+    int ev[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int p = b + 64 * u + lane;
+      ev[u] = p < c1 ? ids[p] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (ev[u] >= 0 && ev[u] < E) atomicAdd(&s_wcnt[wave][ev[u]], 1);
   }
   __syncthreads();
-  align_scan(tid < E ? s_count[tid] : 0, E, block_m, tid, lane, wave, s_off, offsets, active, tile_offsets);
+  // expert totals, offsets and work list; then each column of counts becomes the
+  // base positions of the wavefronts' chunks
+  int c = 0;
+  if (tid < E) {
+#pragma unroll
+    for (int w = 0; w < kAlignWaves; ++w) c += s_wcnt[w][tid];
+  }
+  align_scan(c, E, block_m, tid, lane, wave, s_off, offsets, active, tile_offsets);
   __syncthreads();
-  for (int e = tid; e < E; e += kAlignThreads) s_count[e] = 0;  // now: pairs placed so far
+  if (tid < E) {
+    int base = s_off[tid];
+#pragma unroll
+    for (int w = 0; w < kAlignWaves; ++w) {
+      const int n = s_wcnt[w][tid];
+      s_wcnt[w][tid] = base;
+      base += n;
+    }
+  }
   __syncthreads();
-
-  for (int base = 0; base < P; base += kAlignThreads) {
-    const int p = base + tid;
-    const int e_in = p < P ? ids[p] : 0;
-    const bool valid = p < P && e_in >= 0 && e_in < E;   // out-of-range ids are dropped
-    const int e = valid ? e_in : 0;
-    if (p < P && !valid) pair_pos[p] = -1;
-    const LaneGroup lg = lane_group(e, valid, id_bits, lane);
-    if (valid && lg.rank == 0) s_wcnt[wave][e] = (uint16_t)lg.cnt;
-    __syncthreads();
-    if (valid) {
-      int before = s_count[e];
-      for (int w = 0; w < wave; ++w) before += s_wcnt[w][e];
-      const int q = s_off[e] + before + lg.rank;
-      sorted_pairs[q] = p;
-      pair_pos[p] = q;
+  for (int b = c0; b < c1; b += 64 * kU) {
+    int ev[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int p = b + 64 * u + lane;
+      ev[u] = p < c1 ? ids[p] : -1;
     }
-    __syncthreads();
-    if (valid && lg.rank == 0) {
-      atomicAdd(&s_count[e], lg.cnt);
-      s_wcnt[wave][e] = 0;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int p = b + 64 * u + lane;
+      if (b + 64 * u >= c1) break;
+      const bool valid = p < c1 && ev[u] >= 0 && ev[u] < E;
+      const int e = valid ? ev[u] : 0;
+      if (p < c1 && !valid) pair_pos[p] = -1;
+      const LaneGroup lg = lane_group(e, valid, id_bits, lane);
+      // every lane reads its base before the group leader advances it (one wavefront:
+      // the LDS read and write are issued in this order)
+      const int q = valid ? s_wcnt[wave][e] + lg.rank : 0;
+      __builtin_amdgcn_wave_barrier();
+      if (valid && lg.rank == 0) s_wcnt[wave][e] = q + lg.cnt;
+      __builtin_amdgcn_wave_barrier();
+      if (valid) {
+        sorted_pairs[q] = p;
+        pair_pos[p] = q;
+      }
     }
-    __syncthreads();
   }
 }
 

@@ -3,15 +3,15 @@
 // Inference", Abstract: all selected experts through fused grouped kernels on
 // four-bit group-128 weights).
 //
-// A block of eight wavefronts computes a 512 (weight rows) x 128 (tokens of one
-// expert) tile; wavefront w owns rows 64 w .. 64 w + 63 for all 128 tokens as
-// 4 x 8 blocks of 16x16x32 bf16 MFMA.  Per K group of 128 the block stages,
-// double-buffered in LDS by LDS-DMA (global_load_lds, no registers): the 128
-// activation rows (gathered through the permutation; 16-byte chunks XOR-swizzled
-// so the MFMA B-fragment reads are bank-conflict free), the 32 packed 16 x 128
-// weight tiles and the per-token activation sums; the bf16 scales run one group
-// further ahead in a ring of their own.  Weights are decoded in registers to
-// bf16 1 + c/16.
+// A block of eight wavefronts computes a 256 (weight rows) x 128 (tokens of one
+// expert) tile; wavefront w owns rows 64 (w % 4) .. + 63 and tokens 64 (w / 4) ..
+// + 63 as 4 x 4 blocks of 16x16x32 bf16 MFMA.  Per K group of 128 the block
+// stages, in a 3-stage LDS pipeline filled by LDS-DMA (buffer_load ... lds, no
+// registers): the 128 activation rows (gathered through the permutation; 16-byte
+// chunks XOR-swizzled so the MFMA B-fragment reads are bank-conflict free) and the
+// 16 packed 16 x 128 weight tiles; the per-token activation sums ride one group
+// ahead and the bf16 scales two, in rings of their own.  Weights are decoded in
+// registers to bf16 1 + c/16.
 //
 // One accumulator per output carries the whole K loop.  With D_g the group's
 // sum of (c - 8) x / 16 and e_g the group's scale (a zero scale replaced by the

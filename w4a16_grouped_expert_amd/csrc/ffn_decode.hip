@@ -379,6 +379,172 @@ __global__ __launch_bounds__(512, 4) void k_gateup_dense(FfnDev f, uint16_t* __r
   }
 }
 
+// The same gate/up pass with each stripe's K range split over a pair of
+// wavefronts of the workgroup, for steps with few active experts (few stripes):
+// twice the wavefronts stream weights.  Wavefront w works on stripe slot w % 4 of
+// the workgroup's round and K half w / 4; the upper half hands its sums to the
+// lower half through LDS (lower + upper, in that order), which applies SwiGLU.
+// Rounds are workgroup-uniform (every wavefront meets every barrier).
+template <int RT, int NB, int MAXG>
+__global__ __launch_bounds__(512, 4) void k_gateup_dense_ks2(FfnDev f, uint16_t* __restrict__ hout) {
+  constexpr int kWaves = 8, kSlots = 4;
+  const int G = f.d / kGroup;
+  const int n_stripes = 2 * f.I / (kTileRows * RT);
+  const int n_items = f.umax * n_stripes;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = lane_id();
+  const int slot = wave & (kSlots - 1), half = wave >> 2;
+  const int col = lane & 15, kq = lane >> 4;
+  const int stride_items = gridDim.x * kSlots;
+  const i32x4_t* work = reinterpret_cast<const i32x4_t*>(f.active + 4);
+  const int U = f.active[0];
+  const int64_t tile_stride_c = (int64_t)G * kTileBytes;
+  const int64_t tile_stride_s = (int64_t)G * kTileRows;
+  const int gh = (G + 1) / 2;
+  const int g0 = half ? gh : 0, g1 = half ? G : gh;
+
+  struct Buf {
+    u32x4_t c[RT];
+    u32x2_t s[RT];
+  };
+  Buf buf[NB];
+  const uint8_t* codes = nullptr;
+  const uint16_t* scales = nullptr;
+  auto load = [&](Buf& b, int g) {
+    const int gl = min(g, g1 - 1);
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      b.c[r] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4_t*>(codes + r * tile_stride_c + (int64_t)gl * kTileBytes));
+      b.s[r] = *reinterpret_cast<const u32x2_t*>(scales + r * tile_stride_s + gl * kTileRows);
+    }
+  };
+  // round setup: this wavefront's item, its pointers and its first NB - 1 loads
+  int e = -1, row0 = 0, stripe = 0;
+  auto setup = [&](int base) {
+    const int item = base + slot;
+    e = -1;
+    if (item < n_items && item / n_stripes < U) {
+      const i32x4_t cur = work[item / n_stripes];
+      const uint8_t* blob = f.blob(cur[0]);
+      if (blob) {
+        stripe = item % n_stripes;
+        codes = blob + f.off_w13_codes + (int64_t)(RT * stripe) * G * kTileBytes + 16 * lane;
+        scales = reinterpret_cast<const uint16_t*>(blob + f.off_w13_scales) + (int64_t)(RT * stripe) * G * kTileRows +
+                 4 * kq;
+#pragma unroll
+        for (int j = 0; j < NB - 1; ++j) load(buf[j], g0 + j);
+        e = cur[0];
+        row0 = cur[1];
+      }
+    }
+  };
+  int base = blockIdx.x * kSlots;
+  setup(base);
+
+  __shared__ u32x4_t s_x[MAXG * 4 * 64];
+  __shared__ float s_xs[MAXG * 16];
+  __shared__ int s_ids[16][MOE_MAX_TOPK];
+  __shared__ f32x4_t s_part[kSlots][RT][64];
+  {
+    const u32x4_t ones_w = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    const bf16x8_t ones = as_bf16x8(ones_w);
+    const __amdgpu_buffer_rsrc_t xres =
+        __builtin_amdgcn_make_buffer_rsrc((void*)f.x, (short)0, (int)(f.T * f.d * 2), kBufferRsrcWord3);
+    const uint32_t xoff = (uint32_t)(col * f.d + 8 * kq) * 2u;
+    for (int g = wave; g < G; g += kWaves) {
+      u32x4_t xv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        xv[i] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xres, xoff + (uint32_t)(g * kGroup + 32 * i) * 2u, 0, 0));
+      f32x4_t as = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s_x[(4 * g + i) * 64 + lane] = xv[i];
+        as = mfma16x16x32(ones, as_bf16x8(xv[i]), as);
+      }
+      if (lane < 16) s_xs[g * 16 + lane] = as[0];
+    }
+    for (int i = threadIdx.x; i < 16 * MOE_MAX_TOPK; i += kWaves * 64) {
+      const int t = i / MOE_MAX_TOPK, j = i % MOE_MAX_TOPK;
+      s_ids[t][j] = (j < f.k && t < f.T) ? f.topk_ids[t * f.k + j] : -1;
+    }
+  }
+  __syncthreads();
+  const uint32_t kMask = vgpr_const(0x00780078u), kOne = vgpr_const(0x3F803F80u);
+
+  // rounds continue while the workgroup's first slot has an active item (items are
+  // visited in increasing expert order, so later slots have none either otherwise)
+  while (base < n_items && base / n_stripes < U) {
+    f32x4_t tot[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) tot[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int cur_e = e, cur_row0 = row0, cur_stripe = stripe;
+    if (cur_e >= 0) {
+      auto compute = [&](const Buf& b, int g) {
+        const int gl = min(g, g1 - 1);
+        const float gv = g < g1 ? 1.f : 0.f;
+        const float xs = -24.f * s_xs[gl * 16 + col];
+        f32x4_t acc[RT];
+#pragma unroll
+        for (int r = 0; r < RT; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bf16x8_t xv = as_bf16x8(s_x[(4 * gl + i) * 64 + lane]);
+#pragma unroll
+          for (int r = 0; r < RT; ++r)
+            acc[r] = mfma16x16x32(as_bf16x8(decode_word_biased(b.c[r][i], kMask, kOne)), xv, acc[r]);
+        }
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+          const float s4[4] = {__uint_as_float(b.s[r][0] << 16), __uint_as_float(b.s[r][0] & 0xFFFF0000u),
+                               __uint_as_float(b.s[r][1] << 16), __uint_as_float(b.s[r][1] & 0xFFFF0000u)};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) tot[r][q] = fmaf(gv * s4[q], fmaf(16.f, acc[r][q], xs), tot[r][q]);
+        }
+      };
+      for (int gc = g0; gc < g1; gc += NB) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          load(buf[(j + NB - 1) % NB], gc + j + NB - 1);
+          compute(buf[j], gc + j);
+        }
+      }
+    }
+    base += stride_items;
+    setup(base);  // the next round's first loads go out before the hand-over
+    if (half == 1 && cur_e >= 0) {
+#pragma unroll
+      for (int r = 0; r < RT; ++r) s_part[slot][r][lane] = tot[r];
+    }
+    __syncthreads();
+    if (half == 0 && cur_e >= 0) {
+      bool routed = false;
+      for (int j = 0; j < f.k; ++j) routed |= (s_ids[col][j] == cur_e);
+      const uint32_t colmask = (uint32_t)__ballot(routed) & 0xFFFFu;
+      const int out_row = cur_row0 + __popc(colmask & ((1u << col) - 1u));
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        const f32x4_t o = s_part[slot][r][lane];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) tot[r][q] = tot[r][q] + o[q];
+      }
+#pragma unroll
+      for (int p = 0; p < RT / 2; ++p) {
+        uint32_t hv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) hv[q] = f32_to_bf16_bits(silu_f32(tot[2 * p][q]) * tot[2 * p + 1][q]);
+        if (routed) {
+          const int hcol = kTileRows * ((RT / 2) * cur_stripe + p) + 4 * kq;
+          u32x2_t o = {hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16)};
+          *reinterpret_cast<u32x2_t*>(hout + (int64_t)out_row * f.I + hcol) = o;
+        }
+      }
+    }
+    __syncthreads();  // s_part is free for the next round
+  }
+}
+
 template <int NB, int RT, int GPW, bool GATEUP>
 __global__ __launch_bounds__(256) void k_ffn_decode(FfnDev f, const uint16_t* __restrict__ hin,
                                                     uint16_t* __restrict__ hout, float* __restrict__ y, int ksplit) {
@@ -612,12 +778,18 @@ int launch_decode(const FfnDev& f, uint16_t* h, float* y, int ksplit, int nb, hi
     timing_begin(K_GATEUP_DECODE, s);
     if (f.d <= 32 * kGroup) {
       const int G = f.d / kGroup;
-      // d <= 2048: 2 workgroups per CU and 4 wavefronts per SIMD; d <= 4096: 1 (LDS)
-      auto kgu = G <= 16 ? k_gateup_dense<kDenseRT, kDenseNB, 16> : k_gateup_dense<kDenseRT, kDenseNB, 32>;
-      const int slot = G <= 16 ? 4 : 5;
+      // d <= 2048: 2 workgroups per CU and 4 wavefronts per SIMD; d <= 4096: 1 (LDS).
+      // Few stripes (at most half the resident wavefronts): K split over wavefront pairs.
       const int64_t items_gu = umax * (2 * f.I / (kTileRows * kDenseRT));
-      const int64_t grid_gu = std::min<int64_t>(persistent_grid(kgu, slot, 512), ceil_div(items_gu, 8));
-      hipLaunchKernelGGL(kgu, dim3((unsigned)grid_gu), dim3(512), 0, s, f, h);
+      auto kgu = G <= 16 ? k_gateup_dense<kDenseRT, kDenseNB, 16> : k_gateup_dense<kDenseRT, kDenseNB, 32>;
+      const int64_t cap = persistent_grid(kgu, G <= 16 ? 4 : 5, 512);
+      if (G >= 2 * kDenseNB && items_gu * 2 <= cap * 8) {
+        auto kks = G <= 16 ? k_gateup_dense_ks2<kDenseRT, kDenseNB, 16> : k_gateup_dense_ks2<kDenseRT, kDenseNB, 32>;
+        const int64_t grid_ks = std::min<int64_t>(persistent_grid(kks, G <= 16 ? 6 : 7, 512), ceil_div(items_gu, 4));
+        hipLaunchKernelGGL(kks, dim3((unsigned)grid_ks), dim3(512), 0, s, f, h);
+      } else {
+        hipLaunchKernelGGL(kgu, dim3((unsigned)std::min<int64_t>(cap, ceil_div(items_gu, 8))), dim3(512), 0, s, f, h);
+      }
     } else {
       auto kgu = ring ? k_decode_persist<kPersistRT, kRingNG, true, true, true>
                       : k_decode_persist<kPersistRT, kPersistNG, true, true, false>;

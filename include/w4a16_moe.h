@@ -175,7 +175,15 @@ typedef struct {
   int64_t workspace_bytes;
 } moe_ffn_args;
 
-/* Workspace the call needs for these sizes and mode (bytes). */
+/* Workspace the call needs for these sizes and mode (bytes).
+ * moe_w4a16_grouped_ffn: the experts of a token must be distinct (as moe_route
+ * returns them).  Decode steps of at most 16 tokens called with combine = 1 and
+ * slot_of_expert = NULL finish the combine inside the down pass (each group's
+ * contribution scaled by its routing weight as it is accumulated, partial sums
+ * added in a fixed order): the output is deterministic but is not bit-identical
+ * to the two-pass combine, and no per-pair results are left in the workspace.
+ * Calls with a slot table keep the two passes, so subsets of the experts can run
+ * in separate calls with combine = 0 and the last one combines. */
 int64_t moe_ffn_workspace_bytes(int T, int d, int I, int E, int k, int mode);
 int moe_w4a16_grouped_ffn(const moe_ffn_args* args, void* stream);
 

@@ -63,7 +63,10 @@ def run_slot_steps(wl, S, steps, T, seed_layer=0, prefetch=False):
         assert rounds == len(expect)
         slot_state, _, _ = cache.state()
         assert slot_state == sim.slot_expert
-        ref_out = moe.moe_w4a16_grouped_ffn(x, r, a, bank, s.I, mode=moe.MODE_DECODE)
+        # all experts resident, through an all-experts slot table: the same two-pass
+        # kernels as the slot-cache calls, so the outputs agree bit for bit
+        ident = torch.arange(s.E, dtype=torch.int32, device=DEV)
+        ref_out = moe.moe_w4a16_grouped_ffn(x, r, a, bank, s.I, mode=moe.MODE_DECODE, slot_of_expert=ident)
         torch.cuda.synchronize()
         assert torch.equal(out, ref_out), f"step {st}"
         n_rounds.append(rounds)

@@ -51,6 +51,8 @@ constexpr int kTileBytes = 1024;     // bytes per packed tile (16 x 128 x 4 bit)
 // Word 3 of a raw (unswizzled, stride 0) buffer resource on gfx9: 32-bit data
 // format; offsets at or past num_records read as zero.
 constexpr int kBufferRsrcWord3 = 0x00020000;
+// Cache-policy operand of the raw buffer builtins on gfx950: bit 1 = nt (streaming).
+constexpr int kCacheNonTemporal = 2;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 

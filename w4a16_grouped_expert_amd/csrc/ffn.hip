@@ -77,8 +77,12 @@ static int down_ksplit(int T, int d, int I, int E, int k, int mode) {
 static int64_t align256(int64_t v) { return (v + 255) / 256 * 256; }
 
 struct WsLayout {
-  int64_t h_off, y_off, xsum_off, hsum_off, total;
+  int64_t h_off, y_off, xsum_off, hsum_off, dc_part_off, dc_ctr_off, total;
 };
+
+// fused down + combine (steps of at most 16 tokens): up to 32 chunks x 512
+// partial values per 32-row output stripe, and one counter per stripe
+static int64_t dc_part_bytes(int d) { return (int64_t)(d / 32) * 32 * 512 * 4; }
 
 static WsLayout ws_layout(int T, int d, int I, int E, int k, int mode) {
   const int64_t P = (int64_t)T * k;
@@ -89,6 +93,12 @@ static WsLayout ws_layout(int T, int d, int I, int E, int k, int mode) {
   L.xsum_off = L.y_off + align256((int64_t)ks * P * d * 4);
   L.hsum_off = L.xsum_off;
   L.total = L.xsum_off;
+  L.dc_part_off = L.dc_ctr_off = -1;
+  if (mode == MOE_MODE_DECODE && T <= 16) {
+    L.dc_part_off = L.total;
+    L.dc_ctr_off = L.dc_part_off + align256(dc_part_bytes(d));
+    L.total = L.dc_ctr_off + align256((int64_t)(d / 32) * 4);
+  }
   if (mode == MOE_MODE_PREFILL) {
     L.hsum_off = L.xsum_off + align256((int64_t)T * (d / kGroup) * 4);
     L.total = L.hsum_off + align256(P * (I / kGroup) * 4);
@@ -104,6 +114,8 @@ FfnWorkspace ffn_workspace(int T, int d, int I, int E, int k, int mode, void* ws
   w.y = reinterpret_cast<float*>(b + L.y_off);
   w.xsum = reinterpret_cast<float*>(b + L.xsum_off);
   w.hsum = reinterpret_cast<float*>(b + L.hsum_off);
+  w.dc_part = L.dc_part_off >= 0 ? reinterpret_cast<float*>(b + L.dc_part_off) : nullptr;
+  w.dc_counters = L.dc_ctr_off >= 0 ? reinterpret_cast<int32_t*>(b + L.dc_ctr_off) : nullptr;
   w.ksplit = down_ksplit(T, d, I, E, k, mode);
   return w;
 }
@@ -186,13 +198,18 @@ extern "C" int moe_w4a16_grouped_ffn(const moe_ffn_args* a, void* stream) {
 
   const FfnWorkspace w = ffn_workspace(a->T, a->d, a->I, a->E, a->k, mode, a->workspace);
   hipStream_t s = (hipStream_t)stream;
+  // every expert in the call and the combine requested: at most 16 tokens finish
+  // the combine inside the down pass
+  const bool fused = mode == MOE_MODE_DECODE && a->T <= 16 && a->combine && !a->slot_of_expert && w.dc_part &&
+                     a->bank_stride < ((int64_t)1 << 31) && dc_units_per_wave(f.umax, a->I / kGroup, a->d / 32) > 0;
   if (mode == MOE_MODE_DECODE) {
     const double per_expert = (double)a->T * a->k / a->E;
-    rc = launch_decode(f, w.h, w.y, w.ksplit, per_expert <= 8.0 ? 1 : 2, s);
+    rc = launch_decode(f, w.h, w.y, w.ksplit, per_expert <= 8.0 ? 1 : 2, s, fused ? a->out : nullptr, w.dc_part,
+                       w.dc_counters);
   } else {
     rc = launch_prefill(f, w.h, w.y, w.xsum, w.hsum, s);
   }
   if (rc) return rc;
-  if (a->combine) rc = launch_combine(f, w.y, w.ksplit, a->topk_weights, a->out, s);
+  if (a->combine && !fused) rc = launch_combine(f, w.y, w.ksplit, a->topk_weights, a->out, s);
   return rc;
 }

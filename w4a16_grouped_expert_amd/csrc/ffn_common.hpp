@@ -23,6 +23,9 @@ struct FfnDev {
   int64_t bank_stride;
   const int32_t* slot_of_expert;
   int64_t off_w13_codes, off_w13_scales, off_w2_codes, off_w2_scales;
+  // counters of the fused down + combine pass, zeroed by the gate/up pass before it
+  int32_t* zero_ctr = nullptr;
+  int n_zero_ctr = 0;
 
   // Blob of expert e, or nullptr when the expert is not part of this call.
   __device__ __forceinline__ const uint8_t* blob(int e) const {
@@ -31,21 +34,34 @@ struct FfnDev {
   }
 };
 
+__device__ __forceinline__ void zero_down_counters(const FfnDev& f) {
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < f.n_zero_ctr; i += blockDim.x) f.zero_ctr[i] = 0;
+}
+
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
 
-// Workspace of one call: h [T*k][I] bf16, y [ksplit][T*k][d] fp32, and for the
-// prefill variant the group sums of x and h.
+// Workspace of one call: h [T*k][I] bf16, y [ksplit][T*k][d] fp32, for the
+// prefill variant the group sums of x and h, and for steps of at most 16 tokens
+// the partial sums and stripe counters of the fused down + combine pass.
 struct FfnWorkspace {
   uint16_t* h;
   float* y;
   float* xsum;
   float* hsum;
+  float* dc_part;       // [d / 32][32][512] fp32, or nullptr
+  int32_t* dc_counters;  // [d / 32], or nullptr
   int ksplit;
 };
 FfnWorkspace ffn_workspace(int T, int d, int I, int E, int k, int mode, void* ws);
 int launch_combine(const FfnDev& f, const float* y, int ksplit, const float* weights, uint16_t* out, hipStream_t s);
 
-int launch_decode(const FfnDev& f, uint16_t* h, float* y, int ksplit, int nb, hipStream_t s);
+// out != nullptr (T <= 16, dc_part and dc_counters set): the down pass also
+// performs the routing-weighted combine into out, and y is not written.
+int launch_decode(const FfnDev& f, uint16_t* h, float* y, int ksplit, int nb, hipStream_t s,
+                  uint16_t* out = nullptr, float* dc_part = nullptr, int32_t* dc_counters = nullptr);
+// Units per wavefront of the fused down + combine pass, 0 if the step is too large for it.
+int dc_units_per_wave(int umax, int G, int stripes);
 int launch_prefill(const FfnDev& f, uint16_t* h, float* y, float* xsum, float* hsum, hipStream_t s);
 int64_t prefill_extra_bytes(int T, int d, int I, int k);
 

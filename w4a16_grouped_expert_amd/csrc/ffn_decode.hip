@@ -55,6 +55,7 @@ template <int RT, int NG, bool GATEUP, bool DENSE, bool RING>
 __global__ __launch_bounds__(256) void k_decode_persist(FfnDev f, const uint16_t* __restrict__ hin,
                                                         uint16_t* __restrict__ hout, float* __restrict__ y,
                                                         int ksplit) {
+  if (GATEUP) zero_down_counters(f);
   const int K = GATEUP ? f.d : f.I;
   const int N = GATEUP ? 2 * f.I : f.d;
   const int G = K / kGroup;
@@ -236,6 +237,7 @@ __global__ __launch_bounds__(256) void k_decode_persist(FfnDev f, const uint16_t
 // are issued before the staging, whose latency they hide.
 template <int RT, int NB, int MAXG>
 __global__ __launch_bounds__(512, 4) void k_gateup_dense(FfnDev f, uint16_t* __restrict__ hout) {
+  zero_down_counters(f);
   constexpr int kWaves = 8;
   const int G = f.d / kGroup;
   const int n_stripes = 2 * f.I / (kTileRows * RT);
@@ -387,6 +389,7 @@ __global__ __launch_bounds__(512, 4) void k_gateup_dense(FfnDev f, uint16_t* __r
 // Rounds are workgroup-uniform (every wavefront meets every barrier).
 template <int RT, int NB, int MAXG>
 __global__ __launch_bounds__(512, 4) void k_gateup_dense_ks2(FfnDev f, uint16_t* __restrict__ hout) {
+  zero_down_counters(f);
   constexpr int kWaves = 8, kSlots = 4;
   const int G = f.d / kGroup;
   const int n_stripes = 2 * f.I / (kTileRows * RT);
@@ -542,6 +545,187 @@ __global__ __launch_bounds__(512, 4) void k_gateup_dense_ks2(FfnDev f, uint16_t*
       }
     }
     __syncthreads();  // s_part is free for the next round
+  }
+}
+
+// Down projection and routing-weighted combine in one pass, for steps of at most
+// 16 tokens whose experts all take part in the call.  The combine is linear, so
+// every group's contribution is scaled by the routing weight of its (token,
+// expert) pair as it is accumulated: each partial sum is then already a sum over
+// the token's routed outputs, and no per-pair fp32 result leaves the kernel.
+//
+// Work split: a wavefront owns one output stripe of RT tiles (16 RT rows of d),
+// one active expert and one slice of UPW of its K groups (the 16 MFMA columns
+// being the step's tokens, as in the gate/up pass); a workgroup holds WAVES
+// consecutive (expert, slice) items of one stripe, a chunk of the stripe's list.
+// The slice is unrolled completely: the loads of group i + D (weights, scales,
+// the pairs' h fragments) go out before group i is multiplied, in straight-line
+// code with no branch, so the compiler counts the loads to wait for exactly and
+// never moves registers that a load in flight will write.  The wavefronts meet
+// in LDS in wavefront order, and the workgroup stores its 16 tokens x 16 RT rows
+// of partial sums with device-coherent stores; the workgroup that counts itself
+// last on the stripe's counter adds the chunks' partials in chunk order and
+// writes the bf16 rows.  The counters are zeroed by the gate/up pass, which runs
+// before this one on the stream.
+constexpr int kDcMaxChunks = 32;
+
+template <int RT, int D, int UPW, int WAVES, int OCC>
+__global__ __launch_bounds__(WAVES * 64, OCC) void k_down_combine(FfnDev f, const uint16_t* __restrict__ h,
+                                                                  uint16_t* __restrict__ out,
+                                                                  float* __restrict__ part,
+                                                                  int32_t* __restrict__ counters) {
+  constexpr int kRows = RT * kTileRows, kValues = 16 * kRows;  // 16 tokens x the stripe's rows
+  constexpr int kThreads = WAVES * 64, kPer = kValues / kThreads;
+  static_assert(kValues % kThreads == 0, "whole partial values per thread");
+  const int G = f.I / kGroup;
+  const int n_slices = (G + UPW - 1) / UPW;
+  const int n_stripes = f.d / (kTileRows * RT);
+  const int stripe = blockIdx.x % n_stripes, chunk = blockIdx.x / n_stripes;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = lane_id();
+  const int col = lane & 15, kq = lane >> 4;
+  const int item = chunk * WAVES + wave;
+  // the active count, the wavefront's work record (read within the work list's
+  // capacity, used only if the item exists) and the routing table: one round trip
+  const int U = f.active[0];
+  const i32x4_t rec = reinterpret_cast<const i32x4_t*>(f.active + 4)[min(item / n_slices, f.umax - 1)];
+
+  __shared__ int s_ids[16][MOE_MAX_TOPK];
+  __shared__ float s_w[16][MOE_MAX_TOPK];
+  __shared__ f32x4_t s_red[WAVES][RT][64];
+  __shared__ int s_last;
+  for (int i = tid; i < 16 * MOE_MAX_TOPK; i += kThreads) {
+    const int t = i / MOE_MAX_TOPK, j = i % MOE_MAX_TOPK;
+    const bool in = j < f.k && t < f.T;
+    s_ids[t][j] = in ? f.topk_ids[t * f.k + j] : -1;
+    s_w[t][j] = in ? f.topk_weights[t * f.k + j] : 0.f;
+  }
+  const int n_items = U * n_slices;
+  const int nch = (n_items + WAVES - 1) / WAVES;          // chunks with work on every stripe
+  if (chunk >= nch && !(chunk == 0 && nch == 0)) return;  // (no active expert: chunk 0 writes zeros)
+  __syncthreads();
+
+  f32x4_t tot[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) tot[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if (item < n_items) {
+    const int e = rec[0];
+    const int g0 = (item % n_slices) * UPW, ng = min(UPW, G - g0);
+    const int slot = f.slot_of_expert ? f.slot_of_expert[e] : e;
+    const uint32_t kMask = vgpr_const(0x00780078u), kOne = vgpr_const(0x3F803F80u);
+    const u32x4_t ones_w = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    const bf16x8_t ones = as_bf16x8(ones_w);
+    const __amdgpu_buffer_rsrc_t hres =
+        __builtin_amdgcn_make_buffer_rsrc((void*)h, (short)0, (int)(f.P * f.I * 2), kBufferRsrcWord3);
+    const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(f.bank + (int64_t)slot * f.bank_stride), (short)0, 0x7FFFFFFF, kBufferRsrcWord3);
+    // the lane's token: its slot for expert e (if routed there), its h row
+    int hit = -1;
+    for (int j = 0; j < f.k; ++j) hit = s_ids[col][j] == e ? j : hit;
+    const uint32_t colmask = (uint32_t)__ballot(hit >= 0) & 0xFFFFu;
+    const int hrow = rec[1] + __popc(colmask & ((1u << col) - 1u));
+    const uint32_t hoff = hit >= 0 ? (uint32_t)(hrow * f.I + 8 * kq) * 2u : 0x7F000000u;  // else reads zeros
+    const float wt = hit >= 0 ? s_w[col][hit] : 0.f;
+    const uint32_t voff_c = 16u * lane, voff_s = 8u * kq;
+    const uint32_t soff_c = (uint32_t)(f.off_w2_codes + (int64_t)(RT * stripe) * G * kTileBytes);
+    const uint32_t soff_s = (uint32_t)(f.off_w2_scales + (int64_t)(RT * stripe) * G * kTileRows * 2);
+
+    struct Buf {
+      u32x4_t c[RT];
+      u32x2_t s[RT];
+      u32x4_t x[4];
+    };
+    // group i of the slice; past the slice's end the loads repeat its last group
+    // (weight 0), so the loads and their waits do not depend on the slice length
+    auto load = [&](Buf& b, int i) {
+      const int g = g0 + min(i, ng - 1);
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        b.c[r] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                         wres, voff_c, soff_c + (uint32_t)(r * G + g) * kTileBytes, kCacheNonTemporal));
+        b.s[r] = __builtin_bit_cast(
+            u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(wres, voff_s,
+                                                          soff_s + (uint32_t)(r * G + g) * kTileRows * 2, 0));
+      }
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4)
+        b.x[i4] = __builtin_bit_cast(
+            u32x4_t,
+            __builtin_amdgcn_raw_buffer_load_b128(hres, hoff + (uint32_t)(g * kGroup + 32 * i4) * 2u, 0, 0));
+    };
+    auto compute = [&](const Buf& b, int i) {
+      const float w = i < ng ? wt : 0.f;
+      f32x4_t acc[RT], as = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int r = 0; r < RT; ++r) acc[r] = as;
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const bf16x8_t xv = as_bf16x8(b.x[i4]);
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+          acc[r] = mfma16x16x32(as_bf16x8(decode_word_biased(b.c[r][i4], kMask, kOne)), xv, acc[r]);
+        as = mfma16x16x32(ones, xv, as);
+      }
+      const float xs = -24.f * as[0];  // every row of the ones product holds the column's group sum
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        const float s4[4] = {__uint_as_float(b.s[r][0] << 16), __uint_as_float(b.s[r][0] & 0xFFFF0000u),
+                             __uint_as_float(b.s[r][1] << 16), __uint_as_float(b.s[r][1] & 0xFFFF0000u)};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) tot[r][q] = fmaf(w * s4[q], fmaf(16.f, acc[r][q], xs), tot[r][q]);
+      }
+    };
+    Buf buf[D + 1];
+#pragma unroll
+    for (int j = 0; j < D; ++j) load(buf[j], j);
+    // the scheduling barriers keep each group's loads ahead of the multiply that
+    // precedes their use (the scheduler would otherwise sink them to their users)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < UPW; ++i) {
+      if (i + D < UPW) load(buf[(i + D) % (D + 1)], i + D);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(buf[i % (D + 1)], i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // wavefronts' sums in wavefront order; value v = rows * t + n of the
+  // workgroup's partial (token t, stripe row n) is owned by thread v % threads
+#pragma unroll
+  for (int r = 0; r < RT; ++r) s_red[wave][r][lane] = tot[r];
+  __syncthreads();
+  float* pp = part + (int64_t)stripe * kDcMaxChunks * kValues;
+#pragma unroll
+  for (int m = 0; m < kPer; ++m) {
+    const int vi = tid + kThreads * m, t = vi / kRows, n = vi % kRows;
+    const int rt = n >> 4, src = ((n & 15) >> 2) * 16 + t, q = n & 3;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) v += s_red[w][rt][src][q];
+    __hip_atomic_store(pp + chunk * kValues + vi, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's partials have reached device scope
+  __syncthreads();
+  const int n_arrive = max(nch, 1);
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(counters + stripe, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n_arrive - 1;
+  __syncthreads();
+  if (!s_last) return;
+  // every chunk's partial is complete at device scope: add them in chunk order
+#pragma unroll
+  for (int m = 0; m < kPer; ++m) {
+    const int vi = tid + kThreads * m, t = vi / kRows, n = vi % kRows;
+    float pv[kDcMaxChunks];
+#pragma unroll
+    for (int c = 0; c < kDcMaxChunks; ++c)
+      pv[c] = c < n_arrive ? __hip_atomic_load(pp + c * kValues + vi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                           : 0.f;
+    float sum = pv[0];
+#pragma unroll
+    for (int c = 1; c < kDcMaxChunks; ++c)
+      if (c < n_arrive) sum += pv[c];
+    if (t < f.T) out[(int64_t)t * f.d + kRows * stripe + n] = (uint16_t)f32_to_bf16_bits(sum);
   }
 }
 
@@ -725,6 +909,9 @@ __global__ __launch_bounds__(256) void k_ffn_decode(FfnDev f, const uint16_t* __
 constexpr int kGateUpRT = 2, kDownRT = 4;
 constexpr int kPersistRT = 4, kPersistNG = 8, kRingRT = 2, kRingNG = 4;
 constexpr int kDenseRT = 2, kDenseNB = 4;  // LDS-activation gate/up: tiles per stripe, ring depth
+// fused down + combine: tiles per stripe, prefetch distance in units, wavefronts
+// per workgroup and resident wavefronts per SIMD
+constexpr int kDcRT = 2, kDcD = 2, kDcWaves = 8, kDcOcc = 4;
 
 int decode_down_gpw(int I, int ksplit) {
   const int G = I / kGroup;
@@ -763,9 +950,31 @@ static void launch_nb(const FfnDev& f, uint16_t* h, float* y, int ksplit, hipStr
   timing_end(K_DOWN_DECODE, s);
 }
 
-int launch_decode(const FfnDev& f, uint16_t* h, float* y, int ksplit, int nb, hipStream_t s) {
+// K groups per wavefront of the fused down + combine pass: the largest of 16, 8,
+// 4 (not above G rounded up to a power of two) that still gives at least 2048
+// wavefronts, else 4; 0 if the step has too many (expert, slice) items for
+// kDcMaxChunks workgroups per stripe.
+int dc_units_per_wave(int umax, int G, int stripes) {
+  int upw = 4;
+  for (int u = 16; u > 4; u /= 2)
+    if (u / 2 < G && (int64_t)umax * ((G + u - 1) / u) * stripes >= 2048) {
+      upw = u;
+      break;
+    }
+  return (int64_t)umax * ((G + upw - 1) / upw) <= (int64_t)kDcMaxChunks * kDcWaves ? upw : 0;
+}
+
+int launch_decode(const FfnDev& f_in, uint16_t* h, float* y, int ksplit, int nb, hipStream_t s, uint16_t* out,
+                  float* dc_part, int32_t* dc_counters) {
+  FfnDev f = f_in;
   const int64_t umax = f.umax;
   if (f.T <= 16) {
+    const bool fused = out && dc_part && dc_counters;
+    const int dc_stripes = f.d / (kTileRows * kDcRT);
+    if (fused) {
+      f.zero_ctr = dc_counters;
+      f.n_zero_ctr = dc_stripes;
+    }
     // gate/up: activations in LDS when they fit (d <= 4096), else read per group;
     // down: up to 4 tokens a 4-deep ring of group loads over 2-tile stripes (twice
     // the weight streams), more tokens double buffering over 4-tile stripes (more
@@ -800,7 +1009,25 @@ int launch_decode(const FfnDev& f, uint16_t* h, float* y, int ksplit, int nb, hi
     }
     timing_end(K_GATEUP_DECODE, s);
     timing_begin(K_DOWN_DECODE, s);
-    hipLaunchKernelGGL(kdn, dim3((unsigned)grid_dn), dim3(256), 0, s, f, (const uint16_t*)h, (uint16_t*)nullptr, y, ksplit);
+    if (fused) {
+      // K groups per wavefront (checked when the call chose this path)
+      const int upw = dc_units_per_wave(f.umax, f.I / kGroup, dc_stripes);
+      const int64_t slices = ceil_div(f.I / kGroup, upw);
+      const dim3 grid((unsigned)(dc_stripes * ceil_div((int64_t)f.umax * slices, kDcWaves)));
+      const dim3 block(kDcWaves * 64);
+      if (upw <= 4)
+        hipLaunchKernelGGL((k_down_combine<kDcRT, kDcD, 4, kDcWaves, kDcOcc>), grid, block, 0, s, f, h, out, dc_part,
+                           dc_counters);
+      else if (upw <= 8)
+        hipLaunchKernelGGL((k_down_combine<kDcRT, kDcD, 8, kDcWaves, kDcOcc>), grid, block, 0, s, f, h, out, dc_part,
+                           dc_counters);
+      else
+        hipLaunchKernelGGL((k_down_combine<kDcRT, kDcD, 16, kDcWaves, kDcOcc>), grid, block, 0, s, f, h, out, dc_part,
+                           dc_counters);
+    } else {
+      hipLaunchKernelGGL(kdn, dim3((unsigned)grid_dn), dim3(256), 0, s, f, (const uint16_t*)h, (uint16_t*)nullptr, y,
+                         ksplit);
+    }
     timing_end(K_DOWN_DECODE, s);
     return check_launch("grouped expert FFN (decode, T <= 16)");
   }

@@ -31,7 +31,8 @@ HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "gateup_decode_olmoe_t16_hbm_counters.txt")
 COUNTED_SOURCES = ["w4a16_grouped_expert_amd/csrc/ffn_decode.hip", "w4a16_grouped_expert_amd/csrc/ffn_common.hpp",
-                   "w4a16_grouped_expert_amd/csrc/common.hpp"]
+                   "w4a16_grouped_expert_amd/csrc/common.hpp", "w4a16_grouped_expert_amd/csrc/ffn_layer.hip",
+                   "w4a16_grouped_expert_amd/csrc/align_block.hpp"]
 
 
 def parse():
@@ -51,6 +52,8 @@ def parse():
     p.add_argument("--no-ablation", action="store_true", help="skip the fused vs per-expert ablation")
     p.add_argument("--no-bf16", action="store_true", help="skip the BF16-expert comparison")
     p.add_argument("--no-mat", action="store_true", help="skip the nested two/four-bit comparison")
+    p.add_argument("--two-call", action="store_true",
+                   help="decode steps through moe_route_align + moe_w4a16_grouped_ffn instead of moe_decode_layer")
     p.add_argument("--slot-steps", type=int, default=24, help="timed steps of the slot-cache workload")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain device copy of known size (for HBM counter calibration)")
@@ -72,13 +75,16 @@ class Decoder:
     """16 resident MoE layers with shared per-step buffers: four-bit experts, or
     (bf16=True) the same experts unquantised for the W4 versus BF16 comparison."""
 
-    def __init__(self, wl, T_max, device, bf16=False, mat=False):
+    def __init__(self, wl, T_max, device, bf16=False, mat=False, fused=True):
         import torch
         import synth
         import w4a16_grouped_expert_amd as moe
         self.moe, self.torch = moe, torch
         s = wl.shape
         self.wl, self.s, self.bf16, self.mat, self.tau = wl, s, bf16, mat, 0.0
+        # steps of at most 16 tokens on four-bit experts: the whole layer in two
+        # launches (moe_decode_layer); else moe_route_align + the grouped FFN call
+        self.fused = fused and not bf16 and not mat
         self.layers = []
         for l in range(wl.layers):
             w13, w2 = synth.expert_weights(wl, l, device=device)
@@ -101,12 +107,23 @@ class Decoder:
                    for t in range(1, T_max + 1))
         self.ws = torch.empty(need, dtype=torch.uint8, device=device)
         self.out = [torch.empty((T_max, s.d), dtype=torch.bfloat16, device=device) for _ in range(wl.layers)]
+        if self.fused:
+            t_l = min(T_max, 16)
+            self.lws = torch.empty(moe.decode_layer_workspace_bytes(t_l, s.d, s.I, s.E, s.k), dtype=torch.uint8,
+                                   device=device)
+            self.lctr = moe.alloc_layer_counters(device)
+
+    def uses_layer(self, T):
+        return self.fused and T <= 16
 
     def layer(self, l, x):
         moe, s = self.moe, self.s
         T = x.shape[0]
         wr, bank = self.layers[l]
         r = moe.RouteOut(self.route.logits[:T], self.route.ids[:T], self.route.weights[:T])
+        if self.uses_layer(T):
+            moe.moe_decode_layer_into(x, wr, bank, s.I, s.k, r, self.out[l][:T], self.lws, self.lctr)
+            return None
         a = moe.AlignOut(self.align.offsets, self.align.sorted_pairs[:T * s.k], self.align.pair_pos[:T * s.k],
                          self.align.active, None, 0)
         moe.moe_route_align_into(x, wr, s.k, r, a, self.counter)
@@ -126,8 +143,8 @@ class Decoder:
         """Active experts per layer for this step (untimed pre-pass)."""
         us = []
         for l, x in enumerate(xs):
-            a = self.layer(l, x)
-            us.append(int(a.active[0].item()))
+            self.layer(l, x)
+            us.append(int(self.torch.unique(self.route.ids[:x.shape[0]]).numel()))
         return us
 
 
@@ -355,6 +372,8 @@ def run_decode(dec, T, steps, warmup, x_sets, timed_kernels=("gateup_decode", "d
     # dominant kernel: grouped gate/up; algorithmic bytes per launch = distinct experts x
     # (W13 codes + scales) + activations read + h written (bf16)
     gu_bytes = u_mean * b13 + T * s.d * 2 + T * s.k * s.I * 2
+    if dec.uses_layer(T):
+        gu_bytes += router  # the same launch computes the routing
     res["gateup_bytes_per_launch"] = gu_bytes
     return res
 
@@ -650,7 +669,7 @@ def main():
     wl = synth.OLMOE_DECODE
     s = wl.shape
     Ts = sorted({args.tokens} | {int(t) for t in args.sweep.split(",") if t})
-    dec = Decoder(wl, max(Ts), "cuda")
+    dec = Decoder(wl, max(Ts), "cuda", fused=not args.two_call)
     head = run_decode(dec, args.tokens, args.steps, args.warmup, args.x_sets)
     sweep = {}
     for T in Ts:
@@ -664,7 +683,9 @@ def main():
             sweep[f"T={T}"]["gateup_gbps"] = r["gateup_bytes_per_launch"] / (kt * 1e-6) / 1e9
     kern = head["kernels"]["gateup_decode"]
     achieved = head["gateup_bytes_per_launch"] / (kern["avg_us"] * 1e-6) / 1e9
-    roofline = {"bound": "hbm", "kernel": "k_gateup_dense (grouped gate/up)", "achieved": round(achieved, 1),
+    kname = ("k_layer_gateup (routing + grouped gate/up)" if dec.uses_layer(args.tokens)
+             else "k_gateup_dense (grouped gate/up)")
+    roofline = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": measured_traffic(), "avg_us": round(kern["avg_us"], 3),
                 "bytes_per_launch": int(head["gateup_bytes_per_launch"])}

@@ -188,6 +188,50 @@ int64_t moe_ffn_workspace_bytes(int T, int d, int I, int E, int k, int mode);
 int moe_w4a16_grouped_ffn(const moe_ffn_args* args, void* stream);
 
 /*
+ * moe_decode_layer -- one decode step of the whole layer (router, top-k,
+ * grouped gate/up + SwiGLU, grouped down, routing-weighted combine) for at most
+ * 16 tokens, in two launches (ExactMoE, Abstract: the BF16 router with its
+ * unchanged top-k and every selected expert through fused grouped kernels).
+ * Routing overlaps the start of the weight stream; no expert-sorted permutation
+ * is formed (h rows are kept in pair order).  logits, topk_ids and topk_weights
+ * are bit-identical to moe_route_align; out equals moe_w4a16_grouped_ffn
+ * (combine = 1, no slot table) on them bit for bit when that call accumulates
+ * each gate/up item's K range in one wavefront (many active experts), else up
+ * to the fp32 summation order (it splits K over two wavefronts when few experts
+ * are active).
+ *
+ *  x [T][d] bf16, w_router [E][d] bf16 (16-byte aligned); bank: expert blobs
+ *  (layout v1, 256-byte aligned, stride >= blob bytes, multiple of 256, below
+ *  2^31); outputs logits [T][E] fp32, topk_ids [T][k], topk_weights [T][k], out
+ *  [T][d] bf16; workspace of moe_decode_layer_workspace_bytes (256-byte
+ *  aligned).  counters: MOE_DECODE_LAYER_COUNTERS int32 of device memory owned
+ *  by the caller, all zero before the first call; every call leaves them zero,
+ *  except counters[MOE_DECODE_LAYER_COUNTERS - 1], which a call sets to 1 if a
+ *  workgroup gave up waiting for the routing (its results are then invalid).
+ *  Calls sharing a counters buffer must not overlap.
+ *  Limits: 1 <= T <= 16 (T == 0 is a no-op), d <= 4096, d and I multiples of
+ *  128, E <= 1024, k <= min(E, 16); MOE_ERR_UNSUPPORTED_SHAPE otherwise.
+ */
+#define MOE_DECODE_LAYER_COUNTERS 1024
+typedef struct {
+  const uint16_t* x;
+  const uint16_t* w_router;
+  int T, d, I, E, k;
+  int renormalize;
+  const uint8_t* bank;
+  int64_t bank_stride;
+  float* logits;
+  int32_t* topk_ids;
+  float* topk_weights;
+  uint16_t* out;
+  void* workspace;
+  int64_t workspace_bytes;
+  int32_t* counters;
+} moe_decode_layer_args;
+int64_t moe_decode_layer_workspace_bytes(int T, int d, int I, int E, int k);
+int moe_decode_layer(const moe_decode_layer_args* args, void* stream);
+
+/*
  * BF16 experts: the same grouped pass over unquantised experts, the BF16 side of
  * the page's four-bit versus BF16 decode comparison (ExactMoE, Abstract: W4A16
  * experts against the BF16 model).

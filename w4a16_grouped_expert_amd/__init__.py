@@ -10,5 +10,6 @@ from .api import (MODE_AUTO, active_experts, MODE_DECODE, MODE_PREFILL, AlignOut
                   moe_align, moe_align_into, moe_route, moe_route_align_into, moe_route_into, moe_w4a16_grouped_ffn,
                   moe_w4a16_grouped_ffn_into, pack_experts, pack_w4_g128, timing_enable, timing_read,
                   timing_reset, bf16_expert_bytes, pack_bf16_experts, moe_bf16_grouped_ffn, moe_bf16_grouped_ffn_into,
-                  mat_layout, mat_from_w4, moe_mat_grouped_ffn_into)
+                  mat_layout, mat_from_w4, moe_mat_grouped_ffn_into, alloc_layer_counters,
+                  decode_layer_workspace_bytes, moe_decode_layer, moe_decode_layer_into)
 from ._lib import LIB_PATH, MoeError, lib  # noqa: F401

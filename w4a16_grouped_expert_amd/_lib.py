@@ -49,6 +49,15 @@ class FfnArgs(ctypes.Structure):
     ]
 
 
+class LayerArgs(ctypes.Structure):
+    _fields_ = [
+        ("x", c_vp), ("w_router", c_vp), ("T", c_int), ("d", c_int), ("I", c_int), ("E", c_int), ("k", c_int),
+        ("renormalize", c_int), ("bank", c_vp), ("bank_stride", c_i64),
+        ("logits", c_vp), ("topk_ids", c_vp), ("topk_weights", c_vp), ("out", c_vp),
+        ("workspace", c_vp), ("workspace_bytes", c_i64), ("counters", c_vp),
+    ]
+
+
 # name -> (restype, argtypes)
 SIGNATURES = {
     "moe_status_string": (ctypes.c_char_p, [c_int]),
@@ -68,6 +77,8 @@ SIGNATURES = {
     "moe_mat_layout_get": (c_int, [c_int, c_int, ctypes.POINTER(MatLayout)]),
     "moe_mat_from_w4": (c_int, [c_vp, c_i64, c_int, c_int, c_int, c_vp, c_i64, c_vp]),
     "moe_mat_grouped_ffn": (c_int, [ctypes.POINTER(FfnArgs), ctypes.c_float, c_vp]),
+    "moe_decode_layer_workspace_bytes": (c_i64, [c_int, c_int, c_int, c_int, c_int]),
+    "moe_decode_layer": (c_int, [ctypes.POINTER(LayerArgs), c_vp]),
     "moe_slot_cache_create": (c_int, [c_int, c_int, c_i64, c_vp, c_vp, ctypes.POINTER(c_vp)]),
     "moe_slot_cache_destroy": (c_int, [c_vp]),
     "slot_cache_load": (c_int, [c_vp, c_u64p, c_u64p, c_vp, c_i32p, c_i32p, c_vp, c_vp, c_vp]),

@@ -213,6 +213,61 @@ def moe_w4a16_grouped_ffn_into(x, route: RouteOut, al: AlignOut, bank: torch.Ten
     return out
 
 
+# ---------------------------------------------------------------- whole decode layer
+
+DECODE_LAYER_COUNTERS = 1024  # MOE_DECODE_LAYER_COUNTERS in w4a16_moe.h
+
+
+def alloc_layer_counters(device) -> torch.Tensor:
+    """Zeroed device counters for moe_decode_layer (each call leaves them zero,
+    the last one excepted: a timeout flag)."""
+    return torch.zeros(DECODE_LAYER_COUNTERS, dtype=torch.int32, device=device)
+
+
+def decode_layer_workspace_bytes(T, d, I, E, k) -> int:
+    return int(lib().moe_decode_layer_workspace_bytes(T, d, I, E, k))
+
+
+def moe_decode_layer_into(x, w_router, bank: torch.Tensor, I: int, k: int, route: RouteOut, out: torch.Tensor,
+                          workspace: torch.Tensor, counters: torch.Tensor, renormalize=True,
+                          bank_stride: Optional[int] = None, stream=None):
+    """Router, top-k, grouped gate/up, down and combine of one decode step (T <= 16)
+    in two launches; outputs bit-identical to moe_route_align + moe_w4a16_grouped_ffn."""
+    _need(x, torch.bfloat16, "x")
+    _need(w_router, torch.bfloat16, "w_router")
+    _need(bank, torch.uint8, "bank")
+    _need(out, torch.bfloat16, "out")
+    _need(workspace, torch.uint8, "workspace")
+    _need(counters, torch.int32, "counters")
+    if counters.numel() < DECODE_LAYER_COUNTERS:
+        raise ValueError(f"moe_decode_layer needs {DECODE_LAYER_COUNTERS} counters, got {counters.numel()}")
+    T, d = x.shape
+    E = w_router.shape[0]
+    a = _lib.LayerArgs()
+    a.x, a.w_router, a.T, a.d, a.I, a.E, a.k = x.data_ptr(), w_router.data_ptr(), T, d, I, E, k
+    a.renormalize = int(bool(renormalize))
+    a.bank = bank.data_ptr()
+    a.bank_stride = bank.stride(0) if bank_stride is None else bank_stride
+    a.logits, a.topk_ids, a.topk_weights = route.logits.data_ptr(), route.ids.data_ptr(), route.weights.data_ptr()
+    a.out = out.data_ptr()
+    a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
+    a.counters = counters.data_ptr()
+    check("moe_decode_layer", lib().moe_decode_layer(ctypes.byref(a), _stream(stream)))
+    return out
+
+
+def moe_decode_layer(x, w_router, bank: torch.Tensor, I: int, k: int, renormalize=True, stream=None):
+    """Allocating convenience form of moe_decode_layer_into: returns (out, route)."""
+    T, d = x.shape
+    E = w_router.shape[0]
+    route = alloc_route(T, E, k, x.device)
+    out = torch.empty((T, d), dtype=torch.bfloat16, device=x.device)
+    ws = torch.empty(max(decode_layer_workspace_bytes(T, d, I, E, k), 256), dtype=torch.uint8, device=x.device)
+    ctr = alloc_layer_counters(x.device)
+    moe_decode_layer_into(x, w_router, bank, I, k, route, out, ws, ctr, renormalize, stream=stream)
+    return out, route
+
+
 def bf16_expert_bytes(d: int, I: int) -> int:
     return int(lib().moe_bf16_expert_bytes(d, I))
 

@@ -208,4 +208,34 @@ __device__ __forceinline__ void align_block(const int32_t* __restrict__ ids, int
   }
 }
 
+// Active experts of the step in ascending id order, from the routing table in
+// LDS (s_ids[t][j], -1 = none): a bit mask (s_mask), then one wavefront
+// compacts it into s_act (skipped when s_act is null).  Returns U; every
+// workgroup builds the same list.
+__device__ inline int build_active(const int (*s_ids)[MOE_MAX_TOPK], int T, int k, int E, uint32_t* s_mask, int* s_act,
+                            int* s_u) {
+  const int tid = threadIdx.x, n = blockDim.x;
+  for (int i = tid; i < MOE_MAX_EXPERTS / 32; i += n) s_mask[i] = 0u;
+  __syncthreads();
+  for (int i = tid; i < T * k; i += n) {
+    const int id = s_ids[i / k][i % k];
+    if (id >= 0 && id < E) atomicOr(&s_mask[id >> 5], 1u << (id & 31));
+  }
+  __syncthreads();
+  if (tid < 64) {
+    uint32_t m = tid < MOE_MAX_EXPERTS / 32 ? s_mask[tid] : 0u;
+    const int c = __popc(m);
+    const int incl = wave_incl_scan(c);
+    int pos = incl - c;
+    while (s_act && m) {
+      const int b = __ffs(m) - 1;
+      s_act[pos++] = tid * 32 + b;
+      m &= m - 1u;
+    }
+    if (tid == 63) *s_u = incl;
+  }
+  __syncthreads();
+  return *s_u;
+}
+
 }  // namespace moe

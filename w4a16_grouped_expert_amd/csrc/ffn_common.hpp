@@ -60,6 +60,11 @@ int launch_combine(const FfnDev& f, const float* y, int ksplit, const float* wei
 // performs the routing-weighted combine into out, and y is not written.
 int launch_decode(const FfnDev& f, uint16_t* h, float* y, int ksplit, int nb, hipStream_t s,
                   uint16_t* out = nullptr, float* dc_part = nullptr, int32_t* dc_counters = nullptr);
+// The fused down + combine pass alone (see launch_decode); pair: h rows in pair
+// order and the active experts built from the routing table (the n_route_ctr
+// counters at route_ctr zeroed).
+void launch_down_combine(const FfnDev& f, const uint16_t* h, uint16_t* out, float* part, int32_t* counters,
+                         int32_t* route_ctr, int n_route_ctr, hipStream_t s, bool pair);
 // Units per wavefront of the fused down + combine pass, 0 if the step is too large for it.
 int dc_units_per_wave(int umax, int G, int stripes);
 int launch_prefill(const FfnDev& f, uint16_t* h, float* y, float* xsum, float* hsum, hipStream_t s);

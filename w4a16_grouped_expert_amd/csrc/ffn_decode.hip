@@ -22,6 +22,7 @@
 // per wavefront in flight) before decoding, then the partial sums meet in LDS in
 // a fixed order.  Down may further split K over blocks (partials summed in a
 // fixed order by the combine kernel).
+#include "align_block.hpp"
 #include "ffn_common.hpp"
 
 namespace moe {
@@ -381,6 +382,164 @@ __global__ __launch_bounds__(512, 4) void k_gateup_dense(FfnDev f, uint16_t* __r
   }
 }
 
+// The same gate/up pass with each item's groups in straight-line chunks of CH:
+// within a chunk the loads of group i + D go out before group i is multiplied,
+// fully unrolled with scheduling barriers, so every wait is exact and no
+// register that a load in flight will write is ever moved; the weight pointers
+// are wave-uniform buffer resources.  Groups past G (G not a multiple of CH)
+// repeat group G - 1's loads with weight 0.
+template <int RT, int D, int CH, int MAXG>
+__global__ __launch_bounds__(512, 4) void k_gateup_line(FfnDev f, uint16_t* __restrict__ hout) {
+  zero_down_counters(f);
+  constexpr int kWaves = 8;
+  const int G = f.d / kGroup;
+  const int n_stripes = 2 * f.I / (kTileRows * RT);
+  const int n_items = f.umax * n_stripes;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = lane_id();
+  const int col = lane & 15, kq = lane >> 4;
+  const int worker = blockIdx.x * kWaves + wave, n_workers = gridDim.x * kWaves;
+  const i32x4_t* work = reinterpret_cast<const i32x4_t*>(f.active + 4);
+  const int U = f.active[0];
+
+  struct Buf {
+    u32x4_t c[RT];
+    u32x2_t s[RT];
+  };
+  Buf buf[D + 1];
+  __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc((void*)f.bank, (short)0, 0, kBufferRsrcWord3);
+  uint32_t soff_c = 0, soff_s = 0;
+  const uint32_t voff_c = 16u * lane, voff_s = 8u * kq;
+  auto load = [&](Buf& b, int g) {
+    const int gl = min(g, G - 1);
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      b.c[r] = __builtin_bit_cast(
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wres, voff_c, soff_c + (uint32_t)(r * G + gl) * kTileBytes,
+                                                         kCacheNonTemporal));
+      b.s[r] = __builtin_bit_cast(
+          u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(wres, voff_s, soff_s + (uint32_t)(r * G + gl) * kTileRows * 2,
+                                                        0));
+    }
+  };
+  // Item setup: its record, its weight resource and the loads of its first D
+  // groups.  Returns the expert (-1: no item left for this worker).
+  int item = worker, row0 = 0;
+  i32x4_t w4 = work[min(item / n_stripes, f.umax - 1)];
+  auto start_item = [&]() -> int {
+    for (; item < n_items; item += n_workers) {
+      const i32x4_t cur = w4;
+      w4 = work[min((item + n_workers) / n_stripes, f.umax - 1)];  // next record, in flight now
+      if (item / n_stripes >= U) break;  // items are visited in increasing u: nothing active remains
+      const uint8_t* blob = f.blob(cur[0]);
+      if (!blob) continue;
+      const int stripe = item % n_stripes;
+      wres = __builtin_amdgcn_make_buffer_rsrc((void*)blob, (short)0, 0x7FFFFFFF, kBufferRsrcWord3);
+      soff_c = (uint32_t)(f.off_w13_codes + (int64_t)(RT * stripe) * G * kTileBytes);
+      soff_s = (uint32_t)(f.off_w13_scales + (int64_t)(RT * stripe) * G * kTileRows * 2);
+#pragma unroll
+      for (int j = 0; j < D; ++j) load(buf[j], j);
+      row0 = cur[1];
+      return cur[0];
+    }
+    item = n_items;
+    return -1;
+  };
+  int e = start_item();
+
+  __shared__ u32x4_t s_x[MAXG * 4 * 64];
+  __shared__ float s_xs[MAXG * 16];
+  __shared__ int s_ids[16][MOE_MAX_TOPK];
+  {
+    const u32x4_t ones_w = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    const bf16x8_t ones = as_bf16x8(ones_w);
+    const __amdgpu_buffer_rsrc_t xres =
+        __builtin_amdgcn_make_buffer_rsrc((void*)f.x, (short)0, (int)(f.T * f.d * 2), kBufferRsrcWord3);
+    const uint32_t xoff = (uint32_t)(col * f.d + 8 * kq) * 2u;
+    for (int g = wave; g < G; g += kWaves) {
+      u32x4_t xv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        xv[i] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xres, xoff + (uint32_t)(g * kGroup + 32 * i) * 2u, 0, 0));
+      f32x4_t as = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s_x[(4 * g + i) * 64 + lane] = xv[i];
+        as = mfma16x16x32(ones, as_bf16x8(xv[i]), as);
+      }
+      if (lane < 16) s_xs[g * 16 + lane] = as[0];  // C column = lane, every row the same sum
+    }
+    for (int i = threadIdx.x; i < 16 * MOE_MAX_TOPK; i += kWaves * 64) {
+      const int t = i / MOE_MAX_TOPK, j = i % MOE_MAX_TOPK;
+      s_ids[t][j] = (j < f.k && t < f.T) ? f.topk_ids[t * f.k + j] : -1;
+    }
+  }
+  __syncthreads();
+  const uint32_t kMask = vgpr_const(0x00780078u), kOne = vgpr_const(0x3F803F80u);
+
+  while (e >= 0) {
+    const int cur_stripe = item % n_stripes;
+    bool routed = false;
+    for (int j = 0; j < f.k; ++j) routed |= (s_ids[col][j] == e);
+    const uint32_t colmask = (uint32_t)__ballot(routed) & 0xFFFFu;
+    const int out_row = row0 + __popc(colmask & ((1u << col) - 1u));
+
+    f32x4_t tot[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) tot[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](const Buf& b, int g) {
+      const int gl = min(g, G - 1);
+      const float gv = g < G ? 1.f : 0.f;
+      const float xs = -24.f * s_xs[gl * 16 + col];
+      f32x4_t acc[RT];
+#pragma unroll
+      for (int r = 0; r < RT; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x8_t xv = as_bf16x8(s_x[(4 * gl + i) * 64 + lane]);
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+          acc[r] = mfma16x16x32(as_bf16x8(decode_word_biased(b.c[r][i], kMask, kOne)), xv, acc[r]);
+      }
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        const float s4[4] = {__uint_as_float(b.s[r][0] << 16), __uint_as_float(b.s[r][0] & 0xFFFF0000u),
+                             __uint_as_float(b.s[r][1] << 16), __uint_as_float(b.s[r][1] & 0xFFFF0000u)};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) tot[r][q] = fmaf(gv * s4[q], fmaf(16.f, acc[r][q], xs), tot[r][q]);
+      }
+    };
+    for (int gc = 0; gc < G; gc += CH) {
+      if (gc > 0) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) load(buf[j], gc + j);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        if (i + D < CH) load(buf[(i + D) % (D + 1)], gc + i + D);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(buf[i % (D + 1)], gc + i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // the next item's first loads go out before this item's stores
+    item += n_workers;
+    e = start_item();
+#pragma unroll
+    for (int p = 0; p < RT / 2; ++p) {
+      uint32_t hv[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) hv[q] = f32_to_bf16_bits(silu_f32(tot[2 * p][q]) * tot[2 * p + 1][q]);
+      if (routed) {
+        const int hcol = kTileRows * ((RT / 2) * cur_stripe + p) + 4 * kq;
+        u32x2_t o = {hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16)};
+        *reinterpret_cast<u32x2_t*>(hout + (int64_t)out_row * f.I + hcol) = o;
+      }
+    }
+  }
+}
+
 // The same gate/up pass with each stripe's K range split over a pair of
 // wavefronts of the workgroup, for steps with few active experts (few stripes):
 // twice the wavefronts stream weights.  Wavefront w works on stripe slot w % 4 of
@@ -569,11 +728,16 @@ __global__ __launch_bounds__(512, 4) void k_gateup_dense_ks2(FfnDev f, uint16_t*
 // before this one on the stream.
 constexpr int kDcMaxChunks = 32;
 
-template <int RT, int D, int UPW, int WAVES, int OCC>
+// PAIR: h rows in pair order (t * k + j) and the active experts built from the
+// routing table in each workgroup (the fused decode layer); else h rows in
+// expert-sorted order with the active list of moe_align.  route_ctr (PAIR): the
+// n_route_ctr counters of the routing pass, zeroed here for the next step.
+template <int RT, int D, int UPW, int WAVES, int OCC, bool PAIR>
 __global__ __launch_bounds__(WAVES * 64, OCC) void k_down_combine(FfnDev f, const uint16_t* __restrict__ h,
                                                                   uint16_t* __restrict__ out,
                                                                   float* __restrict__ part,
-                                                                  int32_t* __restrict__ counters) {
+                                                                  int32_t* __restrict__ counters,
+                                                                  int32_t* __restrict__ route_ctr, int n_route_ctr) {
   constexpr int kRows = RT * kTileRows, kValues = 16 * kRows;  // 16 tokens x the stripe's rows
   constexpr int kThreads = WAVES * 64, kPer = kValues / kThreads;
   static_assert(kValues % kThreads == 0, "whole partial values per thread");
@@ -586,18 +750,29 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_down_combine(FfnDev f, cons
   const int item = chunk * WAVES + wave;
   // the active count, the wavefront's work record (read within the work list's
   // capacity, used only if the item exists) and the routing table: one round trip
-  const int U = f.active[0];
-  const i32x4_t rec = reinterpret_cast<const i32x4_t*>(f.active + 4)[min(item / n_slices, f.umax - 1)];
+  int U = PAIR ? 0 : f.active[0];
+  i32x4_t rec = PAIR ? i32x4_t{0, 0, 0, 0}
+                     : reinterpret_cast<const i32x4_t*>(f.active + 4)[min(item / n_slices, f.umax - 1)];
 
   __shared__ int s_ids[16][MOE_MAX_TOPK];
   __shared__ float s_w[16][MOE_MAX_TOPK];
   __shared__ f32x4_t s_red[WAVES][RT][64];
   __shared__ int s_last;
+  __shared__ uint32_t s_mask[PAIR ? MOE_MAX_EXPERTS / 32 : 1];
+  __shared__ int s_act[PAIR ? 16 * MOE_MAX_TOPK : 1];
+  __shared__ int s_u;
   for (int i = tid; i < 16 * MOE_MAX_TOPK; i += kThreads) {
     const int t = i / MOE_MAX_TOPK, j = i % MOE_MAX_TOPK;
     const bool in = j < f.k && t < f.T;
     s_ids[t][j] = in ? f.topk_ids[t * f.k + j] : -1;
     s_w[t][j] = in ? f.topk_weights[t * f.k + j] : 0.f;
+  }
+  if (PAIR) {
+    if (blockIdx.x == 0)
+      for (int i = tid; i < n_route_ctr; i += kThreads) route_ctr[i] = 0;
+    __syncthreads();
+    U = build_active(s_ids, f.T, f.k, f.E, s_mask, s_act, &s_u);
+    rec[0] = s_act[min(item / n_slices, max(U - 1, 0))];
   }
   const int n_items = U * n_slices;
   const int nch = (n_items + WAVES - 1) / WAVES;          // chunks with work on every stripe
@@ -622,7 +797,7 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_down_combine(FfnDev f, cons
     int hit = -1;
     for (int j = 0; j < f.k; ++j) hit = s_ids[col][j] == e ? j : hit;
     const uint32_t colmask = (uint32_t)__ballot(hit >= 0) & 0xFFFFu;
-    const int hrow = rec[1] + __popc(colmask & ((1u << col) - 1u));
+    const int hrow = PAIR ? col * f.k + hit : rec[1] + __popc(colmask & ((1u << col) - 1u));
     const uint32_t hoff = hit >= 0 ? (uint32_t)(hrow * f.I + 8 * kq) * 2u : 0x7F000000u;  // else reads zeros
     const float wt = hit >= 0 ? s_w[col][hit] : 0.f;
     const uint32_t voff_c = 16u * lane, voff_s = 8u * kq;
@@ -712,6 +887,7 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_down_combine(FfnDev f, cons
     s_last = __hip_atomic_fetch_add(counters + stripe, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n_arrive - 1;
   __syncthreads();
   if (!s_last) return;
+  if (tid == 0) counters[stripe] = 0;  // left at zero for the next call
   // every chunk's partial is complete at device scope: add them in chunk order
 #pragma unroll
   for (int m = 0; m < kPer; ++m) {
@@ -909,6 +1085,7 @@ __global__ __launch_bounds__(256) void k_ffn_decode(FfnDev f, const uint16_t* __
 constexpr int kGateUpRT = 2, kDownRT = 4;
 constexpr int kPersistRT = 4, kPersistNG = 8, kRingRT = 2, kRingNG = 4;
 constexpr int kDenseRT = 2, kDenseNB = 4;  // LDS-activation gate/up: tiles per stripe, ring depth
+constexpr int kLineD = 3;                   // straight-line gate/up: groups in flight ahead
 // fused down + combine: tiles per stripe, prefetch distance in units, wavefronts
 // per workgroup and resident wavefronts per SIMD
 constexpr int kDcRT = 2, kDcD = 2, kDcWaves = 8, kDcOcc = 4;
@@ -922,7 +1099,7 @@ int decode_down_gpw(int I, int ksplit) {
 // Resident blocks per CU for a kernel, times the CU count (cached per slot).
 template <typename Kern>
 static int persistent_grid(Kern kern, int slot, int threads = 256) {
-  static int cached[8] = {0};
+  static int cached[16] = {0};
   if (!cached[slot]) {
     int dev = 0, cus = 0, per_cu = 0;
     (void)hipGetDevice(&dev);
@@ -964,6 +1141,33 @@ int dc_units_per_wave(int umax, int G, int stripes) {
   return (int64_t)umax * ((G + upw - 1) / upw) <= (int64_t)kDcMaxChunks * kDcWaves ? upw : 0;
 }
 
+template <int UPW>
+static void launch_dc(const FfnDev& f, const uint16_t* h, uint16_t* out, float* part, int32_t* counters,
+                      int32_t* route_ctr, int n_route_ctr, hipStream_t s, bool pair, dim3 grid) {
+  const dim3 block(kDcWaves * 64);
+  if (pair)
+    hipLaunchKernelGGL((k_down_combine<kDcRT, kDcD, UPW, kDcWaves, kDcOcc, true>), grid, block, 0, s, f, h, out, part,
+                       counters, route_ctr, n_route_ctr);
+  else
+    hipLaunchKernelGGL((k_down_combine<kDcRT, kDcD, UPW, kDcWaves, kDcOcc, false>), grid, block, 0, s, f, h, out, part,
+                       counters, route_ctr, n_route_ctr);
+}
+
+void launch_down_combine(const FfnDev& f, const uint16_t* h, uint16_t* out, float* part, int32_t* counters,
+                         int32_t* route_ctr, int n_route_ctr, hipStream_t s, bool pair) {
+  // K groups per wavefront (checked when the call chose this path)
+  const int stripes = f.d / (kTileRows * kDcRT);
+  const int upw = dc_units_per_wave(f.umax, f.I / kGroup, stripes);
+  const int64_t slices = ceil_div(f.I / kGroup, upw);
+  const dim3 grid((unsigned)(stripes * ceil_div((int64_t)f.umax * slices, kDcWaves)));
+  if (upw <= 4)
+    launch_dc<4>(f, h, out, part, counters, route_ctr, n_route_ctr, s, pair, grid);
+  else if (upw <= 8)
+    launch_dc<8>(f, h, out, part, counters, route_ctr, n_route_ctr, s, pair, grid);
+  else
+    launch_dc<16>(f, h, out, part, counters, route_ctr, n_route_ctr, s, pair, grid);
+}
+
 int launch_decode(const FfnDev& f_in, uint16_t* h, float* y, int ksplit, int nb, hipStream_t s, uint16_t* out,
                   float* dc_part, int32_t* dc_counters) {
   FfnDev f = f_in;
@@ -996,6 +1200,14 @@ int launch_decode(const FfnDev& f_in, uint16_t* h, float* y, int ksplit, int nb,
         auto kks = G <= 16 ? k_gateup_dense_ks2<kDenseRT, kDenseNB, 16> : k_gateup_dense_ks2<kDenseRT, kDenseNB, 32>;
         const int64_t grid_ks = std::min<int64_t>(persistent_grid(kks, G <= 16 ? 6 : 7, 512), ceil_div(items_gu, 4));
         hipLaunchKernelGGL(kks, dim3((unsigned)grid_ks), dim3(512), 0, s, f, h);
+      } else if (f.bank_stride < ((int64_t)1 << 31)) {
+        // straight-line group chunks of 16 (8, 4 for smaller d)
+        auto kln = G > 8 ? (G <= 16 ? k_gateup_line<kDenseRT, kLineD, 16, 16> : k_gateup_line<kDenseRT, kLineD, 16, 32>)
+                         : (G > 4 ? k_gateup_line<kDenseRT, kLineD, 8, 16> : k_gateup_line<kDenseRT, kLineD, 4, 16>);
+        const int slot = G > 16 ? 8 : (G > 8 ? 9 : (G > 4 ? 10 : 11));
+        const int64_t cap_ln = persistent_grid(kln, slot, 512);
+        hipLaunchKernelGGL(kln, dim3((unsigned)std::min<int64_t>(cap_ln, ceil_div(items_gu, 8))), dim3(512), 0, s, f,
+                           h);
       } else {
         hipLaunchKernelGGL(kgu, dim3((unsigned)std::min<int64_t>(cap, ceil_div(items_gu, 8))), dim3(512), 0, s, f, h);
       }
@@ -1010,20 +1222,7 @@ int launch_decode(const FfnDev& f_in, uint16_t* h, float* y, int ksplit, int nb,
     timing_end(K_GATEUP_DECODE, s);
     timing_begin(K_DOWN_DECODE, s);
     if (fused) {
-      // K groups per wavefront (checked when the call chose this path)
-      const int upw = dc_units_per_wave(f.umax, f.I / kGroup, dc_stripes);
-      const int64_t slices = ceil_div(f.I / kGroup, upw);
-      const dim3 grid((unsigned)(dc_stripes * ceil_div((int64_t)f.umax * slices, kDcWaves)));
-      const dim3 block(kDcWaves * 64);
-      if (upw <= 4)
-        hipLaunchKernelGGL((k_down_combine<kDcRT, kDcD, 4, kDcWaves, kDcOcc>), grid, block, 0, s, f, h, out, dc_part,
-                           dc_counters);
-      else if (upw <= 8)
-        hipLaunchKernelGGL((k_down_combine<kDcRT, kDcD, 8, kDcWaves, kDcOcc>), grid, block, 0, s, f, h, out, dc_part,
-                           dc_counters);
-      else
-        hipLaunchKernelGGL((k_down_combine<kDcRT, kDcD, 16, kDcWaves, kDcOcc>), grid, block, 0, s, f, h, out, dc_part,
-                           dc_counters);
+      launch_down_combine(f, h, out, dc_part, dc_counters, nullptr, 0, s, false);
     } else {
       hipLaunchKernelGGL(kdn, dim3((unsigned)grid_dn), dim3(256), 0, s, f, (const uint16_t*)h, (uint16_t*)nullptr, y,
                          ksplit);

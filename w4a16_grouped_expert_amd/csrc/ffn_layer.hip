@@ -1,0 +1,520 @@
+// moe_decode_layer: a whole decode step of the W4A16 MoE layer (at most 16
+// tokens) in two launches: routing + grouped gate/up + SwiGLU, then the grouped
+// down projection with the routing-weighted combine (ExactMoE, page "Every
+// Expert Counts: ExactMoE for Memory-Efficient W4A16 Inference", Abstract: the
+// BF16 router and its unchanged top-k, every selected expert through fused
+// grouped kernels on four-bit weights).
+//
+// The first launch is persistent (every workgroup resident).  Each wavefront
+// first issues the weight loads of its first gate/up item when that item is
+// known without the routing (every expert in order, used when the step routes
+// at least as many pairs as there are experts, so that few are idle); the
+// workgroups with the lowest indices then compute the router logits, one
+// (token, expert) dot product per wavefront, with the arithmetic of moe_route
+// (float64 sums of the exact bf16 products, rounded once); the wavefront that
+// completes a token's logits selects its top-k and weights and publishes the
+// ids in a ready table, and the workgroups stage their activations in LDS, then
+// wait (a bounded poll of the ready table) until every pair is routed.  The gate/up items then run as in
+// the grouped decode pass, h going to rows in pair order (t * k + j): no
+// expert-sorted permutation is needed when every MFMA column is a token.  The
+// second launch is the fused down + combine pass, which builds the active
+// expert list from the routing table itself.  Routing results are bit-identical
+// to moe_route_align; the arithmetic of every gate/up item and of the down pass
+// is that of moe_w4a16_grouped_ffn's decode kernels with one wavefront per item.
+#include "align_block.hpp"
+#include "ffn_common.hpp"
+#include "route_rank.hpp"
+
+namespace moe {
+
+// counters (MOE_DECODE_LAYER_COUNTERS int32, zero between calls); the counters
+// that many workgroups update or poll sit on 128-byte lines of their own
+constexpr int kLine = 32;                         // int32 per 128-byte line
+constexpr int kCtrLogits = kLine;                 // [kLine * (1 + t)]: logits of token t written
+constexpr int kCtrReady = kLine * 17;             // [t * k + j]: expert id + 1 once token t is routed
+constexpr int kCtrRouteEnd = kCtrReady + 16 * MOE_MAX_TOPK;  // routing counters: [0, kCtrRouteEnd)
+constexpr int kCtrDown = kCtrRouteEnd;            // fused down + combine stripe counters (d / 32 <= 128)
+constexpr int kCtrError = MOE_DECODE_LAYER_COUNTERS - 1;
+static_assert(kCtrDown + 128 <= kCtrError, "counter block too small");
+constexpr int kSpinLimit = 1 << 22;
+
+struct RouteDev {
+  const uint16_t* wr;
+  int renormalize;
+  float* logits;
+  int32_t* ids;
+  float* weights;
+  int32_t* ctr;
+};
+
+// Top-k and weights of token t by one wavefront, from its E logits (read with
+// device-coherent loads), in the order and with the sums of moe_route: for E up
+// to kRankMaxE every logit's rank (the logits it loses to, by value desc, index
+// asc) is counted against the row in the wavefront's LDS area, and the k best
+// land at their rank; beyond that, k rounds of a wave-wide argmax.  The ids also
+// go, plus one, to the ready table with device-coherent stores: a non-zero
+// entry is a routed pair.
+constexpr int kRankMaxE = 128;
+
+__device__ void route_token(const RouteDev& r, int t, int E, int k, float* s_lg, float* s_sel_v, int* s_sel_i) {
+  const int lane = lane_id();
+  const int nper = (E + 63) / 64;  // <= 16
+  const float* lg = r.logits + (int64_t)t * E;
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = (i < nper && e < E) ? __hip_atomic_load(lg + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : -INFINITY;
+  }
+  float sel_v = 0.f, lmax = 0.f;  // lane j < k: selection j
+  int sel_i = 0;
+  if (E <= kRankMaxE) {
+#pragma unroll
+    for (int i = 0; i < kRankMaxE / 64; ++i)
+      if (lane + 64 * i < E) s_lg[lane + 64 * i] = v[i];
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < kRankMaxE / 64; ++i) {
+      const int e = lane + 64 * i;
+      if (e < E) {
+        const int rank = rank_in_row(s_lg, E, v[i], e);
+        if (rank < k) {
+          s_sel_v[rank] = v[i];
+          s_sel_i[rank] = e;
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    lmax = s_sel_v[0];
+    if (lane < k) {
+      sel_v = s_sel_v[lane];
+      sel_i = s_sel_i[lane];
+    }
+  } else {
+    uint32_t taken = 0;
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+      if (j >= k) break;
+      float bv = -INFINITY;
+      int bi = 0x7FFFFFFF;  // sentinel below every candidate
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int e = lane + 64 * i;
+        if (i < nper && e < E && !((taken >> i) & 1u) && better(v[i], e, bv, bi)) {
+          bv = v[i];
+          bi = e;
+        }
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(bv, off);
+        const int oi = __shfl_xor(bi, off);
+        if (better(ov, oi, bv, bi)) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+      if (j == 0) lmax = bv;
+      if (lane == j) {
+        sel_v = bv;
+        sel_i = bi;
+      }
+    }
+  }
+  const float ex = lane < k ? expf(sel_v - lmax) : 0.f;
+  float den = 0.f;
+  if (r.renormalize) {
+    for (int j = 0; j < k; ++j) den += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
+  } else {
+    float part = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (i < nper && lane + 64 * i < E) part += expf(v[i] - lmax);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+    den = part;
+  }
+  if (lane < k) {
+    r.ids[(int64_t)t * k + lane] = sel_i;
+    r.weights[(int64_t)t * k + lane] = ex / den;
+    __hip_atomic_store(r.ctr + kCtrReady + t * k + lane, sel_i + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Routing + grouped gate/up + SwiGLU.  SPEC: items are (expert, stripe) over
+// every expert in id order, the first one prefetched before the routing is
+// known (an item of an expert without pairs is skipped); else over the active
+// experts, known after the routing.
+template <int RT, int NB, int MAXG, bool SPEC>
+__global__ __launch_bounds__(512, 4) void k_layer_gateup(FfnDev f, RouteDev r, uint16_t* __restrict__ hout) {
+  constexpr int kWaves = 8;
+  zero_down_counters(f);
+  const int G = f.d / kGroup;
+  const int T = f.T, E = f.E, k = f.k;
+  const int n_stripes = 2 * f.I / (kTileRows * RT);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = lane_id();
+  const int col = lane & 15, kq = lane >> 4;
+  const int worker = blockIdx.x * kWaves + wave, n_workers = gridDim.x * kWaves;
+  const int64_t tile_stride_c = (int64_t)G * kTileBytes;
+  const int64_t tile_stride_s = (int64_t)G * kTileRows;
+
+  struct Buf {
+    u32x4_t c[RT];
+    u32x2_t s[RT];
+  };
+  Buf buf[NB];
+  const uint8_t* codes = nullptr;
+  const uint16_t* scales = nullptr;
+  // past the item's last group the loads repeat group G - 1 and the group's
+  // weight is 0, so no load sits under a branch and the wait counts stay exact
+  auto load = [&](Buf& b, int g) {
+    const int gl = min(g, G - 1);
+#pragma unroll
+    for (int rr = 0; rr < RT; ++rr) {
+      b.c[rr] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4_t*>(codes + rr * tile_stride_c + (int64_t)gl * kTileBytes));
+      b.s[rr] = *reinterpret_cast<const u32x2_t*>(scales + rr * tile_stride_s + gl * kTileRows);
+    }
+  };
+  auto set_item = [&](int e, int stripe) {
+    const uint8_t* blob = f.bank + (int64_t)e * f.bank_stride;
+    codes = blob + f.off_w13_codes + (int64_t)(RT * stripe) * G * kTileBytes + 16 * lane;
+    scales = reinterpret_cast<const uint16_t*>(blob + f.off_w13_scales) + (int64_t)(RT * stripe) * G * kTileRows +
+             4 * kq;
+  };
+
+  // 1. the first item's weights, when it does not depend on the routing (the
+  //    wavefronts that compute logits issue them after their router loads)
+  int item = worker;
+  const bool prefetched = SPEC && item < E * n_stripes;
+  const int n_tasks = T * E;
+  const int n_logit = min(n_workers, n_tasks);
+  auto prefetch = [&]() {
+    if (prefetched) {
+      set_item(item / n_stripes, item % n_stripes);
+#pragma unroll
+      for (int j = 0; j < NB - 1; ++j) load(buf[j], j);
+    }
+  };
+
+  // 2. router logits, one (token, expert) per wavefront of the lowest workgroups
+  __shared__ float s_lg[kWaves][kRankMaxE];
+  __shared__ float s_sel_v[kWaves][MOE_MAX_TOPK];
+  __shared__ int s_sel_i[kWaves][MOE_MAX_TOPK];
+  if (worker >= n_logit) {
+    prefetch();
+  } else {
+    const int nch = f.d / 8;
+    for (int task = worker; task < n_tasks; task += n_logit) {
+      const int t = task / E, e = task % E;
+      const uint16_t* xr = f.x + (int64_t)t * f.d;
+      const uint16_t* wrow = r.wr + (int64_t)e * f.d;
+      double acc = 0.0;
+      constexpr int kB = 4;  // chunks per lane in flight (the sum order does not depend on it)
+      for (int c0 = 0; c0 < nch; c0 += 64 * kB) {
+        u32x4_t xq[kB], wq[kB];
+#pragma unroll
+        for (int c = 0; c < kB; ++c) {
+          const int ch = c0 + lane + 64 * c;
+          xq[c] = ch < nch ? *reinterpret_cast<const u32x4_t*>(xr + 8 * ch) : u32x4_t{0u, 0u, 0u, 0u};
+          wq[c] = ch < nch ? *reinterpret_cast<const u32x4_t*>(wrow + 8 * ch) : u32x4_t{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int c = 0; c < kB; ++c)
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            acc = fma((double)bf16_bits_to_f32(xq[c][m] & 0xFFFFu), (double)bf16_bits_to_f32(wq[c][m] & 0xFFFFu),
+                      acc);
+            acc = fma((double)bf16_bits_to_f32(xq[c][m] >> 16), (double)bf16_bits_to_f32(wq[c][m] >> 16), acc);
+          }
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+      if (lane == 0)
+        __hip_atomic_store(r.logits + (int64_t)t * E + e, (float)acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the logit has reached device scope
+      int last = 0;
+      if (lane == 0)
+        last = __hip_atomic_fetch_add(r.ctr + kCtrLogits + kLine * t, 1, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT) == E - 1;
+      if (__builtin_amdgcn_readfirstlane(last)) route_token(r, t, E, k, s_lg[wave], s_sel_v[wave], s_sel_i[wave]);
+    }
+    prefetch();
+  }
+
+  // 3. activations in LDS (as the grouped gate/up pass), while the routing completes
+  __shared__ u32x4_t s_x[MAXG * 4 * 64];
+  __shared__ float s_xs[MAXG * 16];
+  __shared__ int s_ids[16][MOE_MAX_TOPK];
+  __shared__ uint32_t s_mask[MOE_MAX_EXPERTS / 32];
+  __shared__ int s_act[SPEC ? 1 : MOE_MAX_EXPERTS];
+  __shared__ int s_u;
+  {
+    const u32x4_t ones_w = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    const bf16x8_t ones = as_bf16x8(ones_w);
+    const __amdgpu_buffer_rsrc_t xres =
+        __builtin_amdgcn_make_buffer_rsrc((void*)f.x, (short)0, (int)(f.T * f.d * 2), kBufferRsrcWord3);
+    const uint32_t xoff = (uint32_t)(col * f.d + 8 * kq) * 2u;
+    for (int g = wave; g < G; g += kWaves) {
+      u32x4_t xv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        xv[i] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xres, xoff + (uint32_t)(g * kGroup + 32 * i) * 2u, 0, 0));
+      f32x4_t as = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s_x[(4 * g + i) * 64 + lane] = xv[i];
+        as = mfma16x16x32(ones, as_bf16x8(xv[i]), as);
+      }
+      if (lane < 16) s_xs[g * 16 + lane] = as[0];  // C column = lane, every row the same sum
+    }
+  }
+
+  // 4. wait until every token is routed: wavefront 0 polls the ready table
+  //    until every pair's entry is set (bounded: a timeout is flagged in the
+  //    counters and the pass goes on with whatever the table holds), and
+  //    leaves the routing table in LDS
+  if (wave == 0) {
+    const int n = T * k;  // <= 256: at most 4 entries per lane
+    int id[4];
+    int spins = 0;
+    for (;;) {
+      bool ready = true;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int i = lane + 64 * m;
+        id[m] = i < n ? __hip_atomic_load(r.ctr + kCtrReady + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 1;
+        ready &= id[m] != 0;
+      }
+      if (__builtin_amdgcn_read_exec() == __ballot(ready)) break;
+      if (++spins > kSpinLimit) {
+        if (lane == 0) __hip_atomic_store(r.ctr + kCtrError, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(4);
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int i = lane + 64 * m;
+      if (i < 16 * MOE_MAX_TOPK) {
+        const int t = i / MOE_MAX_TOPK, j = i % MOE_MAX_TOPK;
+        s_ids[t][j] = -1;
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int i = lane + 64 * m;
+      if (i < n) s_ids[i / k][i % k] = id[m] - 1;
+    }
+  }
+  __syncthreads();
+  const int U = build_active(s_ids, T, k, E, s_mask, SPEC ? nullptr : s_act, &s_u);
+  const int n_items = (SPEC ? E : U) * n_stripes;
+
+  // 5. gate/up items
+  auto start_item = [&](bool have_loads) -> int {
+    for (; item < n_items; item += n_workers) {
+      const int u = item / n_stripes;
+      const int e = SPEC ? u : s_act[u];
+      if (SPEC && !((s_mask[e >> 5] >> (e & 31)) & 1u)) {
+        have_loads = false;  // an expert without pairs: nothing to compute
+        continue;
+      }
+      if (!have_loads) {
+        set_item(e, item % n_stripes);
+#pragma unroll
+        for (int j = 0; j < NB - 1; ++j) load(buf[j], j);
+      }
+      return e;
+    }
+    return -1;
+  };
+  int e = start_item(prefetched);
+  const uint32_t kMask = vgpr_const(0x00780078u), kOne = vgpr_const(0x3F803F80u);
+  while (e >= 0) {
+    const int stripe = item % n_stripes;
+    int hit = -1;
+    for (int j = 0; j < k; ++j) hit = s_ids[col][j] == e ? j : hit;
+    const bool routed = hit >= 0;
+    const int out_row = col * k + hit;  // pair order
+
+    f32x4_t tot[RT];
+#pragma unroll
+    for (int rr = 0; rr < RT; ++rr) tot[rr] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](const Buf& b, int g) {
+      const int gl = min(g, G - 1);
+      const float gv = g < G ? 1.f : 0.f;
+      const float xs = -24.f * s_xs[gl * 16 + col];
+      f32x4_t acc[RT];
+#pragma unroll
+      for (int rr = 0; rr < RT; ++rr) acc[rr] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x8_t xv = as_bf16x8(s_x[(4 * gl + i) * 64 + lane]);
+#pragma unroll
+        for (int rr = 0; rr < RT; ++rr)
+          acc[rr] = mfma16x16x32(as_bf16x8(decode_word_biased(b.c[rr][i], kMask, kOne)), xv, acc[rr]);
+      }
+#pragma unroll
+      for (int rr = 0; rr < RT; ++rr) {
+        const float s4[4] = {__uint_as_float(b.s[rr][0] << 16), __uint_as_float(b.s[rr][0] & 0xFFFF0000u),
+                             __uint_as_float(b.s[rr][1] << 16), __uint_as_float(b.s[rr][1] & 0xFFFF0000u)};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) tot[rr][q] = fmaf(gv * s4[q], fmaf(16.f, acc[rr][q], xs), tot[rr][q]);
+      }
+    };
+    for (int gc = 0; gc < G; gc += NB) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        load(buf[(j + NB - 1) % NB], gc + j + NB - 1);
+        compute(buf[j], gc + j);
+      }
+    }
+    // the next item's first loads go out before this item's stores
+    item += n_workers;
+    e = start_item(false);
+#pragma unroll
+    for (int p = 0; p < RT / 2; ++p) {
+      uint32_t hv[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) hv[q] = f32_to_bf16_bits(silu_f32(tot[2 * p][q]) * tot[2 * p + 1][q]);
+      if (routed) {
+        const int hcol = kTileRows * ((RT / 2) * stripe + p) + 4 * kq;
+        u32x2_t o = {hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16)};
+        *reinterpret_cast<u32x2_t*>(hout + (int64_t)out_row * f.I + hcol) = o;
+      }
+    }
+  }
+}
+
+constexpr int kLayerRT = 2, kLayerNB = 4;
+
+template <typename Kern>
+static int layer_grid(Kern kern, int slot) {
+  static int cached[4] = {0};
+  if (!cached[slot]) {
+    int dev = 0, cus = 0, per_cu = 0;
+    (void)hipGetDevice(&dev);
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 512, 0);
+    cached[slot] = std::max(1, cus) * std::max(1, per_cu);
+  }
+  return cached[slot];
+}
+
+static int64_t align256(int64_t v) { return (v + 255) / 256 * 256; }
+
+static int64_t layer_ws_h(int T, int I, int k) { return align256((int64_t)T * k * I * 2); }
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" int64_t moe_decode_layer_workspace_bytes(int T, int d, int I, int E, int k) {
+  if (T < 0 || d <= 0 || I <= 0 || E <= 0 || k <= 0) return -1;
+  return layer_ws_h(T, I, k) + align256((int64_t)(d / 32) * 32 * 512 * 4);
+}
+
+extern "C" int moe_decode_layer(const moe_decode_layer_args* a, void* stream) {
+  clear_error();
+  MOE_CHECK_ARG(a != nullptr, MOE_ERR_INVALID_ARG, "moe_decode_layer: args is NULL");
+  MOE_CHECK_ARG(a->T >= 0 && a->d > 0 && a->I > 0 && a->E > 0 && a->k > 0, MOE_ERR_INVALID_ARG,
+                "moe_decode_layer: bad sizes T=%d d=%d I=%d E=%d k=%d", a->T, a->d, a->I, a->E, a->k);
+  MOE_CHECK_ARG(a->T <= 16 && a->d % kGroup == 0 && a->d <= 32 * kGroup && a->I % kGroup == 0 &&
+                    a->E <= MOE_MAX_EXPERTS && a->k <= MOE_MAX_TOPK && a->k <= a->E &&
+                    (int64_t)a->T * a->k * a->I * 2 < ((int64_t)1 << 31),
+                MOE_ERR_UNSUPPORTED_SHAPE,
+                "moe_decode_layer: unsupported shape T=%d d=%d I=%d E=%d k=%d (T <= 16, d <= 4096, d and I "
+                "multiples of 128, E <= 1024, k <= min(E,16))",
+                a->T, a->d, a->I, a->E, a->k);
+  if (a->T == 0) return MOE_OK;
+  MOE_CHECK_ARG(a->x && a->w_router && a->bank && a->logits && a->topk_ids && a->topk_weights && a->out &&
+                    a->workspace && a->counters,
+                MOE_ERR_INVALID_ARG, "moe_decode_layer: null pointer");
+  moe_expert_layout lay;
+  int rc = moe_expert_layout_get(a->d, a->I, &lay);
+  if (rc) return rc;
+  MOE_CHECK_ARG(a->bank_stride >= lay.blob_bytes && a->bank_stride % 256 == 0 && ((uintptr_t)a->bank % 256) == 0 &&
+                    a->bank_stride < ((int64_t)1 << 31),
+                MOE_ERR_INVALID_ARG,
+                "moe_decode_layer: bank must be 256-byte aligned with stride >= %lld (multiple of 256, below 2^31), "
+                "got %lld",
+                (long long)lay.blob_bytes, (long long)a->bank_stride);
+  MOE_CHECK_ARG(((uintptr_t)a->x % 16) == 0 && ((uintptr_t)a->w_router % 16) == 0 &&
+                    ((uintptr_t)a->workspace % 256) == 0,
+                MOE_ERR_INVALID_ARG, "moe_decode_layer: x and w_router must be 16-byte, workspace 256-byte aligned");
+  const int64_t need = moe_decode_layer_workspace_bytes(a->T, a->d, a->I, a->E, a->k);
+  MOE_CHECK_ARG(a->workspace_bytes >= need, MOE_ERR_WORKSPACE, "moe_decode_layer: workspace %lld bytes < %lld needed",
+                (long long)a->workspace_bytes, (long long)need);
+  const int umax = (int)std::min<int64_t>(a->E, (int64_t)a->T * a->k);
+  const int dc_stripes = a->d / 32;
+  MOE_CHECK_ARG(dc_units_per_wave(umax, a->I / kGroup, dc_stripes) > 0, MOE_ERR_UNSUPPORTED_SHAPE,
+                "moe_decode_layer: too many (expert, K slice) items for the down pass (E=%d k=%d I=%d)", a->E, a->k,
+                a->I);
+
+  FfnDev f;
+  f.x = a->x;
+  f.T = a->T;
+  f.d = a->d;
+  f.I = a->I;
+  f.E = a->E;
+  f.k = a->k;
+  f.P = (int64_t)a->T * a->k;
+  f.umax = umax;
+  f.topk_ids = a->topk_ids;
+  f.topk_weights = a->topk_weights;
+  f.offsets = nullptr;
+  f.sorted_pairs = nullptr;
+  f.pair_pos = nullptr;
+  f.active = nullptr;
+  f.tile_offsets = nullptr;
+  f.bank = a->bank;
+  f.bank_stride = a->bank_stride;
+  f.slot_of_expert = nullptr;
+  f.off_w13_codes = lay.w13_codes;
+  f.off_w13_scales = lay.w13_scales;
+  f.off_w2_codes = lay.w2_codes;
+  f.off_w2_scales = lay.w2_scales;
+  f.zero_ctr = a->counters + kCtrDown;
+  f.n_zero_ctr = dc_stripes;
+
+  RouteDev r;
+  r.wr = a->w_router;
+  r.renormalize = a->renormalize;
+  r.logits = a->logits;
+  r.ids = a->topk_ids;
+  r.weights = a->topk_weights;
+  r.ctr = a->counters;
+
+  uint8_t* ws = static_cast<uint8_t*>(a->workspace);
+  uint16_t* h = reinterpret_cast<uint16_t*>(ws);
+  float* dc_part = reinterpret_cast<float*>(ws + layer_ws_h(a->T, a->I, a->k));
+  hipStream_t s = (hipStream_t)stream;
+
+  // every expert in order (prefetch before routing) when the step routes at
+  // least one pair per expert on average; else the active experts only
+  const bool spec = (int64_t)a->T * a->k >= a->E;
+  const int G = a->d / kGroup;
+  const int n_stripes = 2 * a->I / (kTileRows * kLayerRT);
+  const int64_t items = (int64_t)(spec ? a->E : umax) * n_stripes;
+  const int64_t want = std::max<int64_t>(ceil_div(items, 8), ceil_div((int64_t)a->T * a->E, 8));
+  timing_begin(K_GATEUP_DECODE, s);
+  if (G <= 16) {
+    auto kern = spec ? k_layer_gateup<kLayerRT, kLayerNB, 16, true> : k_layer_gateup<kLayerRT, kLayerNB, 16, false>;
+    const int cap = layer_grid(kern, spec ? 0 : 1);
+    hipLaunchKernelGGL(kern, dim3((unsigned)std::min<int64_t>(cap, want)), dim3(512), 0, s, f, r, h);
+  } else {
+    auto kern = spec ? k_layer_gateup<kLayerRT, kLayerNB, 32, true> : k_layer_gateup<kLayerRT, kLayerNB, 32, false>;
+    const int cap = layer_grid(kern, spec ? 2 : 3);
+    hipLaunchKernelGGL(kern, dim3((unsigned)std::min<int64_t>(cap, want)), dim3(512), 0, s, f, r, h);
+  }
+  timing_end(K_GATEUP_DECODE, s);
+  rc = check_launch("moe_decode_layer (routing + gate/up)");
+  if (rc) return rc;
+  timing_begin(K_DOWN_DECODE, s);
+  launch_down_combine(f, h, a->out, dc_part, a->counters + kCtrDown, a->counters, kCtrRouteEnd, s, true);
+  timing_end(K_DOWN_DECODE, s);
+  return check_launch("moe_decode_layer (down + combine)");
+}

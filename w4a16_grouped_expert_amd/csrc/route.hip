@@ -10,31 +10,13 @@
 // blocks of TB tokens x all experts for large T (router weights reused across
 // the TB tokens).
 #include "align_block.hpp"
+#include "route_rank.hpp"
 
 namespace moe {
 
 constexpr int kRouteMaxTB = 4;
 
 __device__ __forceinline__ double bf16_to_f64(uint32_t bits16) { return (double)bf16_bits_to_f32(bits16); }
-
-__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
-  return v > bv || (v == bv && i < bi);
-}
-
-// Number of the token's E logits (row, in LDS) that beat (v, e): 16 broadcast
-// reads are issued before their compares, so the LDS latency is paid once per 16.
-__device__ __forceinline__ int rank_in_row(const float* row, int E, float v, int e) {
-  int rank = 0, o = 0;
-  for (; o + 16 <= E; o += 16) {
-    float r[16];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) r[u] = row[o + u];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) rank += better(r[u], o + u, v, e) ? 1 : 0;
-  }
-  for (; o < E; ++o) rank += better(row[o], o, v, e) ? 1 : 0;
-  return rank;
-}
 
 // Top-k of one token's E logits (in LDS) by one wavefront: lane l owns experts
 // l, l+64, ...; k rounds of a wave-wide (value desc, index asc) argmax.

@@ -732,7 +732,7 @@ constexpr int kDcMaxChunks = 32;
 // routing table in each workgroup (the fused decode layer); else h rows in
 // expert-sorted order with the active list of moe_align.  route_ctr (PAIR): the
 // n_route_ctr counters of the routing pass, zeroed here for the next step.
-template <int RT, int D, int UPW, int WAVES, int OCC, bool PAIR>
+template <int RT, int D, int UPW, int WAVES, int OCC, bool PAIR, bool SPEC>
 __global__ __launch_bounds__(WAVES * 64, OCC) void k_down_combine(FfnDev f, const uint16_t* __restrict__ h,
                                                                   uint16_t* __restrict__ out,
                                                                   float* __restrict__ part,
@@ -750,9 +750,54 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_down_combine(FfnDev f, cons
   const int item = chunk * WAVES + wave;
   // the active count, the wavefront's work record (read within the work list's
   // capacity, used only if the item exists) and the routing table: one round trip
-  int U = PAIR ? 0 : f.active[0];
-  i32x4_t rec = PAIR ? i32x4_t{0, 0, 0, 0}
-                     : reinterpret_cast<const i32x4_t*>(f.active + 4)[min(item / n_slices, f.umax - 1)];
+  int U = (PAIR || SPEC) ? 0 : f.active[0];
+  i32x4_t rec = (PAIR || SPEC) ? i32x4_t{0, 0, 0, 0}
+                               : reinterpret_cast<const i32x4_t*>(f.active + 4)[min(item / n_slices, f.umax - 1)];
+
+  const uint32_t voff_c = 16u * lane, voff_s = 8u * kq;
+  const uint32_t soff_c = (uint32_t)(f.off_w2_codes + (int64_t)(RT * stripe) * G * kTileBytes);
+  const uint32_t soff_s = (uint32_t)(f.off_w2_scales + (int64_t)(RT * stripe) * G * kTileRows * 2);
+  struct Buf {
+    u32x4_t c[RT];
+    u32x2_t s[RT];
+    u32x4_t x[4];
+  };
+  Buf buf[D + 1];
+  __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc((void*)f.bank, (short)0, 0, kBufferRsrcWord3);
+  int g0 = 0, ng = 1;
+  // group i of the slice; past the slice's end the loads repeat its last group
+  // (weight 0), so the loads and their waits do not depend on the slice length
+  auto wload = [&](Buf& b, int i) {
+    const int g = g0 + min(i, ng - 1);
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      b.c[r] = __builtin_bit_cast(
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                       wres, voff_c, soff_c + (uint32_t)(r * G + g) * kTileBytes, kCacheNonTemporal));
+      b.s[r] = __builtin_bit_cast(
+          u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(wres, voff_s,
+                                                        soff_s + (uint32_t)(r * G + g) * kTileRows * 2, 0));
+    }
+  };
+  auto set_expert = [&](int e) {
+    const int slot = f.slot_of_expert ? f.slot_of_expert[e] : e;
+    wres = __builtin_amdgcn_make_buffer_rsrc((void*)(f.bank + (int64_t)slot * f.bank_stride), (short)0, 0x7FFFFFFF,
+                                             kBufferRsrcWord3);
+    g0 = (item % n_slices) * UPW;
+    ng = min(UPW, G - g0);
+  };
+  // SPEC: items over every expert in id order (steps that route at least one
+  // pair per expert on average): the wavefront knows its expert before the
+  // routing table is read and requests its first D groups of weights at once;
+  // an expert without pairs computes nothing
+  const bool early = SPEC && item < f.E * n_slices;
+  if (early) {
+    rec[0] = item / n_slices;
+    if (!PAIR) rec[1] = f.offsets[rec[0]];
+    set_expert(rec[0]);
+#pragma unroll
+    for (int j = 0; j < D; ++j) wload(buf[j], j);
+  }
 
   __shared__ int s_ids[16][MOE_MAX_TOPK];
   __shared__ float s_w[16][MOE_MAX_TOPK];
@@ -770,11 +815,13 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_down_combine(FfnDev f, cons
   if (PAIR) {
     if (blockIdx.x == 0)
       for (int i = tid; i < n_route_ctr; i += kThreads) route_ctr[i] = 0;
-    __syncthreads();
-    U = build_active(s_ids, f.T, f.k, f.E, s_mask, s_act, &s_u);
-    rec[0] = s_act[min(item / n_slices, max(U - 1, 0))];
+    if (!SPEC) {
+      __syncthreads();
+      U = build_active(s_ids, f.T, f.k, f.E, s_mask, s_act, &s_u);
+      rec[0] = s_act[min(item / n_slices, max(U - 1, 0))];
+    }
   }
-  const int n_items = U * n_slices;
+  const int n_items = SPEC ? f.E * n_slices : U * n_slices;
   const int nch = (n_items + WAVES - 1) / WAVES;          // chunks with work on every stripe
   if (chunk >= nch && !(chunk == 0 && nch == 0)) return;  // (no active expert: chunk 0 writes zeros)
   __syncthreads();
@@ -782,46 +829,24 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_down_combine(FfnDev f, cons
   f32x4_t tot[RT];
 #pragma unroll
   for (int r = 0; r < RT; ++r) tot[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  if (item < n_items) {
-    const int e = rec[0];
-    const int g0 = (item % n_slices) * UPW, ng = min(UPW, G - g0);
-    const int slot = f.slot_of_expert ? f.slot_of_expert[e] : e;
+  // the lane's token: its slot for the item's expert (if routed there), its h row
+  const int e = rec[0];
+  int hit = -1;
+  if (item < n_items)
+    for (int j = 0; j < f.k; ++j) hit = s_ids[col][j] == e ? j : hit;
+  const uint32_t colmask = (uint32_t)__ballot(hit >= 0) & 0xFFFFu;
+  if (item < n_items && colmask != 0u) {
+    if (!early) set_expert(e);
     const uint32_t kMask = vgpr_const(0x00780078u), kOne = vgpr_const(0x3F803F80u);
     const u32x4_t ones_w = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
     const bf16x8_t ones = as_bf16x8(ones_w);
     const __amdgpu_buffer_rsrc_t hres =
         __builtin_amdgcn_make_buffer_rsrc((void*)h, (short)0, (int)(f.P * f.I * 2), kBufferRsrcWord3);
-    const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(f.bank + (int64_t)slot * f.bank_stride), (short)0, 0x7FFFFFFF, kBufferRsrcWord3);
-    // the lane's token: its slot for expert e (if routed there), its h row
-    int hit = -1;
-    for (int j = 0; j < f.k; ++j) hit = s_ids[col][j] == e ? j : hit;
-    const uint32_t colmask = (uint32_t)__ballot(hit >= 0) & 0xFFFFu;
     const int hrow = PAIR ? col * f.k + hit : rec[1] + __popc(colmask & ((1u << col) - 1u));
     const uint32_t hoff = hit >= 0 ? (uint32_t)(hrow * f.I + 8 * kq) * 2u : 0x7F000000u;  // else reads zeros
     const float wt = hit >= 0 ? s_w[col][hit] : 0.f;
-    const uint32_t voff_c = 16u * lane, voff_s = 8u * kq;
-    const uint32_t soff_c = (uint32_t)(f.off_w2_codes + (int64_t)(RT * stripe) * G * kTileBytes);
-    const uint32_t soff_s = (uint32_t)(f.off_w2_scales + (int64_t)(RT * stripe) * G * kTileRows * 2);
-
-    struct Buf {
-      u32x4_t c[RT];
-      u32x2_t s[RT];
-      u32x4_t x[4];
-    };
-    // group i of the slice; past the slice's end the loads repeat its last group
-    // (weight 0), so the loads and their waits do not depend on the slice length
-    auto load = [&](Buf& b, int i) {
+    auto xload = [&](Buf& b, int i) {
       const int g = g0 + min(i, ng - 1);
-#pragma unroll
-      for (int r = 0; r < RT; ++r) {
-        b.c[r] = __builtin_bit_cast(
-            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                         wres, voff_c, soff_c + (uint32_t)(r * G + g) * kTileBytes, kCacheNonTemporal));
-        b.s[r] = __builtin_bit_cast(
-            u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(wres, voff_s,
-                                                          soff_s + (uint32_t)(r * G + g) * kTileRows * 2, 0));
-      }
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4)
         b.x[i4] = __builtin_bit_cast(
@@ -850,15 +875,21 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_down_combine(FfnDev f, cons
         for (int q = 0; q < 4; ++q) tot[r][q] = fmaf(w * s4[q], fmaf(16.f, acc[r][q], xs), tot[r][q]);
       }
     };
-    Buf buf[D + 1];
+    if (!early) {
 #pragma unroll
-    for (int j = 0; j < D; ++j) load(buf[j], j);
+      for (int j = 0; j < D; ++j) wload(buf[j], j);
+    }
+#pragma unroll
+    for (int j = 0; j < D; ++j) xload(buf[j], j);
     // the scheduling barriers keep each group's loads ahead of the multiply that
     // precedes their use (the scheduler would otherwise sink them to their users)
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < UPW; ++i) {
-      if (i + D < UPW) load(buf[(i + D) % (D + 1)], i + D);
+      if (i + D < UPW) {
+        wload(buf[(i + D) % (D + 1)], i + D);
+        xload(buf[(i + D) % (D + 1)], i + D);
+      }
       __builtin_amdgcn_sched_barrier(0);
       compute(buf[i % (D + 1)], i);
       __builtin_amdgcn_sched_barrier(0);
@@ -1141,16 +1172,16 @@ int dc_units_per_wave(int umax, int G, int stripes) {
   return (int64_t)umax * ((G + upw - 1) / upw) <= (int64_t)kDcMaxChunks * kDcWaves ? upw : 0;
 }
 
-template <int UPW>
+template <int UPW, bool SPEC>
 static void launch_dc(const FfnDev& f, const uint16_t* h, uint16_t* out, float* part, int32_t* counters,
                       int32_t* route_ctr, int n_route_ctr, hipStream_t s, bool pair, dim3 grid) {
   const dim3 block(kDcWaves * 64);
   if (pair)
-    hipLaunchKernelGGL((k_down_combine<kDcRT, kDcD, UPW, kDcWaves, kDcOcc, true>), grid, block, 0, s, f, h, out, part,
-                       counters, route_ctr, n_route_ctr);
+    hipLaunchKernelGGL((k_down_combine<kDcRT, kDcD, UPW, kDcWaves, kDcOcc, true, SPEC>), grid, block, 0, s, f, h, out,
+                       part, counters, route_ctr, n_route_ctr);
   else
-    hipLaunchKernelGGL((k_down_combine<kDcRT, kDcD, UPW, kDcWaves, kDcOcc, false>), grid, block, 0, s, f, h, out, part,
-                       counters, route_ctr, n_route_ctr);
+    hipLaunchKernelGGL((k_down_combine<kDcRT, kDcD, UPW, kDcWaves, kDcOcc, false, SPEC>), grid, block, 0, s, f, h,
+                       out, part, counters, route_ctr, n_route_ctr);
 }
 
 void launch_down_combine(const FfnDev& f, const uint16_t* h, uint16_t* out, float* part, int32_t* counters,
@@ -1160,12 +1191,19 @@ void launch_down_combine(const FfnDev& f, const uint16_t* h, uint16_t* out, floa
   const int upw = dc_units_per_wave(f.umax, f.I / kGroup, stripes);
   const int64_t slices = ceil_div(f.I / kGroup, upw);
   const dim3 grid((unsigned)(stripes * ceil_div((int64_t)f.umax * slices, kDcWaves)));
-  if (upw <= 4)
-    launch_dc<4>(f, h, out, part, counters, route_ctr, n_route_ctr, s, pair, grid);
-  else if (upw <= 8)
-    launch_dc<8>(f, h, out, part, counters, route_ctr, n_route_ctr, s, pair, grid);
-  else
-    launch_dc<16>(f, h, out, part, counters, route_ctr, n_route_ctr, s, pair, grid);
+  // every expert in id order when the step routes at least one pair per expert
+  // on average (umax == E then), else the active experts
+  const bool spec = (int64_t)f.T * f.k >= f.E;
+  if (upw <= 4) {
+    if (spec) launch_dc<4, true>(f, h, out, part, counters, route_ctr, n_route_ctr, s, pair, grid);
+    else launch_dc<4, false>(f, h, out, part, counters, route_ctr, n_route_ctr, s, pair, grid);
+  } else if (upw <= 8) {
+    if (spec) launch_dc<8, true>(f, h, out, part, counters, route_ctr, n_route_ctr, s, pair, grid);
+    else launch_dc<8, false>(f, h, out, part, counters, route_ctr, n_route_ctr, s, pair, grid);
+  } else {
+    if (spec) launch_dc<16, true>(f, h, out, part, counters, route_ctr, n_route_ctr, s, pair, grid);
+    else launch_dc<16, false>(f, h, out, part, counters, route_ctr, n_route_ctr, s, pair, grid);
+  }
 }
 
 int launch_decode(const FfnDev& f_in, uint16_t* h, float* y, int ksplit, int nb, hipStream_t s, uint16_t* out,

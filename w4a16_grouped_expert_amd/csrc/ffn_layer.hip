@@ -202,38 +202,66 @@ __global__ __launch_bounds__(512, 4) void k_layer_gateup(FfnDev f, RouteDev r, u
   __shared__ float s_lg[kWaves][kRankMaxE];
   __shared__ float s_sel_v[kWaves][MOE_MAX_TOPK];
   __shared__ int s_sel_i[kWaves][MOE_MAX_TOPK];
-  if (worker >= n_logit) {
-    prefetch();
-  } else {
-    const int nch = f.d / 8;
-    for (int task = worker; task < n_tasks; task += n_logit) {
-      const int t = task / E, e = task % E;
-      const uint16_t* xr = f.x + (int64_t)t * f.d;
-      const uint16_t* wrow = r.wr + (int64_t)e * f.d;
-      double acc = 0.0;
-      constexpr int kB = 4;  // chunks per lane in flight (the sum order does not depend on it)
-      for (int c0 = 0; c0 < nch; c0 += 64 * kB) {
-        u32x4_t xq[kB], wq[kB];
+  __shared__ int s_route[kWaves];
+  const int nch = f.d / 8;
+  // logit of task (t, e), rounded once; lane 0 stores it with a device-coherent store
+  auto logit = [&](int task) {
+    const int t = task / E, e = task % E;
+    const uint16_t* xr = f.x + (int64_t)t * f.d;
+    const uint16_t* wrow = r.wr + (int64_t)e * f.d;
+    double acc = 0.0;
+    constexpr int kB = 4;  // chunks per lane in flight (the sum order does not depend on it)
+    for (int c0 = 0; c0 < nch; c0 += 64 * kB) {
+      u32x4_t xq[kB], wq[kB];
 #pragma unroll
-        for (int c = 0; c < kB; ++c) {
-          const int ch = c0 + lane + 64 * c;
-          xq[c] = ch < nch ? *reinterpret_cast<const u32x4_t*>(xr + 8 * ch) : u32x4_t{0u, 0u, 0u, 0u};
-          wq[c] = ch < nch ? *reinterpret_cast<const u32x4_t*>(wrow + 8 * ch) : u32x4_t{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int c = 0; c < kB; ++c)
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            acc = fma((double)bf16_bits_to_f32(xq[c][m] & 0xFFFFu), (double)bf16_bits_to_f32(wq[c][m] & 0xFFFFu),
-                      acc);
-            acc = fma((double)bf16_bits_to_f32(xq[c][m] >> 16), (double)bf16_bits_to_f32(wq[c][m] >> 16), acc);
-          }
+      for (int c = 0; c < kB; ++c) {
+        const int ch = c0 + lane + 64 * c;
+        xq[c] = ch < nch ? *reinterpret_cast<const u32x4_t*>(xr + 8 * ch) : u32x4_t{0u, 0u, 0u, 0u};
+        wq[c] = ch < nch ? *reinterpret_cast<const u32x4_t*>(wrow + 8 * ch) : u32x4_t{0u, 0u, 0u, 0u};
       }
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-      if (lane == 0)
-        __hip_atomic_store(r.logits + (int64_t)t * E + e, (float)acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the logit has reached device scope
+      for (int c = 0; c < kB; ++c)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          acc = fma((double)bf16_bits_to_f32(xq[c][m] & 0xFFFFu), (double)bf16_bits_to_f32(wq[c][m] & 0xFFFFu),
+                    acc);
+          acc = fma((double)bf16_bits_to_f32(xq[c][m] >> 16), (double)bf16_bits_to_f32(wq[c][m] >> 16), acc);
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    if (lane == 0)
+      __hip_atomic_store(r.logits + (int64_t)t * E + e, (float)acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the logit has reached device scope
+  };
+  if (n_tasks <= n_workers) {
+    // one task per wavefront, counted once per workgroup and token: the
+    // workgroup that completes a token's E logits routes it (a wavefront per token)
+    if ((int)blockIdx.x * kWaves < n_tasks) {
+      if (worker < n_tasks) logit(worker);
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        const int first = blockIdx.x * kWaves, last_task = min(first + kWaves, n_tasks) - 1;
+        int n_done = 0;
+        for (int t = first / E; t <= last_task / E; ++t) {
+          const int cnt = min(last_task, t * E + E - 1) - max(first, t * E) + 1;
+          if (__hip_atomic_fetch_add(r.ctr + kCtrLogits + kLine * t, cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) +
+                  cnt == E)
+            s_route[n_done++] = t;
+        }
+        for (int j = n_done; j < kWaves; ++j) s_route[j] = -1;
+      }
+      __syncthreads();
+      const int t = s_route[wave];
+      if (t >= 0) route_token(r, t, E, k, s_lg[wave], s_sel_v[wave], s_sel_i[wave]);
+    }
+    prefetch();
+  } else if (worker >= n_logit) {
+    prefetch();
+  } else {
+    for (int task = worker; task < n_tasks; task += n_logit) {
+      logit(task);
+      const int t = task / E;
       int last = 0;
       if (lane == 0)
         last = __hip_atomic_fetch_add(r.ctr + kCtrLogits + kLine * t, 1, __ATOMIC_RELAXED,

@@ -186,7 +186,10 @@ __global__ __launch_bounds__(512, 4) void k_layer_gateup(FfnDev f, RouteDev r, u
 
   // 1. the first item's weights, when it does not depend on the routing (the
   //    wavefronts that compute logits issue them after their router loads)
-  int item = worker;
+  // items are dealt to the workgroups in turn (item i to workgroup i mod the grid),
+  // so every workgroup, and every CU, gets the same share of them, idle experts
+  // included
+  int item = wave * gridDim.x + blockIdx.x;
   const bool prefetched = SPEC && item < E * n_stripes;
   const int n_tasks = T * E;
   const int n_logit = min(n_workers, n_tasks);

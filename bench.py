@@ -29,10 +29,11 @@ if ROOT not in sys.path:
 METRIC = "MoE-layer tokens/s + achieved HBM GB/s (W4A16, OLMoE shape, T=1..4096)"
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "gateup_decode_olmoe_t16_hbm_counters.txt")
-COUNTED_SOURCES = ["w4a16_grouped_expert_amd/csrc/ffn_decode.hip", "w4a16_grouped_expert_amd/csrc/ffn_common.hpp",
-                   "w4a16_grouped_expert_amd/csrc/common.hpp", "w4a16_grouped_expert_amd/csrc/ffn_layer.hip",
-                   "w4a16_grouped_expert_amd/csrc/align_block.hpp"]
+# HBM counters of the roofline kernel (routing + grouped gate/up of moe_decode_layer)
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "routing_gateup_decode_olmoe_t16_hbm_counters.txt")
+COUNTED_SOURCES = ["w4a16_grouped_expert_amd/csrc/ffn_layer.hip", "w4a16_grouped_expert_amd/csrc/ffn_common.hpp",
+                   "w4a16_grouped_expert_amd/csrc/common.hpp", "w4a16_grouped_expert_amd/csrc/align_block.hpp",
+                   "w4a16_grouped_expert_amd/csrc/route_rank.hpp"]
 
 
 def parse():
@@ -379,7 +380,7 @@ def run_decode(dec, T, steps, warmup, x_sets, timed_kernels=("gateup_decode", "d
 
 
 def measured_traffic():
-    """HBM bytes per launch of the decode gate/up kernel from the committed rocprofv3
+    """HBM bytes per launch of the decode roofline kernel from the committed rocprofv3
     counter summary, if it was taken on the kernel sources as they are now."""
     import hashlib
     try:

@@ -123,3 +123,31 @@ def test_workspace_bytes_sizes(L):
     ws = L.moe_ffn_workspace_bytes(16, 2048, 1024, 64, 8, 1)
     assert ws >= 16 * 8 * 1024 * 2 + 16 * 8 * 2048 * 4
     assert L.moe_ffn_workspace_bytes(-1, 2048, 1024, 64, 8, 0) == -1
+
+
+def test_decode_layer_host_checks(L):
+    """moe_decode_layer: argument errors are reported before anything is enqueued."""
+    from w4a16_grouped_expert_amd import _lib
+    vp = 256
+    assert L.moe_decode_layer(None, None) == 1
+    a = _lib.LayerArgs()
+    a.T, a.d, a.I, a.E, a.k, a.renormalize = 17, 256, 512, 8, 2, 1
+    assert L.moe_decode_layer(ctypes.byref(a), None) == 2                # T > 16
+    a.T, a.d = 4, 8192
+    assert L.moe_decode_layer(ctypes.byref(a), None) == 2                # d > 4096
+    a.d = 256
+    assert L.moe_decode_layer(ctypes.byref(a), None) == 1                # null pointers
+    for f in ("x", "w_router", "bank", "logits", "topk_ids", "topk_weights", "out", "workspace", "counters"):
+        setattr(a, f, vp)
+    a.bank_stride = 202752
+    a.workspace_bytes = 16
+    assert L.moe_decode_layer(ctypes.byref(a), None) == 3                # workspace too small
+    a.workspace_bytes = L.moe_decode_layer_workspace_bytes(4, 256, 512, 8, 2)
+    a.bank_stride = 1000
+    assert L.moe_decode_layer(ctypes.byref(a), None) == 1                # stride below one blob
+    a.T = 0
+    assert L.moe_decode_layer(ctypes.byref(a), None) == 0                # T = 0: no-op
+    # workspace: h [T*k, I] bf16 + the down pass's partial sums, 256-byte granules
+    ws = L.moe_decode_layer_workspace_bytes(16, 2048, 1024, 64, 8)
+    assert ws >= 16 * 8 * 1024 * 2 + (2048 // 32) * 32 * 512 * 4
+    assert L.moe_decode_layer_workspace_bytes(-1, 2048, 1024, 64, 8) == -1

@@ -146,7 +146,10 @@ __device__ void route_token(const RouteDev& r, int t, int E, int k, float* s_lg,
 // every expert in id order, the first one prefetched before the routing is
 // known (an item of an expert without pairs is skipped); else over the active
 // experts, known after the routing.
-template <int RT, int NB, int MAXG, bool SPEC>
+// KS > 1 (with !SPEC, for steps with few items): each item's K groups are split
+// over KS wavefronts of one workgroup, whose partial sums meet in LDS in part
+// order before the SwiGLU.
+template <int RT, int NB, int MAXG, bool SPEC, int KS>
 __global__ __launch_bounds__(512, 4) void k_layer_gateup(FfnDev f, RouteDev r, uint16_t* __restrict__ hout) {
   constexpr int kWaves = 8;
   zero_down_counters(f);
@@ -166,10 +169,12 @@ __global__ __launch_bounds__(512, 4) void k_layer_gateup(FfnDev f, RouteDev r, u
   Buf buf[NB];
   const uint8_t* codes = nullptr;
   const uint16_t* scales = nullptr;
-  // past the item's last group the loads repeat group G - 1 and the group's
-  // weight is 0, so no load sits under a branch and the wait counts stay exact
+  // past the item's last group (g_lim, G or the end of the wavefront's K part)
+  // the loads repeat the last one and the group's weight is 0, so no load sits
+  // under a branch and the wait counts stay exact
+  int g_lim = G;
   auto load = [&](Buf& b, int g) {
-    const int gl = min(g, G - 1);
+    const int gl = min(g, g_lim - 1);
 #pragma unroll
     for (int rr = 0; rr < RT; ++rr) {
       b.c[rr] = __builtin_nontemporal_load(
@@ -345,77 +350,124 @@ __global__ __launch_bounds__(512, 4) void k_layer_gateup(FfnDev f, RouteDev r, u
   const int n_items = (SPEC ? E : U) * n_stripes;
 
   // 5. gate/up items
-  auto start_item = [&](bool have_loads) -> int {
-    for (; item < n_items; item += n_workers) {
-      const int u = item / n_stripes;
-      const int e = SPEC ? u : s_act[u];
-      if (SPEC && !((s_mask[e >> 5] >> (e & 31)) & 1u)) {
-        have_loads = false;  // an expert without pairs: nothing to compute
-        continue;
-      }
-      if (!have_loads) {
-        set_item(e, item % n_stripes);
-#pragma unroll
-        for (int j = 0; j < NB - 1; ++j) load(buf[j], j);
-      }
-      return e;
-    }
-    return -1;
-  };
-  int e = start_item(prefetched);
   const uint32_t kMask = vgpr_const(0x00780078u), kOne = vgpr_const(0x3F803F80u);
-  while (e >= 0) {
-    const int stripe = item % n_stripes;
+  auto compute = [&](const Buf& b, int g, f32x4_t* tot) {
+    const int gl = min(g, g_lim - 1);
+    const float gv = g < g_lim ? 1.f : 0.f;
+    const float xs = -24.f * s_xs[gl * 16 + col];
+    f32x4_t acc[RT];
+#pragma unroll
+    for (int rr = 0; rr < RT; ++rr) acc[rr] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bf16x8_t xv = as_bf16x8(s_x[(4 * gl + i) * 64 + lane]);
+#pragma unroll
+      for (int rr = 0; rr < RT; ++rr)
+        acc[rr] = mfma16x16x32(as_bf16x8(decode_word_biased(b.c[rr][i], kMask, kOne)), xv, acc[rr]);
+    }
+#pragma unroll
+    for (int rr = 0; rr < RT; ++rr) {
+      const float s4[4] = {__uint_as_float(b.s[rr][0] << 16), __uint_as_float(b.s[rr][0] & 0xFFFF0000u),
+                           __uint_as_float(b.s[rr][1] << 16), __uint_as_float(b.s[rr][1] & 0xFFFF0000u)};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) tot[rr][q] = fmaf(gv * s4[q], fmaf(16.f, acc[rr][q], xs), tot[rr][q]);
+    }
+  };
+  // SwiGLU of a finished item and its h stores (pair order)
+  auto store_h = [&](const f32x4_t* tot, int e, int stripe) {
     int hit = -1;
     for (int j = 0; j < k; ++j) hit = s_ids[col][j] == e ? j : hit;
-    const bool routed = hit >= 0;
-    const int out_row = col * k + hit;  // pair order
-
-    f32x4_t tot[RT];
-#pragma unroll
-    for (int rr = 0; rr < RT; ++rr) tot[rr] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    auto compute = [&](const Buf& b, int g) {
-      const int gl = min(g, G - 1);
-      const float gv = g < G ? 1.f : 0.f;
-      const float xs = -24.f * s_xs[gl * 16 + col];
-      f32x4_t acc[RT];
-#pragma unroll
-      for (int rr = 0; rr < RT; ++rr) acc[rr] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bf16x8_t xv = as_bf16x8(s_x[(4 * gl + i) * 64 + lane]);
-#pragma unroll
-        for (int rr = 0; rr < RT; ++rr)
-          acc[rr] = mfma16x16x32(as_bf16x8(decode_word_biased(b.c[rr][i], kMask, kOne)), xv, acc[rr]);
-      }
-#pragma unroll
-      for (int rr = 0; rr < RT; ++rr) {
-        const float s4[4] = {__uint_as_float(b.s[rr][0] << 16), __uint_as_float(b.s[rr][0] & 0xFFFF0000u),
-                             __uint_as_float(b.s[rr][1] << 16), __uint_as_float(b.s[rr][1] & 0xFFFF0000u)};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) tot[rr][q] = fmaf(gv * s4[q], fmaf(16.f, acc[rr][q], xs), tot[rr][q]);
-      }
-    };
-    for (int gc = 0; gc < G; gc += NB) {
-#pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        load(buf[(j + NB - 1) % NB], gc + j + NB - 1);
-        compute(buf[j], gc + j);
-      }
-    }
-    // the next item's first loads go out before this item's stores
-    item += n_workers;
-    e = start_item(false);
 #pragma unroll
     for (int p = 0; p < RT / 2; ++p) {
       uint32_t hv[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) hv[q] = f32_to_bf16_bits(silu_f32(tot[2 * p][q]) * tot[2 * p + 1][q]);
-      if (routed) {
+      if (hit >= 0) {
         const int hcol = kTileRows * ((RT / 2) * stripe + p) + 4 * kq;
         u32x2_t o = {hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16)};
-        *reinterpret_cast<u32x2_t*>(hout + (int64_t)out_row * f.I + hcol) = o;
+        *reinterpret_cast<u32x2_t*>(hout + (int64_t)(col * k + hit) * f.I + hcol) = o;
       }
+    }
+  };
+  if constexpr (KS > 1) {
+    static_assert(!SPEC, "K parts only for items over the active experts");
+    __shared__ f32x4_t s_part[kWaves][RT][64];
+    constexpr int kGroups = kWaves / KS;  // items per workgroup and round
+    const int grp = wave / KS, kp = wave % KS;
+    const int gq = (G + KS - 1) / KS;
+    const int g0 = min(G, kp * gq);
+    g_lim = min(G, g0 + gq);
+    for (int rnd = 0; (rnd * kGroups) * (int)gridDim.x + (int)blockIdx.x < n_items; ++rnd) {
+      const int it = (rnd * kGroups + grp) * gridDim.x + blockIdx.x;
+      const bool valid = it < n_items && g0 < g_lim;
+      f32x4_t tot[RT];
+#pragma unroll
+      for (int rr = 0; rr < RT; ++rr) tot[rr] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if (valid) {
+        set_item(s_act[it / n_stripes], it % n_stripes);
+#pragma unroll
+        for (int j = 0; j < NB - 1; ++j) load(buf[j], g0 + j);
+        for (int gc = g0; gc < g_lim; gc += NB) {
+#pragma unroll
+          for (int j = 0; j < NB; ++j) {
+            load(buf[(j + NB - 1) % NB], gc + j + NB - 1);
+            compute(buf[j], gc + j, tot);
+          }
+        }
+      }
+      if (kp > 0) {
+#pragma unroll
+        for (int rr = 0; rr < RT; ++rr) s_part[wave][rr][lane] = tot[rr];
+      }
+      __syncthreads();
+      if (kp == 0 && it < n_items) {
+#pragma unroll
+        for (int q = 1; q < KS; ++q)
+#pragma unroll
+          for (int rr = 0; rr < RT; ++rr) {
+            const f32x4_t o = s_part[wave + q][rr][lane];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) tot[rr][c] = tot[rr][c] + o[c];
+          }
+        store_h(tot, s_act[it / n_stripes], it % n_stripes);
+      }
+      __syncthreads();  // s_part is free for the next round
+    }
+  } else {
+    auto start_item = [&](bool have_loads) -> int {
+      for (; item < n_items; item += n_workers) {
+        const int u = item / n_stripes;
+        const int e = SPEC ? u : s_act[u];
+        if (SPEC && !((s_mask[e >> 5] >> (e & 31)) & 1u)) {
+          have_loads = false;  // an expert without pairs: nothing to compute
+          continue;
+        }
+        if (!have_loads) {
+          set_item(e, item % n_stripes);
+#pragma unroll
+          for (int j = 0; j < NB - 1; ++j) load(buf[j], j);
+        }
+        return e;
+      }
+      return -1;
+    };
+    int e = start_item(prefetched);
+    while (e >= 0) {
+      const int stripe = item % n_stripes, cur_e = e;
+      f32x4_t tot[RT];
+#pragma unroll
+      for (int rr = 0; rr < RT; ++rr) tot[rr] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int gc = 0; gc < G; gc += NB) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          load(buf[(j + NB - 1) % NB], gc + j + NB - 1);
+          compute(buf[j], gc + j, tot);
+        }
+      }
+      // the next item's first loads go out before this item's stores
+      item += n_workers;
+      e = start_item(false);
+      store_h(tot, cur_e, stripe);
     }
   }
 }
@@ -424,7 +476,7 @@ constexpr int kLayerRT = 2, kLayerNB = 4;
 
 template <typename Kern>
 static int layer_grid(Kern kern, int slot) {
-  static int cached[4] = {0};
+  static int cached[8] = {0};
   if (!cached[slot]) {
     int dev = 0, cus = 0, per_cu = 0;
     (void)hipGetDevice(&dev);
@@ -433,6 +485,15 @@ static int layer_grid(Kern kern, int slot) {
     cached[slot] = std::max(1, cus) * std::max(1, per_cu);
   }
   return cached[slot];
+}
+
+// every workgroup resident (the launch waits on its own routing): the grid is
+// capped at the resident count
+template <typename Kern>
+static void launch_layer_gateup(Kern kern, int slot, const FfnDev& f, const RouteDev& r, uint16_t* h, int64_t want,
+                                hipStream_t s) {
+  const int cap = layer_grid(kern, slot);
+  hipLaunchKernelGGL(kern, dim3((unsigned)std::min<int64_t>(cap, want)), dim3(512), 0, s, f, r, h);
 }
 
 static int64_t align256(int64_t v) { return (v + 255) / 256 * 256; }
@@ -533,13 +594,27 @@ extern "C" int moe_decode_layer(const moe_decode_layer_args* a, void* stream) {
   const int64_t want = std::max<int64_t>(ceil_div(items, 8), ceil_div((int64_t)a->T * a->E, 8));
   timing_begin(K_GATEUP_DECODE, s);
   if (G <= 16) {
-    auto kern = spec ? k_layer_gateup<kLayerRT, kLayerNB, 16, true> : k_layer_gateup<kLayerRT, kLayerNB, 16, false>;
-    const int cap = layer_grid(kern, spec ? 0 : 1);
-    hipLaunchKernelGGL(kern, dim3((unsigned)std::min<int64_t>(cap, want)), dim3(512), 0, s, f, r, h);
+    if (spec) {
+      launch_layer_gateup(k_layer_gateup<kLayerRT, kLayerNB, 16, true, 1>, 0, f, r, h, want, s);
+    } else {
+      // few items: each item's K groups split over 4 or 2 wavefronts when the
+      // parts still fit in one round of the (one workgroup per CU) grid
+      const int cap4 = layer_grid(k_layer_gateup<kLayerRT, kLayerNB, 16, false, 4>, 4);
+      const int cap2 = layer_grid(k_layer_gateup<kLayerRT, kLayerNB, 16, false, 2>, 5);
+      if (G >= 8 && items * 4 <= (int64_t)cap4 * 8)
+        launch_layer_gateup(k_layer_gateup<kLayerRT, kLayerNB, 16, false, 4>, 4, f, r, h,
+                            std::max<int64_t>(ceil_div(items * 4, 8), ceil_div((int64_t)a->T * a->E, 8)), s);
+      else if (G >= 4 && items * 2 <= (int64_t)cap2 * 8)
+        launch_layer_gateup(k_layer_gateup<kLayerRT, kLayerNB, 16, false, 2>, 5, f, r, h,
+                            std::max<int64_t>(ceil_div(items * 2, 8), ceil_div((int64_t)a->T * a->E, 8)), s);
+      else
+        launch_layer_gateup(k_layer_gateup<kLayerRT, kLayerNB, 16, false, 1>, 1, f, r, h, want, s);
+    }
   } else {
-    auto kern = spec ? k_layer_gateup<kLayerRT, kLayerNB, 32, true> : k_layer_gateup<kLayerRT, kLayerNB, 32, false>;
-    const int cap = layer_grid(kern, spec ? 2 : 3);
-    hipLaunchKernelGGL(kern, dim3((unsigned)std::min<int64_t>(cap, want)), dim3(512), 0, s, f, r, h);
+    if (spec)
+      launch_layer_gateup(k_layer_gateup<kLayerRT, kLayerNB, 32, true, 1>, 2, f, r, h, want, s);
+    else
+      launch_layer_gateup(k_layer_gateup<kLayerRT, kLayerNB, 32, false, 1>, 3, f, r, h, want, s);
   }
   timing_end(K_GATEUP_DECODE, s);
   rc = check_launch("moe_decode_layer (routing + gate/up)");

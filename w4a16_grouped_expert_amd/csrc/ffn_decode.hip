@@ -1160,16 +1160,19 @@ static void launch_nb(const FfnDev& f, uint16_t* h, float* y, int ksplit, hipStr
 
 // K groups per wavefront of the fused down + combine pass: the largest of 16, 8,
 // 4 (not above G rounded up to a power of two) that still gives at least 2048
-// wavefronts, else 4; 0 if the step has too many (expert, slice) items for
-// kDcMaxChunks workgroups per stripe.
+// wavefronts, else 4, or 2 when 4 leaves fewer than 2048; 0 if the step has too
+// many (expert, slice) items for kDcMaxChunks workgroups per stripe.
 int dc_units_per_wave(int umax, int G, int stripes) {
+  auto fits = [&](int u) { return (int64_t)umax * ((G + u - 1) / u) <= (int64_t)kDcMaxChunks * kDcWaves; };
+  auto waves = [&](int u) { return (int64_t)umax * ((G + u - 1) / u) * stripes; };
   int upw = 4;
   for (int u = 16; u > 4; u /= 2)
-    if (u / 2 < G && (int64_t)umax * ((G + u - 1) / u) * stripes >= 2048) {
+    if (u / 2 < G && waves(u) >= 2048) {
       upw = u;
       break;
     }
-  return (int64_t)umax * ((G + upw - 1) / upw) <= (int64_t)kDcMaxChunks * kDcWaves ? upw : 0;
+  if (upw == 4 && waves(4) < 2048 && G > 2 && fits(2)) upw = 2;  // few items: shorter runs, more of them
+  return fits(upw) ? upw : 0;
 }
 
 template <int UPW, bool SPEC>
@@ -1194,7 +1197,10 @@ void launch_down_combine(const FfnDev& f, const uint16_t* h, uint16_t* out, floa
   // every expert in id order when the step routes at least one pair per expert
   // on average (umax == E then), else the active experts
   const bool spec = (int64_t)f.T * f.k >= f.E;
-  if (upw <= 4) {
+  if (upw <= 2) {
+    if (spec) launch_dc<2, true>(f, h, out, part, counters, route_ctr, n_route_ctr, s, pair, grid);
+    else launch_dc<2, false>(f, h, out, part, counters, route_ctr, n_route_ctr, s, pair, grid);
+  } else if (upw <= 4) {
     if (spec) launch_dc<4, true>(f, h, out, part, counters, route_ctr, n_route_ctr, s, pair, grid);
     else launch_dc<4, false>(f, h, out, part, counters, route_ctr, n_route_ctr, s, pair, grid);
   } else if (upw <= 8) {

@@ -382,164 +382,6 @@ __global__ __launch_bounds__(512, 4) void k_gateup_dense(FfnDev f, uint16_t* __r
   }
 }
 
-// The same gate/up pass with each item's groups in straight-line chunks of CH:
-// within a chunk the loads of group i + D go out before group i is multiplied,
-// fully unrolled with scheduling barriers, so every wait is exact and no
-// register that a load in flight will write is ever moved; the weight pointers
-// are wave-uniform buffer resources.  Groups past G (G not a multiple of CH)
-// repeat group G - 1's loads with weight 0.
-template <int RT, int D, int CH, int MAXG>
-__global__ __launch_bounds__(512, 4) void k_gateup_line(FfnDev f, uint16_t* __restrict__ hout) {
-  zero_down_counters(f);
-  constexpr int kWaves = 8;
-  const int G = f.d / kGroup;
-  const int n_stripes = 2 * f.I / (kTileRows * RT);
-  const int n_items = f.umax * n_stripes;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = lane_id();
-  const int col = lane & 15, kq = lane >> 4;
-  const int worker = blockIdx.x * kWaves + wave, n_workers = gridDim.x * kWaves;
-  const i32x4_t* work = reinterpret_cast<const i32x4_t*>(f.active + 4);
-  const int U = f.active[0];
-
-  struct Buf {
-    u32x4_t c[RT];
-    u32x2_t s[RT];
-  };
-  Buf buf[D + 1];
-  __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc((void*)f.bank, (short)0, 0, kBufferRsrcWord3);
-  uint32_t soff_c = 0, soff_s = 0;
-  const uint32_t voff_c = 16u * lane, voff_s = 8u * kq;
-  auto load = [&](Buf& b, int g) {
-    const int gl = min(g, G - 1);
-#pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      b.c[r] = __builtin_bit_cast(
-          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wres, voff_c, soff_c + (uint32_t)(r * G + gl) * kTileBytes,
-                                                         kCacheNonTemporal));
-      b.s[r] = __builtin_bit_cast(
-          u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(wres, voff_s, soff_s + (uint32_t)(r * G + gl) * kTileRows * 2,
-                                                        0));
-    }
-  };
-  // Item setup: its record, its weight resource and the loads of its first D
-  // groups.  Returns the expert (-1: no item left for this worker).
-  int item = worker, row0 = 0;
-  i32x4_t w4 = work[min(item / n_stripes, f.umax - 1)];
-  auto start_item = [&]() -> int {
-    for (; item < n_items; item += n_workers) {
-      const i32x4_t cur = w4;
-      w4 = work[min((item + n_workers) / n_stripes, f.umax - 1)];  // next record, in flight now
-      if (item / n_stripes >= U) break;  // items are visited in increasing u: nothing active remains
-      const uint8_t* blob = f.blob(cur[0]);
-      if (!blob) continue;
-      const int stripe = item % n_stripes;
-      wres = __builtin_amdgcn_make_buffer_rsrc((void*)blob, (short)0, 0x7FFFFFFF, kBufferRsrcWord3);
-      soff_c = (uint32_t)(f.off_w13_codes + (int64_t)(RT * stripe) * G * kTileBytes);
-      soff_s = (uint32_t)(f.off_w13_scales + (int64_t)(RT * stripe) * G * kTileRows * 2);
-#pragma unroll
-      for (int j = 0; j < D; ++j) load(buf[j], j);
-      row0 = cur[1];
-      return cur[0];
-    }
-    item = n_items;
-    return -1;
-  };
-  int e = start_item();
-
-  __shared__ u32x4_t s_x[MAXG * 4 * 64];
-  __shared__ float s_xs[MAXG * 16];
-  __shared__ int s_ids[16][MOE_MAX_TOPK];
-  {
-    const u32x4_t ones_w = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-    const bf16x8_t ones = as_bf16x8(ones_w);
-    const __amdgpu_buffer_rsrc_t xres =
-        __builtin_amdgcn_make_buffer_rsrc((void*)f.x, (short)0, (int)(f.T * f.d * 2), kBufferRsrcWord3);
-    const uint32_t xoff = (uint32_t)(col * f.d + 8 * kq) * 2u;
-    for (int g = wave; g < G; g += kWaves) {
-      u32x4_t xv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        xv[i] = __builtin_bit_cast(
-            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xres, xoff + (uint32_t)(g * kGroup + 32 * i) * 2u, 0, 0));
-      f32x4_t as = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s_x[(4 * g + i) * 64 + lane] = xv[i];
-        as = mfma16x16x32(ones, as_bf16x8(xv[i]), as);
-      }
-      if (lane < 16) s_xs[g * 16 + lane] = as[0];  // C column = lane, every row the same sum
-    }
-    for (int i = threadIdx.x; i < 16 * MOE_MAX_TOPK; i += kWaves * 64) {
-      const int t = i / MOE_MAX_TOPK, j = i % MOE_MAX_TOPK;
-      s_ids[t][j] = (j < f.k && t < f.T) ? f.topk_ids[t * f.k + j] : -1;
-    }
-  }
-  __syncthreads();
-  const uint32_t kMask = vgpr_const(0x00780078u), kOne = vgpr_const(0x3F803F80u);
-
-  while (e >= 0) {
-    const int cur_stripe = item % n_stripes;
-    bool routed = false;
-    for (int j = 0; j < f.k; ++j) routed |= (s_ids[col][j] == e);
-    const uint32_t colmask = (uint32_t)__ballot(routed) & 0xFFFFu;
-    const int out_row = row0 + __popc(colmask & ((1u << col) - 1u));
-
-    f32x4_t tot[RT];
-#pragma unroll
-    for (int r = 0; r < RT; ++r) tot[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    auto compute = [&](const Buf& b, int g) {
-      const int gl = min(g, G - 1);
-      const float gv = g < G ? 1.f : 0.f;
-      const float xs = -24.f * s_xs[gl * 16 + col];
-      f32x4_t acc[RT];
-#pragma unroll
-      for (int r = 0; r < RT; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bf16x8_t xv = as_bf16x8(s_x[(4 * gl + i) * 64 + lane]);
-#pragma unroll
-        for (int r = 0; r < RT; ++r)
-          acc[r] = mfma16x16x32(as_bf16x8(decode_word_biased(b.c[r][i], kMask, kOne)), xv, acc[r]);
-      }
-#pragma unroll
-      for (int r = 0; r < RT; ++r) {
-        const float s4[4] = {__uint_as_float(b.s[r][0] << 16), __uint_as_float(b.s[r][0] & 0xFFFF0000u),
-                             __uint_as_float(b.s[r][1] << 16), __uint_as_float(b.s[r][1] & 0xFFFF0000u)};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) tot[r][q] = fmaf(gv * s4[q], fmaf(16.f, acc[r][q], xs), tot[r][q]);
-      }
-    };
-    for (int gc = 0; gc < G; gc += CH) {
-      if (gc > 0) {
-#pragma unroll
-        for (int j = 0; j < D; ++j) load(buf[j], gc + j);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < CH; ++i) {
-        if (i + D < CH) load(buf[(i + D) % (D + 1)], gc + i + D);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(buf[i % (D + 1)], gc + i);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    // the next item's first loads go out before this item's stores
-    item += n_workers;
-    e = start_item();
-#pragma unroll
-    for (int p = 0; p < RT / 2; ++p) {
-      uint32_t hv[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) hv[q] = f32_to_bf16_bits(silu_f32(tot[2 * p][q]) * tot[2 * p + 1][q]);
-      if (routed) {
-        const int hcol = kTileRows * ((RT / 2) * cur_stripe + p) + 4 * kq;
-        u32x2_t o = {hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16)};
-        *reinterpret_cast<u32x2_t*>(hout + (int64_t)out_row * f.I + hcol) = o;
-      }
-    }
-  }
-}
-
 // The same gate/up pass with each stripe's K range split over a pair of
 // wavefronts of the workgroup, for steps with few active experts (few stripes):
 // twice the wavefronts stream weights.  Wavefront w works on stripe slot w % 4 of
@@ -1116,7 +958,6 @@ __global__ __launch_bounds__(256) void k_ffn_decode(FfnDev f, const uint16_t* __
 constexpr int kGateUpRT = 2, kDownRT = 4;
 constexpr int kPersistRT = 4, kPersistNG = 8, kRingRT = 2, kRingNG = 4;
 constexpr int kDenseRT = 2, kDenseNB = 4;  // LDS-activation gate/up: tiles per stripe, ring depth
-constexpr int kLineD = 3;                   // straight-line gate/up: groups in flight ahead
 // fused down + combine: tiles per stripe, prefetch distance in units, wavefronts
 // per workgroup and resident wavefronts per SIMD
 constexpr int kDcRT = 2, kDcD = 2, kDcWaves = 8, kDcOcc = 4;
@@ -1244,14 +1085,6 @@ int launch_decode(const FfnDev& f_in, uint16_t* h, float* y, int ksplit, int nb,
         auto kks = G <= 16 ? k_gateup_dense_ks2<kDenseRT, kDenseNB, 16> : k_gateup_dense_ks2<kDenseRT, kDenseNB, 32>;
         const int64_t grid_ks = std::min<int64_t>(persistent_grid(kks, G <= 16 ? 6 : 7, 512), ceil_div(items_gu, 4));
         hipLaunchKernelGGL(kks, dim3((unsigned)grid_ks), dim3(512), 0, s, f, h);
-      } else if (f.bank_stride < ((int64_t)1 << 31)) {
-        // straight-line group chunks of 16 (8, 4 for smaller d)
-        auto kln = G > 8 ? (G <= 16 ? k_gateup_line<kDenseRT, kLineD, 16, 16> : k_gateup_line<kDenseRT, kLineD, 16, 32>)
-                         : (G > 4 ? k_gateup_line<kDenseRT, kLineD, 8, 16> : k_gateup_line<kDenseRT, kLineD, 4, 16>);
-        const int slot = G > 16 ? 8 : (G > 8 ? 9 : (G > 4 ? 10 : 11));
-        const int64_t cap_ln = persistent_grid(kln, slot, 512);
-        hipLaunchKernelGGL(kln, dim3((unsigned)std::min<int64_t>(cap_ln, ceil_div(items_gu, 8))), dim3(512), 0, s, f,
-                           h);
       } else {
         hipLaunchKernelGGL(kgu, dim3((unsigned)std::min<int64_t>(cap, ceil_div(items_gu, 8))), dim3(512), 0, s, f, h);
       }

@@ -13,10 +13,13 @@
 // (token, expert) dot product per wavefront, with the arithmetic of moe_route
 // (float64 sums of the exact bf16 products, rounded once); the wavefront that
 // completes a token's logits selects its top-k and weights and publishes the
-// ids in a ready table, and the workgroups stage their activations in LDS, then
-// wait (a bounded poll of the ready table) until every pair is routed.  The gate/up items then run as in
-// the grouped decode pass, h going to rows in pair order (t * k + j): no
-// expert-sorted permutation is needed when every MFMA column is a token.  The
+// ids in a ready table, and the workgroups stage their activations in LDS.  The
+// gate/up items run as in the grouped decode pass, h going to rows in pair order
+// (t * k + j): no expert-sorted permutation is needed when every MFMA column is a
+// token.  Items over every expert do not depend on the routing, so a workgroup
+// waits for it (a bounded poll of the ready table) only before its first h
+// store, and skips the items of experts without pairs after that; items over
+// the active experts wait for it before the first item.  The
 // second launch is the fused down + combine pass, which builds the active
 // expert list from the routing table itself.  Routing results are bit-identical
 // to moe_route_align; the arithmetic of every gate/up item and of the down pass
@@ -308,11 +311,13 @@ __global__ __launch_bounds__(512, 4) void k_layer_gateup(FfnDev f, RouteDev r, u
     }
   }
 
-  // 4. wait until every token is routed: wavefront 0 polls the ready table
-  //    until every pair's entry is set (bounded: a timeout is flagged in the
-  //    counters and the pass goes on with whatever the table holds), and
-  //    leaves the routing table in LDS
-  if (wave == 0) {
+  // 4. the routing table in LDS: wavefront 0 polls the ready table until every
+  //    pair's entry is set (bounded: a timeout is flagged in the counters and the
+  //    pass goes on with whatever the table holds).  SPEC: items do not depend on
+  //    the routing, so the wait moves to the first h store (below); s_routed
+  //    tells the other wavefronts that s_ids and s_mask are filled.
+  __shared__ int s_routed;
+  auto read_routing = [&]() {
     const int n = T * k;  // <= 256: at most 4 entries per lane
     int id[4];
     int spins = 0;
@@ -344,10 +349,32 @@ __global__ __launch_bounds__(512, 4) void k_layer_gateup(FfnDev f, RouteDev r, u
       const int i = lane + 64 * m;
       if (i < n) s_ids[i / k][i % k] = id[m] - 1;
     }
-  }
+    if (SPEC) {
+      for (int i = lane; i < MOE_MAX_EXPERTS / 32; i += 64) s_mask[i] = 0u;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int i = lane + 64 * m, ex = id[m] - 1;
+        if (i < n && ex >= 0 && ex < E) atomicOr(&s_mask[ex >> 5], 1u << (ex & 31));
+      }
+    }
+  };
+  // SPEC: wavefront 0 publishes the routing table; the others wait for it (bounded)
+  auto await_routing = [&]() {
+    if (wave == 0) {
+      read_routing();
+      __hip_atomic_store(&s_routed, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    } else {
+      for (int spins = 0; __hip_atomic_load(&s_routed, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0 &&
+                          spins < kSpinLimit;
+           ++spins)
+        __builtin_amdgcn_s_sleep(2);
+    }
+  };
+  if (!SPEC && wave == 0) read_routing();
+  if (SPEC && threadIdx.x == 0) s_routed = 0;
   __syncthreads();
-  const int U = build_active(s_ids, T, k, E, s_mask, SPEC ? nullptr : s_act, &s_u);
-  const int n_items = (SPEC ? E : U) * n_stripes;
+  const int U = SPEC ? E : build_active(s_ids, T, k, E, s_mask, s_act, &s_u);
+  const int n_items = U * n_stripes;
 
   // 5. gate/up items
   const uint32_t kMask = vgpr_const(0x00780078u), kOne = vgpr_const(0x3F803F80u);
@@ -434,11 +461,14 @@ __global__ __launch_bounds__(512, 4) void k_layer_gateup(FfnDev f, RouteDev r, u
       __syncthreads();  // s_part is free for the next round
     }
   } else {
+    // SPEC: an item is skipped for an expert without pairs once the routing is
+    // known; the items before the first store run whatever their expert
+    bool routed = !SPEC;
     auto start_item = [&](bool have_loads) -> int {
       for (; item < n_items; item += n_workers) {
         const int u = item / n_stripes;
         const int e = SPEC ? u : s_act[u];
-        if (SPEC && !((s_mask[e >> 5] >> (e & 31)) & 1u)) {
+        if (SPEC && routed && !((s_mask[e >> 5] >> (e & 31)) & 1u)) {
           have_loads = false;  // an expert without pairs: nothing to compute
           continue;
         }
@@ -466,9 +496,14 @@ __global__ __launch_bounds__(512, 4) void k_layer_gateup(FfnDev f, RouteDev r, u
       }
       // the next item's first loads go out before this item's stores
       item += n_workers;
+      if (!routed) {
+        await_routing();
+        routed = true;
+      }
       e = start_item(false);
       store_h(tot, cur_e, stripe);
     }
+    if (!routed && wave == 0) await_routing();  // the other wavefronts may wait for the table
   }
 }
 

@@ -180,24 +180,41 @@ __global__ __launch_bounds__(kPThreads) void k_prefill(
 
   const uint32_t kMask = vgpr_const(0x00780078u), kOne = vgpr_const(0x3F803F80u);
 
-  for (int tile = vb; tile < total; tile += nblk) {
-    int lo = 0, hi = U;  // s_pref[lo] <= tile < s_pref[hi]
+  auto active_of = [&](int t) {  // the active expert u with s_pref[u] <= t < s_pref[u + 1]
+    int lo = 0, hi = U;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (s_pref[mid] <= tile) lo = mid; else hi = mid;
+      if (s_pref[mid] <= t) lo = mid; else hi = mid;
     }
-    const int u = lo;
-    const i32x4_t w4 = work[u];
+    return lo;
+  };
+  // The next tile's work record is requested at the start of a tile and (gate/up)
+  // its gathered token ids at the start of the tile's last group, so that neither
+  // round trip waits at the next tile's start.
+  int tile = vb;
+  int un = tile < total ? active_of(tile) : 0;
+  i32x4_t w4n = tile < total ? work[un] : i32x4_t{0, 0, 0, 0};
+  int pair_next = 0, pair_tile = -1;  // thread tid < kPBM: sorted_pairs entry of its row in tile pair_tile
+  for (; tile < total; tile += nblk) {
+    const int u = un;
+    const i32x4_t w4 = w4n;
     const int e = w4[0], row0 = w4[1], n_e = w4[2];
     const int local = tile - s_pref[u];
     const int mt = local / NT, nt = local % NT;  // row tiles fastest: neighbours share the token tile
+    const int next = tile + nblk;
+    if (next < total) {
+      un = active_of(next);
+      w4n = work[un];
+    }
     const uint8_t* blob = f.blob(e);
     if (!blob) continue;  // uniform over the block
 
     __syncthreads();  // the previous tile is done with every LDS buffer
     if (tid < kPBM) {
       const int r = mt * kPBM + tid;
-      s_row[tid] = r < n_e ? (GATEUP ? f.sorted_pairs[row0 + r] / f.k : row0 + r) : -1;
+      int row = -1;
+      if (r < n_e) row = GATEUP ? (pair_tile == tile ? pair_next : f.sorted_pairs[row0 + r]) / f.k : row0 + r;
+      s_row[tid] = row;
     }
     __syncthreads();
 
@@ -282,14 +299,29 @@ __global__ __launch_bounds__(kPThreads) void k_prefill(
     f32x4_t rn[4];       // this lane's ratios for the next group
     f32x4_t xsn;         // this lane's group sums for the next group
 
-    // prologue: scales of groups 0, 1 and the group sums of group 0, then batches 0, 1
+    // prologue: scales of groups 0, 1 and the group sums of group 0, then batches 0
+    // and 1 at once; wavefronts 0 and 1 wait for their prologue loads only (older
+    // than the batches, which may stay in flight)
     if (wave == 0) {
       issue_aux(0);
       if (G > 1) issue_aux(1);
     } else if (wave == 1) {
       issue_aux(0);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int part = 0; part < 4; ++part) issue_part(0, part);
+    if (G > 1) {
+#pragma unroll
+      for (int part = 0; part < 4; ++part) issue_part(1, part);
+    }
+    if (wave < 2) {
+      const int n_after = 6 + (batch_has_aux(0) ? 2 : 0) + (G > 1 ? 6 + (batch_has_aux(1) ? 2 : 0) : 0);
+      if (n_after == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+      else if (n_after == 14) asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
+      else if (n_after == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+      else if (n_after == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     __syncthreads();
     if (tid < kPBN) {
       const float s0 = bf16_at(s_sc[0][tid]);
@@ -305,12 +337,6 @@ __global__ __launch_bounds__(kPThreads) void k_prefill(
       }
       s_ratio[1][tid] = out;
     }
-#pragma unroll
-    for (int part = 0; part < 4; ++part) issue_part(0, part);
-    if (G > 1) {
-#pragma unroll
-      for (int part = 0; part < 4; ++part) issue_part(1, part);
-    }
 
     for (int g = 0; g < G; ++g) {
       // batch g has landed (batch g + 1 may still be in flight); everyone is done with stage g - 1
@@ -318,6 +344,11 @@ __global__ __launch_bounds__(kPThreads) void k_prefill(
         if (batch_has_aux(g + 1)) stage_wait_barrier<8>(); else stage_wait_barrier<6>();
       } else {
         stage_wait_barrier<0>();
+      }
+      if (GATEUP && g == G - 1 && next < total && tid < kPBM) {
+        const int rn = ((next - s_pref[un]) / NT) * kPBM + tid;
+        if (rn < w4n[2]) pair_next = f.sorted_pairs[w4n[1] + rn];
+        pair_tile = next;
       }
       // Row tid's ratio two groups ahead (16 e_last once that is past the end).
       if (tid < kPBN && g + 2 <= G) {

@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kPThreads) void k_prefill(
   __shared__ float s_xs[4][kPBM];      // group sums of group g at [g % 4]: token 64 h + 16 b + c at [64 h + 4 c + b]
   __shared__ uint16_t s_sc[4][kPBN];   // bf16 scales of group g at [g % 4], row r of the block tile at [r]
   __shared__ float s_ratio[2][kPBN];   // e_{g-1} / e_g per row at [g % 2]; 16 e_last at [G % 2]
-  __shared__ int s_row[kPBM];          // activation row (token for gate/up, sorted position for down), -1 = none
+  __shared__ int s_row[2][kPBM];       // activation rows of this tile and the next (see fill_rows)
   __shared__ int s_pref[MOE_MAX_EXPERTS + 1];
   __shared__ float s_hs[4][kPBM];      // gate/up: per-token h sums of each row quarter's 32 columns
   __shared__ int s_wsum[kPWaves];
@@ -188,132 +188,171 @@ __global__ __launch_bounds__(kPThreads) void k_prefill(
     }
     return lo;
   };
-  // The next tile's work record is requested at the start of a tile and (gate/up)
-  // its gathered token ids at the start of the tile's last group, so that neither
-  // round trip waits at the next tile's start.
-  int tile = vb;
-  int un = tile < total ? active_of(tile) : 0;
-  i32x4_t w4n = tile < total ? work[un] : i32x4_t{0, 0, 0, 0};
-  int pair_next = 0, pair_tile = -1;  // thread tid < kPBM: sorted_pairs entry of its row in tile pair_tile
-  for (; tile < total; tile += nblk) {
-    const int u = un;
-    const i32x4_t w4 = w4n;
-    const int e = w4[0], row0 = w4[1], n_e = w4[2];
-    const int local = tile - s_pref[u];
-    const int mt = local / NT, nt = local % NT;  // row tiles fastest: neighbours share the token tile
-    const int next = tile + nblk;
-    if (next < total) {
-      un = active_of(next);
-      w4n = work[un];
-    }
-    const uint8_t* blob = f.blob(e);
-    if (!blob) continue;  // uniform over the block
-
-    __syncthreads();  // the previous tile is done with every LDS buffer
+  struct Tile {
+    int row0, n_e, mt, nt;
+    const uint8_t* blob;
+  };
+  auto tile_of = [&](int t, int u, const i32x4_t& w) {
+    Tile tl;
+    tl.row0 = w[1];
+    tl.n_e = w[2];
+    const int local = t - s_pref[u];
+    tl.mt = local / NT;  // row tiles fastest: neighbours share the token tile
+    tl.nt = local % NT;
+    tl.blob = f.blob(w[0]);
+    return tl;
+  };
+  // activation row of each of the tile's tokens (token for gate/up, sorted position
+  // for down), -1 = none; thread tid < kPBM fills row tid
+  auto fill_rows = [&](const Tile& tl, int* rows, int pair_val, bool have_pair) {
     if (tid < kPBM) {
-      const int r = mt * kPBM + tid;
+      const int r = tl.mt * kPBM + tid;
       int row = -1;
-      if (r < n_e) row = GATEUP ? (pair_tile == tile ? pair_next : f.sorted_pairs[row0 + r]) / f.k : row0 + r;
-      s_row[tid] = row;
+      if (r < tl.n_e) row = GATEUP ? (have_pair ? pair_val : f.sorted_pairs[tl.row0 + r]) / f.k : tl.row0 + r;
+      rows[tid] = row;
     }
-    __syncthreads();
+  };
 
-    // ---- this lane's DMA sources for the tile (group 0; group g adds g * stride)
-    // Activations: instruction j of wavefront w fills slots s = 64 (4 w + j) + lane,
-    // i.e. chunk (s % 16) ^ (t % 16) of token t = s / 16.  Rows are gathered tokens
-    // for gate/up (byte offsets from x, below 4 GiB by the host check) and
-    // consecutive sorted positions for down (offsets from the tile's first row);
-    // padding tokens read the tile's first row and their outputs are dropped.
-    const uint8_t* act_tile = reinterpret_cast<const uint8_t*>(GATEUP ? act : act + (int64_t)(row0 + mt * kPBM) * K);
-    const i32x4_t rs_x = raw_rsrc(act_tile);
-    uint32_t xoff[4];
+  // ---- this lane's DMA sources for a tile (group 0; group g adds g * stride)
+  // Activations: instruction j of wavefront w fills slots s = 64 (4 w + j) + lane,
+  // i.e. chunk (s % 16) ^ (t % 16) of token t = s / 16.  Rows are gathered tokens
+  // for gate/up (byte offsets from x, below 4 GiB by the host check) and
+  // consecutive sorted positions for down (offsets from the tile's first row);
+  // padding tokens read the tile's first row and their outputs are dropped.
+  // Weights: instruction j of wavefront w fills packed tile 2 w + j.  A last row
+  // tile past N reads the final packed tile in place of the missing ones (those
+  // rows are computed but not stored).
+  // Scales (wavefront 0, two 4-byte instructions): word p = 64 j + lane holds rows
+  // 2 (p % 8), + 1 of tile p / 8.  Group sums (wavefront 1, two instructions):
+  // slot p = 64 j + lane holds token 64 j + 16 (p % 4) + (p % 64) / 4.
+  const int last_tile = N / kTileRows - 1;
+  uint32_t xoff[4], woff[2], aoff[2] = {0u, 0u};
+  uint32_t astep = 0;  // bytes per group
+  i32x4_t rs_x, rs_w, rs_a;
+  auto setup_dma = [&](const Tile& tl, const int* rows) {
+    const uint8_t* act_tile =
+        reinterpret_cast<const uint8_t*>(GATEUP ? act : act + (int64_t)(tl.row0 + tl.mt * kPBM) * K);
+    rs_x = raw_rsrc(act_tile);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int sl = (wave * 4 + j) * 64 + lane;
       const int t = sl >> 4, kc = (sl & 15) ^ (t & 15);
       int row;
-      if (GATEUP) row = s_row[t] >= 0 ? s_row[t] : s_row[0];
-      else row = s_row[t] >= 0 ? t : 0;
+      if (GATEUP) row = rows[t] >= 0 ? rows[t] : rows[0];
+      else row = rows[t] >= 0 ? t : 0;
       xoff[j] = ((uint32_t)row * (uint32_t)K + 8u * (uint32_t)kc) * 2u;
     }
-    // Weights: instruction j of wavefront w fills packed tile 2 w + j.  A last row
-    // tile past N reads the final packed tile in place of the missing ones (those
-    // rows are computed but not stored).
-    const int last_tile = N / kTileRows - 1;
-    const i32x4_t rs_w = raw_rsrc(blob + (GATEUP ? f.off_w13_codes : f.off_w2_codes));
-    uint32_t woff[2];
+    rs_w = raw_rsrc(tl.blob + (GATEUP ? f.off_w13_codes : f.off_w2_codes));
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      woff[j] = (uint32_t)min(nt * kPTiles + 2 * wave + j, last_tile) * (uint32_t)(G * kTileBytes) + 16u * lane;
-    // Scales (wavefront 0, two 4-byte instructions): word p = 64 j + lane holds rows
-    // 2 (p % 8), + 1 of tile p / 8.  Group sums (wavefront 1, two instructions):
-    // slot p = 64 j + lane holds token 64 j + 16 (p % 4) + (p % 64) / 4.
-    const i32x4_t rs_a = raw_rsrc(wave == 0 ? (const void*)(blob + (GATEUP ? f.off_w13_scales : f.off_w2_scales))
-                                            : (const void*)asum);
-    uint32_t aoff[2] = {0u, 0u};
-    uint32_t astep = 0;  // bytes per group
+      woff[j] = (uint32_t)min(tl.nt * kPTiles + 2 * wave + j, last_tile) * (uint32_t)(G * kTileBytes) + 16u * lane;
+    rs_a = raw_rsrc(wave == 0 ? (const void*)(tl.blob + (GATEUP ? f.off_w13_scales : f.off_w2_scales))
+                              : (const void*)asum);
     if (wave == 0) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int p = 64 * j + lane;
-        aoff[j] = ((uint32_t)min(nt * kPTiles + (p >> 3), last_tile) * (uint32_t)(G * kTileRows) + 2u * (p & 7)) * 2u;
+        aoff[j] = ((uint32_t)min(tl.nt * kPTiles + (p >> 3), last_tile) * (uint32_t)(G * kTileRows) + 2u * (p & 7)) * 2u;
       }
       astep = kTileRows * 2;
     } else if (wave == 1) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int t = 64 * j + 16 * (lane & 3) + (lane >> 2);
-        const int r = s_row[t] >= 0 ? s_row[t] : s_row[0];
+        const int r = rows[t] >= 0 ? rows[t] : rows[0];
         aoff[j] = (uint32_t)r * (uint32_t)(GATEUP ? G : GH) * 4u;
       }
       astep = 4;
     }
-    auto issue_aux = [&](int g) {  // scales (wave 0) or group sums (wave 1) of group g
-      if (wave == 0) {
+  };
+  // The LDS rings are indexed by a running group count q = qb + g (mod 12: rings
+  // of 2, 3 and 4), so a tile's first batches can land while the previous tile
+  // still reads its last stage.
+  auto issue_aux = [&](int g, int qbase) {  // scales (wave 0) or group sums (wave 1) of group g
+    if (wave == 0) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) buf_dma4(rs_a, aoff[j], (uint32_t)g * astep, lds_addr(&s_sc[g & 3][128 * j]));
-      } else {
+      for (int j = 0; j < 2; ++j)
+        buf_dma4(rs_a, aoff[j], (uint32_t)g * astep, lds_addr(&s_sc[(qbase + g) & 3][128 * j]));
+    } else {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) buf_dma4(rs_a, aoff[j], (uint32_t)g * astep, lds_addr(&s_xs[g & 3][64 * j]));
-      }
-    };
-    // Part `part` (0..3) of batch k: one activation instruction, a weight
-    // instruction on parts 0 and 2, the scales / group sums on part 1.
-    auto issue_part = [&](int k, int part) {
-      PrefillStage& S = st[k % kStages];
-      buf_dma16(rs_x, xoff[part], (uint32_t)k * (kGroup * 2), lds_addr(&S.x[(wave * 4 + part) * 64]));
-      if ((part & 1) == 0)
-        buf_dma16(rs_w, woff[part >> 1], (uint32_t)k * kTileBytes, lds_addr(&S.w[(wave * 2 + (part >> 1)) * 64]));
-      if (part == 1) {
-        if (wave == 0 && k + 2 < G) issue_aux(k + 2);
-        if (wave == 1 && k + 1 < G) issue_aux(k + 1);
-      }
-    };
-    auto bf16_at = [](uint16_t b) { return __uint_as_float((uint32_t)b << 16); };
-    // DMA instructions of this wavefront in batch k (6, plus two for the scales /
-    // group sums it carries)
-    auto batch_has_aux = [&](int k) { return (wave == 0 && k + 2 < G) || (wave == 1 && k + 1 < G); };
+      for (int j = 0; j < 2; ++j)
+        buf_dma4(rs_a, aoff[j], (uint32_t)g * astep, lds_addr(&s_xs[(qbase + g) & 3][64 * j]));
+    }
+  };
+  // Part `part` (0..3) of batch k: one activation instruction, a weight
+  // instruction on parts 0 and 2, the scales / group sums on part 1.
+  auto issue_part = [&](int k, int part, int qbase) {
+    PrefillStage& S = st[(qbase + k) % kStages];
+    buf_dma16(rs_x, xoff[part], (uint32_t)k * (kGroup * 2), lds_addr(&S.x[(wave * 4 + part) * 64]));
+    if ((part & 1) == 0)
+      buf_dma16(rs_w, woff[part >> 1], (uint32_t)k * kTileBytes, lds_addr(&S.w[(wave * 2 + (part >> 1)) * 64]));
+    if (part == 1) {
+      if (wave == 0 && k + 2 < G) issue_aux(k + 2, qbase);
+      if (wave == 1 && k + 1 < G) issue_aux(k + 1, qbase);
+    }
+  };
+  // DMA instructions of this wavefront in batch k (6, plus two for the scales /
+  // group sums it carries)
+  auto batch_has_aux = [&](int k) { return (wave == 0 && k + 2 < G) || (wave == 1 && k + 1 < G); };
+  // prologue DMA of a tile: scales of groups 0, 1 and the group sums of group 0,
+  // then batches 0 and 1
+  auto issue_prologue = [&](int qbase) {
+    if (wave == 0) {
+      issue_aux(0, qbase);
+      if (G > 1) issue_aux(1, qbase);
+    } else if (wave == 1) {
+      issue_aux(0, qbase);
+    }
+#pragma unroll
+    for (int part = 0; part < 4; ++part) issue_part(0, part, qbase);
+    if (G > 1) {
+#pragma unroll
+      for (int part = 0; part < 4; ++part) issue_part(1, part, qbase);
+    }
+  };
+  auto bf16_at = [](uint16_t b) { return __uint_as_float((uint32_t)b << 16); };
+
+  // The next tile's work record is requested at the start of a tile and (gate/up)
+  // its gathered token ids at the top of the tile's second-to-last group.  Down
+  // pass with G >= 4: the next tile's rows, DMA sources and prologue DMA are set
+  // up at the top of the last group, so those round trips overlap the last group
+  // and the epilogue (measured: 5 % off the down pass; the gate/up pass, whose
+  // last group and epilogue carry more work, ran 3 % slower with it).
+  int tile = vb;
+  int un = tile < total ? active_of(tile) : 0;
+  i32x4_t w4n = tile < total ? work[un] : i32x4_t{0, 0, 0, 0};
+  int pair_next = 0, pair_tile = -1;  // thread tid < kPBM: sorted_pairs entry of its row in tile pair_tile
+  bool ready = false;                 // this tile's setup and prologue DMA went out during the previous tile
+  int qb = 0, rb = 0;                 // running group count (mod 12), this tile's s_row buffer
+  for (; tile < total; tile += nblk) {
+    const int u = un;
+    const Tile cur = tile_of(tile, u, w4n);
+    const int row0 = cur.row0, n_e = cur.n_e, mt = cur.mt, nt = cur.nt;
+    const int next = tile + nblk;
+    if (next < total) {
+      un = active_of(next);
+      w4n = work[un];
+    }
+    if (!cur.blob) {  // uniform over the block
+      ready = false;
+      continue;
+    }
+    if (!ready) {
+      __syncthreads();  // the previous tile is done with every LDS buffer
+      fill_rows(cur, s_row[rb], pair_next, pair_tile == tile);
+      __syncthreads();
+      setup_dma(cur, s_row[rb]);
+      issue_prologue(qb);
+    }
+    bool next_ready = false;
 
     f32x4_t acc[4][4];
     float e_next = 1.f;  // scale chain of row `tid` (threads 0 .. 255): e of the newest group seen
     f32x4_t rn[4];       // this lane's ratios for the next group
     f32x4_t xsn;         // this lane's group sums for the next group
 
-    // prologue: scales of groups 0, 1 and the group sums of group 0, then batches 0
-    // and 1 at once; wavefronts 0 and 1 wait for their prologue loads only (older
-    // than the batches, which may stay in flight)
-    if (wave == 0) {
-      issue_aux(0);
-      if (G > 1) issue_aux(1);
-    } else if (wave == 1) {
-      issue_aux(0);
-    }
-#pragma unroll
-    for (int part = 0; part < 4; ++part) issue_part(0, part);
-    if (G > 1) {
-#pragma unroll
-      for (int part = 0; part < 4; ++part) issue_part(1, part);
-    }
+    // wavefronts 0 and 1 wait for their prologue loads only: at most n_after younger
+    // operations (the batches, and any stores since) may stay in flight
     if (wave < 2) {
       const int n_after = 6 + (batch_has_aux(0) ? 2 : 0) + (G > 1 ? 6 + (batch_has_aux(1) ? 2 : 0) : 0);
       if (n_after == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
@@ -324,18 +363,18 @@ __global__ __launch_bounds__(kPThreads) void k_prefill(
     }
     __syncthreads();
     if (tid < kPBN) {
-      const float s0 = bf16_at(s_sc[0][tid]);
+      const float s0 = bf16_at(s_sc[qb & 3][tid]);
       const float e0 = s0 != 0.f ? s0 : 1.f;
       float out;
       if (G > 1) {
-        const float s1 = bf16_at(s_sc[1][tid]);
+        const float s1 = bf16_at(s_sc[(qb + 1) & 3][tid]);
         e_next = s1 != 0.f ? s1 : e0;
         out = e0 * __builtin_amdgcn_rcpf(e_next);
       } else {
         e_next = e0;
         out = 16.f * e0;
       }
-      s_ratio[1][tid] = out;
+      s_ratio[(qb + 1) & 1][tid] = out;
     }
 
     for (int g = 0; g < G; ++g) {
@@ -345,29 +384,39 @@ __global__ __launch_bounds__(kPThreads) void k_prefill(
       } else {
         stage_wait_barrier<0>();
       }
-      if (GATEUP && g == G - 1 && next < total && tid < kPBM) {
-        const int rn = ((next - s_pref[un]) / NT) * kPBM + tid;
-        if (rn < w4n[2]) pair_next = f.sorted_pairs[w4n[1] + rn];
+      if (GATEUP && g == G - 2 && next < total && tid < kPBM) {
+        const int rn_ = ((next - s_pref[un]) / NT) * kPBM + tid;
+        if (rn_ < w4n[2]) pair_next = f.sorted_pairs[w4n[1] + rn_];
         pair_tile = next;
+      }
+      if (!GATEUP && G >= 4 && g == G - 1 && next < total) {
+        const Tile nx = tile_of(next, un, w4n);
+        if (nx.blob) {  // uniform over the block
+          fill_rows(nx, s_row[rb ^ 1], pair_next, pair_tile == next);
+          __syncthreads();
+          setup_dma(nx, s_row[rb ^ 1]);
+          issue_prologue((qb + G) % 12);
+          next_ready = true;
+        }
       }
       // Row tid's ratio two groups ahead (16 e_last once that is past the end).
       if (tid < kPBN && g + 2 <= G) {
         float out;
         if (g + 2 < G) {
-          const float sn = bf16_at(s_sc[(g + 2) & 3][tid]);
+          const float sn = bf16_at(s_sc[(qb + g + 2) & 3][tid]);
           const float en = sn != 0.f ? sn : e_next;
           out = e_next * __builtin_amdgcn_rcpf(en);
           e_next = en;
         } else {
           out = 16.f * e_next;
         }
-        s_ratio[g & 1][tid] = out;
+        s_ratio[(qb + g) & 1][tid] = out;
       }
 
-      const PrefillStage& S = st[g % kStages];
+      const PrefillStage& S = st[(qb + g) % kStages];
       // acc = acc * (e_{g-1} / e_g) - 1.5 sum_k x   (acc = -1.5 sum_k x for g = 0)
       if (g == 0) {
-        const f32x4_t xs = *reinterpret_cast<const f32x4_t*>(&s_xs[0][64 * wt + 4 * col]);
+        const f32x4_t xs = *reinterpret_cast<const f32x4_t*>(&s_xs[qb & 3][64 * wt + 4 * col]);
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const float c = -1.5f * xs[b];
@@ -387,8 +436,9 @@ __global__ __launch_bounds__(kPThreads) void k_prefill(
       // the next group's ratios (written at the top of g - 1) and group sums (batch g)
       if (g + 1 < G) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) rn[t] = *reinterpret_cast<const f32x4_t*>(&s_ratio[(g + 1) & 1][64 * wr + 16 * t + 4 * kq]);
-        xsn = *reinterpret_cast<const f32x4_t*>(&s_xs[(g + 1) & 3][64 * wt + 4 * col]);
+        for (int t = 0; t < 4; ++t)
+          rn[t] = *reinterpret_cast<const f32x4_t*>(&s_ratio[(qb + g + 1) & 1][64 * wr + 16 * t + 4 * kq]);
+        xsn = *reinterpret_cast<const f32x4_t*>(&s_xs[(qb + g + 1) & 3][64 * wt + 4 * col]);
       }
 
       u32x4_t cw[4];
@@ -404,7 +454,7 @@ __global__ __launch_bounds__(kPThreads) void k_prefill(
 #pragma unroll
           for (int b = 0; b < 4; ++b) xn[b] = xrow[b * 256 + ((4 * (i + 1) + kq) ^ col)];
         }
-        if (g + 2 < G) issue_part(g + 2, i);  // spread the DMA issue over the K steps
+        if (g + 2 < G) issue_part(g + 2, i, qb);  // spread the DMA issue over the K steps
         bf16x8_t wa[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) wa[t] = as_bf16x8(decode_word_biased(cw[t][i], kMask, kOne));
@@ -420,7 +470,7 @@ __global__ __launch_bounds__(kPThreads) void k_prefill(
     }
     // 16 e_last (written at the top of G - 2, or in the prologue) is visible since the last barrier
     {
-      const float* mult = &s_ratio[G & 1][64 * wr];
+      const float* mult = &s_ratio[(qb + G) & 1][64 * wr];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const f32x4_t m = *reinterpret_cast<const f32x4_t*>(&mult[16 * t + 4 * kq]);
@@ -481,6 +531,9 @@ __global__ __launch_bounds__(kPThreads) void k_prefill(
         }
       }
     }
+    ready = next_ready;
+    qb = (qb + G) % 12;
+    rb ^= 1;
   }
 }
 

@@ -324,6 +324,31 @@ def test_slot_table_subsets_equal_resident():
     assert torch.equal(out, ref)
 
 
+def test_slot_table_subsets_equal_resident_prefill():
+    # the same in the prefill kernels, at a size where every workgroup walks several
+    # tiles and half the experts have no slot (tiles skipped between computed ones)
+    say("ffn subsets via slot table, prefill OLMoE T=1024")
+    wl = synth.OLMOE_PREFILL
+    s = wl.shape
+    T = 1024
+    w13, w2 = synth.expert_weights(wl, 3, device=DEV)
+    bank, _ = moe.pack_experts(w13, w2)
+    del w13, w2
+    wr = synth.router_weight(wl, 3).to(DEV)
+    x = synth.activations(wl, T, 3).to(DEV)
+    _, r, a = run_layer(x, wr, bank, s.I, s.k, moe.MODE_PREFILL)
+    ident = torch.arange(s.E, dtype=torch.int32, device=DEV)
+    ref = moe.moe_w4a16_grouped_ffn(x, r, a, bank, s.I, moe.MODE_PREFILL, slot_of_expert=ident)
+    ws = moe.alloc_workspace(T, s.d, s.I, s.E, s.k, moe.MODE_PREFILL)
+    out = torch.empty_like(ref)
+    half = torch.tensor([e if e % 2 == 0 else -1 for e in range(s.E)], dtype=torch.int32, device=DEV)
+    other = torch.tensor([e if e % 2 == 1 else -1 for e in range(s.E)], dtype=torch.int32, device=DEV)
+    moe.moe_w4a16_grouped_ffn_into(x, r, a, bank, s.I, out, ws, moe.MODE_PREFILL, False, half)
+    moe.moe_w4a16_grouped_ffn_into(x, r, a, bank, s.I, out, ws, moe.MODE_PREFILL, True, other)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+
+
 @pytest.mark.parametrize("T", [1, 16])
 def test_per_expert_calls_equal_fused(T):
     # the ablation's sequential variant: one grouped-FFN call per active expert (slot

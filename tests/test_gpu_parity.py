@@ -147,6 +147,39 @@ def test_align_bit_exact(T, E, k):
     check_align_gpu(ids, E, block_m=0)
 
 
+@pytest.mark.parametrize("T,E,k", [(600, 64, 8), (300, 1024, 16), (2049, 8, 2)])
+def test_align_chunked_bit_exact(T, E, k):
+    # 4096 pairs and more take the chunked kernel (one workgroup per 2048 pairs):
+    # ragged last chunk, wide ids, few experts
+    say(f"align chunked T={T} E={E} k={k}")
+    ids = synth.random_topk_ids(T, E, k, seed=7 * T + E + k).numpy()
+    check_align_gpu(ids, E, block_m=128)
+    check_align_gpu(ids, E, block_m=0)
+
+
+def test_align_chunked_edges():
+    say("align chunked edges")
+    check_align_gpu(np.full((5000, 1), 5, dtype=np.int32), 8, 128)      # one expert takes everything
+    rng = np.random.default_rng(1)
+    skew = rng.choice(4, size=(3000, 2), p=[0.7, 0.2, 0.05, 0.05])      # ragged, repeated ids per token
+    check_align_gpu(skew, 64, 64)
+    # out-of-range ids (dropped, pair_pos -1) inside several chunks: the valid pairs
+    # must sit where the oracle puts them when the dropped ones are left out
+    ids = synth.random_topk_ids(700, 64, 8, seed=3).numpy().astype(np.int32)
+    ids[::7, 3] = -1
+    ids[5, 0] = 64
+    flat = ids.reshape(-1)
+    keep = np.nonzero((flat >= 0) & (flat < 64))[0]
+    ref = oalign.align(flat[keep], 64)
+    a = moe.moe_align(torch.from_numpy(ids).to(DEV), 64, 0)
+    torch.cuda.synchronize()
+    assert np.array_equal(a.offsets.cpu().numpy(), ref["offsets"])
+    assert np.array_equal(a.sorted_pairs.cpu().numpy()[:keep.size], keep[ref["sorted_pairs"]])
+    pos = np.full(flat.size, -1, dtype=np.int64)
+    pos[keep] = ref["pair_pos"]
+    assert np.array_equal(a.pair_pos.cpu().numpy()[:flat.size], pos)
+
+
 def test_align_edges():
     say("align edges")
     check_align_gpu(np.zeros((0, 4), dtype=np.int32), 8, 16)            # empty

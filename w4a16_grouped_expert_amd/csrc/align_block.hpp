@@ -58,10 +58,12 @@ __device__ __forceinline__ LaneGroup lane_group(int e, bool valid, int id_bits, 
 
 // Block-wide scan over the experts (one per thread, E <= kAlignThreads) of the
 // pair counts: offsets, the compacted work list of active experts and the
-// per-expert tile counts.  Every thread must call it (it synchronises when E > 64).
+// per-expert tile counts (written only when publish is set; s_off always).  Every
+// thread must call it (it synchronises when E > 64).
 __device__ __forceinline__ void align_scan(int c, int E, int block_m, int tid, int lane, int wave,
                                            int32_t* __restrict__ s_off, int32_t* __restrict__ offsets,
-                                           int32_t* __restrict__ active, int32_t* __restrict__ tile_offsets) {
+                                           int32_t* __restrict__ active, int32_t* __restrict__ tile_offsets,
+                                           bool publish = true) {
   __shared__ int s_tot[3][kAlignWaves];
   const int a = c > 0 ? 1 : 0;
   const int tl = (block_m > 0) ? (c + block_m - 1) / block_m : 0;
@@ -83,6 +85,8 @@ __device__ __forceinline__ void align_scan(int c, int E, int block_m, int tid, i
   const int ex_c = bc + ic - c, ex_a = ba + ia - a, ex_t = bt + it - tl;
   if (tid < E) {
     s_off[tid] = ex_c;
+  }
+  if (publish && tid < E) {
     offsets[tid] = ex_c;
     if (a) {
       // work item of the active expert: {id, first sorted position, pair count, 0}
@@ -91,7 +95,7 @@ __device__ __forceinline__ void align_scan(int c, int E, int block_m, int tid, i
     }
     if (tile_offsets) tile_offsets[tid] = ex_t;
   }
-  if (tid == E - 1) {
+  if (publish && tid == E - 1) {
     offsets[E] = ex_c + c;
     const i32x4_t head = {ex_a + a, 0, 0, 0};
     *reinterpret_cast<i32x4_t*>(active) = head;

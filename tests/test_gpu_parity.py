@@ -73,7 +73,7 @@ def test_pack_edge_values():
 
 @pytest.mark.parametrize("T,d,E,k", [(16, 256, 8, 2), (1, 2048, 64, 8), (4, 2048, 64, 8), (16, 2048, 64, 8),
                                      (333, 2048, 64, 8), (4096, 2048, 64, 8), (64, 4096, 8, 2), (7, 512, 1024, 16),
-                                     (5, 128, 1, 1)])
+                                     (5, 128, 1, 1), (300, 256, 128, 16), (300, 256, 256, 8)])
 def test_route_parity(T, d, E, k):
     say(f"route T={T} d={d} E={E} k={k}")
     g = torch.Generator().manual_seed(T * 7 + d + E)

@@ -19,9 +19,11 @@ constexpr int kRouteMaxTB = 4;
 __device__ __forceinline__ double bf16_to_f64(uint32_t bits16) { return (double)bf16_bits_to_f32(bits16); }
 
 // Top-k of one token's E logits (in LDS) by one wavefront: lane l owns experts
-// l, l+64, ...; k rounds of a wave-wide (value desc, index asc) argmax.
+// l, l+64, ...; for E up to 128 every logit's rank in the (value desc, index asc)
+// order is counted against the row and the k best land at their rank (s_sv, s_si:
+// the wavefront's k slots in LDS); beyond that, k rounds of a wave-wide argmax.
 __device__ __forceinline__ void topk_wave(const float* __restrict__ lg, int E, int k, int renormalize, int t,
-                          int32_t* __restrict__ ids, float* __restrict__ weights) {
+                          int32_t* __restrict__ ids, float* __restrict__ weights, float* s_sv, int* s_si) {
   const int lane = lane_id();
   const int nper = (E + 63) / 64;  // <= 16
   float v[16];
@@ -30,36 +32,58 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ lg, int E, i
     const int e = lane + 64 * i;
     v[i] = (i < nper && e < E) ? lg[e] : -INFINITY;
   }
-  uint32_t taken = 0;
   float sel_v[MOE_MAX_TOPK];
   int sel_i[MOE_MAX_TOPK];
+  if (E <= 128) {
 #pragma unroll
-  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
-    if (j >= k) break;
-    // sentinel below every finite logit: a real candidate always wins the reduction
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 2; ++i) {
       const int e = lane + 64 * i;
-      if (i < nper && e < E && !((taken >> i) & 1u) && better(v[i], e, bv, bi)) {
-        bv = v[i];
-        bi = e;
+      if (e < E) {
+        const int rank = rank_in_row(lg, E, v[i], e);
+        if (rank < k) {
+          s_sv[rank] = v[i];
+          s_si[rank] = e;
+        }
       }
     }
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      if (better(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+      if (j < k) {
+        sel_v[j] = s_sv[j];
+        sel_i[j] = s_si[j];
       }
     }
-    bi = min(bi, E - 1);  // unreachable for finite logits; keeps ids in range regardless
-    sel_v[j] = bv;
-    sel_i[j] = bi;
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+  } else {
+    uint32_t taken = 0;
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+      if (j >= k) break;
+      // sentinel below every finite logit: a real candidate always wins the reduction
+      float bv = -INFINITY;
+      int bi = 0x7FFFFFFF;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int e = lane + 64 * i;
+        if (i < nper && e < E && !((taken >> i) & 1u) && better(v[i], e, bv, bi)) {
+          bv = v[i];
+          bi = e;
+        }
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(bv, off);
+        const int oi = __shfl_xor(bi, off);
+        if (better(ov, oi, bv, bi)) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      bi = min(bi, E - 1);  // unreachable for finite logits; keeps ids in range regardless
+      sel_v[j] = bv;
+      sel_i[j] = bi;
+      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    }
   }
   const float lmax = sel_v[0];
   float den = 0.f;
@@ -287,6 +311,8 @@ __global__ __launch_bounds__(256) void k_route(const uint16_t* __restrict__ x, c
                                                float* __restrict__ logits, int32_t* __restrict__ ids,
                                                float* __restrict__ weights) {
   __shared__ float s_logit[TB][MOE_MAX_EXPERTS];
+  __shared__ float s_sv[TB][MOE_MAX_TOPK];
+  __shared__ int s_si[TB][MOE_MAX_TOPK];
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int t0 = blockIdx.x * TB;
   const int nch = d / 8;
@@ -364,7 +390,7 @@ __global__ __launch_bounds__(256) void k_route(const uint16_t* __restrict__ x, c
   }
 
   if (wave >= TB || t0 + wave >= T) return;
-  topk_wave(s_logit[wave], E, k, renormalize, t0 + wave, ids, weights);
+  topk_wave(s_logit[wave], E, k, renormalize, t0 + wave, ids, weights, s_sv[wave], s_si[wave]);
 }
 
 }  // namespace moe

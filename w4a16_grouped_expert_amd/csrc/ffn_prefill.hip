@@ -126,6 +126,9 @@ __device__ __forceinline__ float silu_fast(float z) { return z * __builtin_amdgc
 //     into the ratio e_{k+1} / e_{k+2} (16 e_last once past the end), ring of 2;
 //   during group g - 1 every lane reads the ratios and group sums it needs at the
 //     top of g into registers, so group g starts with the rescale fma right away.
+// Stages and rings are indexed by the workgroup's running group count (its tiles'
+// groups one after another), so a tile's first batches may be issued while the
+// previous tile still reads its last stage.
 template <bool GATEUP>
 __global__ __launch_bounds__(kPThreads) void k_prefill(
     FfnDev f, const uint16_t* __restrict__ act, const float* __restrict__ asum, uint16_t* __restrict__ hout,

@@ -30,7 +30,8 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, in
   f32x4_t v[MOE_MAX_TOPK];
 #pragma unroll
   for (int j = 0; j < MOE_MAX_TOPK; ++j)
-    v[j] = pos[j] >= 0 ? *reinterpret_cast<const f32x4_t*>(y + pos[j] * d + n) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    v[j] = pos[j] >= 0 ? __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(y + pos[j] * d + n))
+                       : f32x4_t{0.f, 0.f, 0.f, 0.f};  // (y is read once: streaming loads)
   for (int s = 1; s < ksplit; ++s) {
     f32x4_t p[MOE_MAX_TOPK];
 #pragma unroll

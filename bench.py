@@ -399,7 +399,7 @@ def measured_traffic():
         return None
 
 
-def run_prefill(T, reps=5, warmup=2):
+def run_prefill(T, reps=20, warmup=3):
     """One OLMoE-shaped layer at T tokens (batched prefill, uniform router): eager
     forward passes with HIP events around each kernel; MFMA roofline of the grouped
     gate/up kernel from its algorithmic flops (2 * T * k * d * 2I per launch)."""

@@ -147,10 +147,11 @@ def test_align_bit_exact(T, E, k):
     check_align_gpu(ids, E, block_m=0)
 
 
-@pytest.mark.parametrize("T,E,k", [(600, 64, 8), (300, 1024, 16), (2049, 8, 2)])
+@pytest.mark.parametrize("T,E,k", [(600, 64, 8), (300, 1024, 16), (2049, 8, 2), (20001, 64, 8)])
 def test_align_chunked_bit_exact(T, E, k):
-    # 4096 pairs and more take the chunked kernel (one workgroup per 2048 pairs):
-    # ragged last chunk, wide ids, few experts
+    # 4096 pairs and more take the chunked kernel (one workgroup per 2048 pairs, at
+    # most 64 workgroups: 160008 pairs use chunks of 4096, two super-batches per
+    # wavefront): ragged last chunk, wide ids, few experts
     say(f"align chunked T={T} E={E} k={k}")
     ids = synth.random_topk_ids(T, E, k, seed=7 * T + E + k).numpy()
     check_align_gpu(ids, E, block_m=128)

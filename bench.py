@@ -3,17 +3,21 @@
 Workload: OLMoE-1B-7B-shaped decode, 16 MoE layers (d_model 2048, 64 experts,
 top-8, expert intermediate 1024, SwiGLU), int4 symmetric group-128 experts with
 bf16 scales, bf16 router and activations, all 64 experts of every layer
-resident in HBM (16 x 207.6 MB).  One step = route + align (one launch) -> grouped FFN
-(gate/up + SwiGLU, down, combine) for each of the 16 layers on fresh
-activations, T tokens per step (headline T = 16).
+resident in HBM (16 x 207.6 MB).  One step = routing + grouped gate/up + SwiGLU
+(one launch) -> grouped down + combine (one launch) for each of the 16 layers on
+fresh activations, T tokens per step (headline T = 16).
 
-Prints one JSON line: MoE-layer tokens/s (T * layers / step time), the
-achieved algorithmic HBM GB/s, the roofline of the dominant kernel (grouped
-gate/up) timed with HIP events on its own stream (its measured HBM traffic comes
-from the committed rocprofv3 counter summary under profiles/ when that was taken
-on the current kernel sources), a batched-prefill layer (T = 4096) with the MFMA
-roofline of its grouped gate/up kernel, and the CPU oracle timed on a bounded
-sample of the decode workload.
+Prints one JSON line: MoE-layer tokens/s (T * layers / step time, the median of 3
+trials of K graph-replayed steps), the achieved algorithmic HBM GB/s, the roofline
+of the dominant kernel (routing + grouped gate/up) timed with HIP events on its
+own stream (its measured HBM traffic comes from the committed rocprofv3 counter
+summary under profiles/ when that was taken on the current kernel sources), a
+batched-prefill layer (T = 4096) with the MFMA roofline of its grouped gate/up
+kernel, the other workloads, and the cpu_baseline leg: the CPU oracle timed on a
+bounded sample of the decode workload on the host's cores, and a parity verdict
+per configuration (layer 0 of each, every token, against the oracle).  A raised
+routing-wait flag of moe_decode_layer stops the run; a failed parity verdict
+makes it exit non-zero after printing the line.
 """
 import argparse
 import json
@@ -72,6 +76,34 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
 
 
+def host_facts():
+    """CPU model, physical cores and the logical CPUs this process may run on."""
+    model, cores = "unknown", set()
+    phys = core = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            k, _, v = line.partition(":")
+            k, v = k.strip(), v.strip()
+            if k == "model name" and model == "unknown":
+                model = v
+            elif k == "physical id":
+                phys = v
+            elif k == "core id":
+                core = v
+            elif not k and phys is not None and core is not None:
+                cores.add((phys, core))
+                phys = core = None
+        if phys is not None and core is not None:
+            cores.add((phys, core))
+    except OSError:
+        pass
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    usable = min(avail, int(cap)) if cap.isdigit() and int(cap) > 0 else avail
+    return {"cpu_model": model, "physical_cores": len(cores) or None, "logical_cpus_available": avail,
+            "threads_allowed": usable}
+
+
 class Decoder:
     """16 resident MoE layers with shared per-step buffers: four-bit experts, or
     (bf16=True) the same experts unquantised for the W4 versus BF16 comparison."""
@@ -116,6 +148,19 @@ class Decoder:
 
     def uses_layer(self, T):
         return self.fused and T <= 16
+
+    def check_wait_flag(self, where):
+        """moe_decode_layer raises its last counter when a workgroup gave up waiting
+        for the routing (its outputs are then invalid): a step timed with that flag
+        up is not a valid measurement, so the run stops."""
+        if not self.fused:
+            return 0
+        self.torch.cuda.synchronize()
+        flag = int(self.lctr[-1].item())
+        if flag:
+            raise SystemExit(f"bench.py: moe_decode_layer routing wait timed out during {where} "
+                             f"(flag {flag}); results invalid")
+        return flag
 
     def layer(self, l, x):
         moe, s = self.moe, self.s
@@ -321,27 +366,35 @@ def capture_graphs(dec, xs_sets):
 
 
 def run_decode(dec, T, steps, warmup, x_sets, timed_kernels=("gateup_decode", "down_decode", "combine", "route",
-                                                              "align")):
-    """Time K steps replayed from HIP graphs (value), then K eager steps with the
-    dominant kernels bracketed by HIP events on their stream (roofline)."""
+                                                              "align"), trials=3):
+    """Time K steps replayed from HIP graphs, in `trials` trials (value: the median
+    trial), then K eager steps with the dominant kernels bracketed by HIP events on
+    their stream (roofline).  After each leg the routing-wait flag of
+    moe_decode_layer is read; a raised flag stops the run."""
     import torch
     import synth
     moe = dec.moe
     wl, s = dec.wl, dec.s
     xs = [[synth.activations(wl, T, l, step=st, device="cuda") for l in range(wl.layers)] for st in range(x_sets)]
     U = [dec.distinct_experts(x) for x in xs]
+    dec.check_wait_flag(f"the T={T} pre-pass")
     graphs = capture_graphs(dec, xs)
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for i in range(warmup):
         graphs[i % x_sets].replay()
     torch.cuda.synchronize()
-    t0.record()
-    for i in range(steps):
-        graphs[i % x_sets].replay()
-    t1.record()
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
+    trial_ms = []
+    for _ in range(max(1, trials)):
+        torch.cuda.synchronize()
+        t0.record()
+        for i in range(steps):
+            graphs[i % x_sets].replay()
+        t1.record()
+        torch.cuda.synchronize()
+        trial_ms.append(t0.elapsed_time(t1) / steps)
+    ms = sorted(trial_ms)[len(trial_ms) // 2]
     del graphs
+    dec.check_wait_flag(f"the T={T} graph replays")
 
     for i in range(warmup):
         dec.step(xs[i % x_sets])
@@ -355,7 +408,8 @@ def run_decode(dec, T, steps, warmup, x_sets, timed_kernels=("gateup_decode", "d
     torch.cuda.synchronize()
     moe.timing_enable(False)
     ms_eager = t0.elapsed_time(t1) / steps
-    res = {"T": T, "ms_per_step": ms, "ms_per_step_eager": ms_eager, "kernels": {}}
+    dec.check_wait_flag(f"the T={T} eager steps")
+    res = {"T": T, "ms_per_step": ms, "ms_per_step_eager": ms_eager, "trial_ms_per_step": trial_ms, "kernels": {}}
     for kname in timed_kernels:
         tot, n = moe.timing_read(kname)
         if n:
@@ -526,6 +580,7 @@ def run_slot_cache(steps, warmup=8, T=16, variants=((16, False), (16, True), (64
             for l in range(wl.layers)]
     main = torch.cuda.current_stream()
     copy = torch.cuda.Stream()
+    probe = []
 
     def one(S, prefetch):
         torch.cuda.synchronize()
@@ -542,7 +597,7 @@ def run_slot_cache(steps, warmup=8, T=16, variants=((16, False), (16, True), (64
             L["ffn_done"].record(main)
         L_ = len(layers)
 
-        def step(st):
+        def step(st, capture=False):
             rounds = misses = pref = floor = 0
             for l, L in enumerate(layers):
                 x = seqs[l][st]
@@ -566,6 +621,8 @@ def run_slot_cache(steps, warmup=8, T=16, variants=((16, False), (16, True), (64
                     rounds += 1
                     misses += nm
                 L["prev"] = need
+                if capture and l == 0:
+                    probe.append((x, out.clone(), route.ids[:T].clone()))
             return rounds, misses, pref, floor
 
         for st in range(warmup):
@@ -575,7 +632,7 @@ def run_slot_cache(steps, warmup=8, T=16, variants=((16, False), (16, True), (64
         t0 = time.perf_counter()
         rounds = misses = pref = floor = 0
         for st in range(warmup, warmup + steps):
-            r, m, p, fl = step(st)
+            r, m, p, fl = step(st, capture=(st == warmup + steps - 1 and S == 16 and not prefetch))
             rounds += r
             misses += m
             pref += p
@@ -607,53 +664,172 @@ def run_slot_cache(steps, warmup=8, T=16, variants=((16, False), (16, True), (64
         res[f"S={S}" + (" prefetch" if pf else "")] = one(S, pf)
     del stores
     torch.cuda.empty_cache()
-    return res
+    # layer 0 of the last timed S=16 step (input, output, routing) for the parity check
+    probe = [(x.cpu(), o.cpu(), ids.cpu().numpy()) for x, o, ids in probe[:1]]
+    return res, (probe[0] if probe else None)
 
 
-def cpu_baseline(wl, T, budget_s):
-    """The CPU oracle on a bounded sample of the same workload: one OLMoE-shaped
-    layer at T tokens (route, align, per-pair SwiGLU FFN in float64, combine),
-    repeated until the time budget is used.  The experts' quantise/dequantise is
-    done up front and not timed, as the GPU path packs its weights offline."""
-    from concurrent.futures import ThreadPoolExecutor
-
+def _bits(t):
     import numpy as np
     import torch
+    return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def _oracle_bank(wl, layer, experts, threads):
+    """Oracle dequantised bank of the listed experts of one layer (drawn on the GPU
+    with the bench's seeds, dequantised on `threads` host threads, untimed)."""
+    from concurrent.futures import ThreadPoolExecutor
+    import synth
+    from oracle import ffn as offn
+    experts = sorted(experts)
+    w13, w2 = synth.expert_weights(wl, layer, device="cuda", experts=experts)
+    host13 = {e: _bits(w13[i]) for i, e in enumerate(experts)}
+    host2 = {e: _bits(w2[i]) for i, e in enumerate(experts)}
+    del w13, w2
+    bank = offn.DequantBank(lambda e: host13[e], lambda e: host2[e])
+    with ThreadPoolExecutor(max_workers=max(1, min(threads, len(experts)))) as ex:
+        list(ex.map(bank.get, experts))
+    return bank
+
+
+def cpu_baseline(wl, T, budget_s, threads, bank=None):
+    """The CPU oracle on a bounded sample of the same workload: one OLMoE-shaped
+    layer at T tokens (route, align, per-pair SwiGLU FFN in float64, combine),
+    repeated until the time budget is used, its matrix products on `threads` host
+    threads.  The experts' quantise/dequantise is done up front and not timed, as
+    the GPU path packs its weights offline."""
     import synth
     from oracle import ffn as offn
     from oracle import route as oroute
-
-    def bits(t):
-        return t.contiguous().view(torch.int16).numpy().view(np.uint16)
-
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
+    from threadpoolctl import threadpool_limits
     layer = 0
-    w13, w2 = synth.expert_weights(wl, layer, device="cuda")
-    wr = bits(synth.router_weight(wl, layer))
-    x = bits(synth.activations(wl, T, layer, step=0))
+    wr = _bits(synth.router_weight(wl, layer))
+    x = _bits(synth.activations(wl, T, layer, step=0))
     used = sorted(set(oroute.route(x, wr, wl.shape.k)[1].reshape(-1).tolist()))
-    host13 = {e: bits(w13[e].cpu()) for e in used}
-    host2 = {e: bits(w2[e].cpu()) for e in used}
-    del w13, w2
-    bank = offn.DequantBank(lambda e: host13[e], lambda e: host2[e])
-    with ThreadPoolExecutor(max_workers=8) as ex:
-        deq = dict(zip(used, ex.map(lambda e: offn.DequantBank(lambda _: host13[e], lambda _: host2[e]).get(e),
-                                    used)))
-    bank._cache.update(deq)
+    if bank is None:
+        bank = _oracle_bank(wl, layer, used, threads)
     calls, elapsed = 0, 0.0
-    while elapsed < budget_s or calls == 0:
-        t0 = time.perf_counter()
-        offn.moe_layer(x, wr, bank, wl.shape.k)
-        elapsed += time.perf_counter() - t0
-        calls += 1
+    with threadpool_limits(limits=threads):
+        while elapsed < budget_s or calls == 0:
+            t0 = time.perf_counter()
+            offn.moe_layer(x, wr, bank, wl.shape.k)
+            elapsed += time.perf_counter() - t0
+            calls += 1
     return {"value": round(calls * T / elapsed, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"1 OLMoE-shaped layer (d=2048, E=64, top-8, I=1024) at T={T}, {len(used)} distinct "
-                      f"experts, run {calls} times in {elapsed:.1f} s (float64 numpy oracle; expert "
-                      "dequantisation done beforehand, untimed)"}
+                      f"experts, run {calls} times in {elapsed:.1f} s (float64 numpy oracle, matrix products on "
+                      f"{threads} threads; expert dequantisation done beforehand, untimed)"}
+
+
+def _errs(got, ref):
+    import numpy as np
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.max(np.abs(ref))
+    whole = float(np.max(np.abs(got - ref)) / den) if den > 0 else float(np.max(np.abs(got)))
+    rden = np.max(np.abs(ref), axis=1)
+    rnum = np.max(np.abs(got - ref), axis=1)
+    tok = float(np.max(np.where(rden > 0, rnum / np.where(rden > 0, rden, 1.0), rnum)))
+    return whole, tok, bool(np.all(np.isfinite(got)))
+
+
+def parity_verdicts(args, threads, slot_probe=None):
+    """Part of the cpu_baseline leg: for each measured configuration, layer 0 of its
+    bank run once more through the same entry points the timing used, every output
+    token compared with the oracle on the same seeded inputs (routing ids bit-exact,
+    max|gpu - ref| / max|ref| <= 1e-2 over the layer and for every token on its
+    own).  Returns ({config: verdict}, oracle bank of the decode layer)."""
+    import numpy as np
+    import torch
+    import synth
+    import w4a16_grouped_expert_amd as moe
+    from oracle import ffn as offn
+    from oracle import route as oroute
+    from threadpoolctl import threadpool_limits
+    tol = 1e-2
+    res = {}
+
+    def verdict(name, wl, bank_o, x, wr, out, ids):
+        with threadpool_limits(limits=threads):
+            ref = offn.moe_layer(_bits(x), _bits(wr), bank_o, wl.shape.k)
+        whole, tok, finite = _errs(out.float().cpu().numpy(), ref["out"])
+        ids_eq = bool(np.array_equal(ids.cpu().numpy(), ref["ids"]))
+        res[name] = {"tokens_compared": int(x.shape[0]), "ids_bit_exact": ids_eq, "max_rel_err": round(whole, 6),
+                     "worst_token_rel_err": round(tok, 6),
+                     "pass": bool(ids_eq and finite and whole <= tol and tok <= tol)}
+
+    def used_experts(wl, xs):
+        wr = _bits(synth.router_weight(wl, 0))
+        u = set()
+        for x in xs:
+            u |= set(oroute.route(_bits(x), wr, wl.shape.k)[1].reshape(-1).tolist())
+        return u
+
+    def gpu_bank(wl):
+        w13, w2 = synth.expert_weights(wl, 0, device="cuda")
+        bank, _ = moe.pack_experts(w13, w2)
+        del w13, w2
+        return bank
+
+    # decode (the headline and the sweep): moe_decode_layer, as timed
+    wl = synth.OLMOE_DECODE
+    s = wl.shape
+    Ts = sorted({args.tokens} | {int(t) for t in args.sweep.split(",") if t})
+    xs = {T: synth.activations(wl, T, 0, step=0) for T in Ts}
+    dec_bank = _oracle_bank(wl, 0, used_experts(wl, xs.values()), threads)
+    bank = gpu_bank(wl)
+    wr = synth.router_weight(wl, 0)
+    for T in Ts:
+        xd = xs[T].cuda()
+        if T <= 16 and not args.two_call:
+            out, r = moe.moe_decode_layer(xd, wr.cuda(), bank, s.I, s.k)
+        else:
+            L = moe.MoELayer(wr.cuda(), bank, s.I, s.k, T)
+            out = L.forward(xd)
+            r = L.route
+        torch.cuda.synchronize()
+        verdict(f"olmoe_decode T={T}", wl, dec_bank, xs[T], wr, out, r.ids[:T])
+    del bank
+    # prefill: route + align + grouped FFN, as timed
+    if args.prefill_tokens > 0:
+        wl = synth.OLMOE_PREFILL
+        s = wl.shape
+        Ts = sorted({args.prefill_tokens} | {int(t) for t in args.prefill_sweep.split(",") if t})
+        xs = {T: synth.activations(wl, T, 0) for T in Ts}
+        bank_o = _oracle_bank(wl, 0, range(s.E), threads)
+        bank = gpu_bank(wl)
+        wr = synth.router_weight(wl, 0)
+        for T in Ts:
+            L = moe.MoELayer(wr.cuda(), bank, s.I, s.k, T)
+            out = L.forward(xs[T].cuda())
+            torch.cuda.synchronize()
+            verdict(f"olmoe_prefill T={T}", wl, bank_o, xs[T], wr, out, L.route.ids[:T])
+            del L
+        del bank, bank_o
+    # large expert
+    if not args.no_large:
+        wl = synth.LARGE
+        s = wl.shape
+        xs = {T: synth.activations(wl, T, 0) for T in wl.tokens}
+        bank_o = _oracle_bank(wl, 0, used_experts(wl, xs.values()), threads)
+        bank = gpu_bank(wl)
+        wr = synth.router_weight(wl, 0)
+        for T in wl.tokens:
+            L = moe.MoELayer(wr.cuda(), bank, s.I, s.k, T)
+            out = L.forward(xs[T].cuda())
+            torch.cuda.synchronize()
+            verdict(f"large_expert T={T}", wl, bank_o, xs[T], wr, out, L.route.ids[:T])
+            del L
+        del bank, bank_o
+    # slot cache: layer 0's output of the last timed step of the S=16 run
+    if slot_probe is not None:
+        wl = synth.OLMOE_SLOT
+        x, out, ids = slot_probe
+        bank_o = _oracle_bank(wl, 0, set(ids.reshape(-1).tolist()), threads)
+        verdict("olmoe_slot S=16 (last timed step, layer 0)", wl, bank_o, x, synth.router_weight(wl, 0), out,
+                torch.from_numpy(ids))
+    torch.cuda.empty_cache()
+    return res, dec_bank
 
 
 def main():
@@ -699,8 +875,11 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(head["ms_per_step"], 4),
         "ms_per_step_eager": round(head["ms_per_step_eager"], 4),
-        "timing": "value: K steps replayed from HIP graphs (one per activation set); roofline: the same K "
-                  "steps run eagerly with HIP events around each grouped gate/up launch on its stream",
+        "trials": len(head["trial_ms_per_step"]),
+        "trial_ms_per_step": [round(t, 4) for t in head["trial_ms_per_step"]],
+        "timing": "value: the median of 3 trials, each timing K steps replayed from HIP graphs (one per "
+                  "activation set); roofline: K steps run eagerly with HIP events around each grouped "
+                  "gate/up launch on its stream",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -714,6 +893,7 @@ def main():
         "mean_distinct_experts": round(head["mean_distinct_experts"], 2),
         "roofline": roofline,
         "kernels_us": {k: round(v["avg_us"], 3) for k, v in head["kernels"].items()},
+        "routing_wait_timeouts": 0,  # moe_decode_layer's flag, read after every leg (a raised flag stops the run)
         "decode_sweep": sweep,
     }
     if not args.no_ablation:
@@ -743,11 +923,26 @@ def main():
             out["prefill_sweep"] = extra
     if not args.no_large:
         out["large_expert"] = run_large(synth.LARGE.tokens)
+    slot_probe = None
     if not args.no_slot_cache:
-        out["slot_cache"] = run_slot_cache(args.slot_steps)
+        out["slot_cache"], slot_probe = run_slot_cache(args.slot_steps)
+    ok = True
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, args.tokens, args.cpu_seconds)
+        host = host_facts()
+        threads = host["threads_allowed"]
+        verdicts, dec_bank = parity_verdicts(args, threads, slot_probe)
+        ok = all(v["pass"] for v in verdicts.values())
+        out["parity"] = {"bar": "routing ids bit-exact; max|gpu - oracle| / max|oracle| <= 1e-2 over the layer "
+                                "and for every token (bf16 outputs vs the float64 oracle on identical "
+                                "dequantised weights); layer 0 of each configuration, every token",
+                         "all_pass": ok, "configs": verdicts}
+        out["cpu_baseline"] = cpu_baseline(wl, args.tokens, args.cpu_seconds, threads, bank=dec_bank)
+        out["cpu_baseline"]["host"] = host
     print(json.dumps(out))
+    if not ok:
+        print("bench.py: parity against the oracle failed for " +
+              ", ".join(k for k, v in out["parity"]["configs"].items() if not v["pass"]), file=sys.stderr)
+        sys.exit(3)
 
 
 if __name__ == "__main__":

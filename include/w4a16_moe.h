@@ -109,6 +109,10 @@ int moe_route(const uint16_t* x, const uint16_t* w_router, int T, int d, int E, 
 /*
  * moe_align -- expert-sorted permutation of the T*k (token, slot) pairs that
  * feeds the grouped kernels.  Stable counting sort, pair p = t*k + j.
+ * (ExactMoE, page "Every Expert Counts: ExactMoE for Memory-Efficient W4A16
+ * Inference", Abstract: every selected expert of a step runs through fused
+ * grouped MoE kernels; grouping a step's pairs by expert is what lets one grouped
+ * pass stream each selected expert's weights once for all of its tokens.)
  *
  *  expert_offsets [E+1] int32: exclusive prefix sum of per-expert pair counts.
  *  sorted_pairs   [T*k] int32: pair ids grouped by expert, increasing within a group.

@@ -1,26 +1,34 @@
 """GPU slot cache: experts in pinned host memory, S device slots, rounds when more
 experts are needed than slots.  Outputs must equal the all-resident path bit for
-bit (same kernels, same per-pair arithmetic), and the hit / miss / slot sequence
-must equal the oracle's LRU simulator."""
+bit (same kernels, same per-pair arithmetic) and the oracle within the layer
+tolerance (every token), and the hit / miss / prefetch / slot sequence must equal
+the oracle's LRU simulator."""
 import numpy as np
 import pytest
 import torch
 
 import synth
 import w4a16_grouped_expert_amd as moe
+from oracle import ffn as offn
 from oracle.slot_cache import LRUSlotCache
 
-from gpu_helpers import say
+from gpu_helpers import bits, check_layer_out, oracle_bank, say, warm_bank
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def run_slot_steps(wl, S, steps, T, seed_layer=0, prefetch=False):
+def run_slot_steps(wl, S, steps, T, seed_layer=0, prefetch=None, check_oracle=True):
+    """Decode steps through an S-slot cache.  prefetch: None, "prev" (at the start of
+    a step, the previous step's experts) or "next" (after a step's last round, the
+    next step's experts from its routing: a predictor that can differ from the
+    resident set, so copies happen).  Returns (rounds per step, hits, misses,
+    prefetch copies)."""
     s = wl.shape
     w13, w2 = synth.expert_weights(wl, seed_layer, device=DEV)
     wr = synth.router_weight(wl, seed_layer).to(DEV)
     bank, lay = moe.pack_experts(w13, w2)
+    ob = warm_bank(oracle_bank(w13, w2), range(s.E)) if check_oracle else None
     B = lay["blob_bytes"]
     store = torch.empty((s.E, B), dtype=torch.uint8, pin_memory=True)
     store.copy_(bank.cpu())
@@ -35,17 +43,25 @@ def run_slot_steps(wl, S, steps, T, seed_layer=0, prefetch=False):
     ffn_done.record(main)
     ws = moe.alloc_workspace(T, s.d, s.I, s.E, s.k, moe.MODE_DECODE)
     xs = synth.ar1_activation_sequence(wl, T, seed_layer, steps, device="cpu")
+    routes = [None] * steps
+
+    def route(st):
+        if routes[st] is None:
+            x = xs[st].to(DEV)
+            r = moe.moe_route(x, wr, s.k)
+            a = moe.moe_align(r.ids, s.E)
+            routes[st] = (x, r, a, {w[0] for w in moe.active_experts(a)})
+        return routes[st]
+
     n_rounds = []
     prev = set()
+    n_pref = 0
     for st in range(steps):
-        x = xs[st].to(DEV)
-        if prefetch and prev:
-            # the previous step's experts, copied ahead of this step's rounds
+        if prefetch == "prev" and prev:
             n = cache.prefetch(prev, S, copy, ffn_done)
             assert n == len(sim.prefetch(prev, S)), st
-        r = moe.moe_route(x, wr, s.k)
-        a = moe.moe_align(r.ids, s.E)
-        need = {w[0] for w in moe.active_experts(a)}
+            n_pref += n
+        x, r, a, need = route(st)
         prev = need
         expect = sim.step(need)
         pending = set(need)
@@ -61,6 +77,12 @@ def run_slot_steps(wl, S, steps, T, seed_layer=0, prefetch=False):
             ffn_done.record(main)
             rounds += 1
         assert rounds == len(expect)
+        if prefetch == "next" and st + 1 < steps:
+            # the copies wait for this step's last round (they may overwrite its slots)
+            nxt = route(st + 1)[3]
+            n = cache.prefetch(nxt, S, copy, ffn_done)
+            assert n == len(sim.prefetch(nxt, S)), st
+            n_pref += n
         slot_state, _, _ = cache.state()
         assert slot_state == sim.slot_expert
         # all experts resident, through an all-experts slot table: the same two-pass
@@ -69,30 +91,47 @@ def run_slot_steps(wl, S, steps, T, seed_layer=0, prefetch=False):
         ref_out = moe.moe_w4a16_grouped_ffn(x, r, a, bank, s.I, mode=moe.MODE_DECODE, slot_of_expert=ident)
         torch.cuda.synchronize()
         assert torch.equal(out, ref_out), f"step {st}"
+        if ob is not None:
+            ref = offn.moe_layer(bits(x), bits(wr), ob, s.k)
+            assert np.array_equal(r.ids.cpu().numpy(), ref["ids"])
+            check_layer_out(f"step {st} ({rounds} rounds)", out.float().cpu().numpy(), ref["out"])
         n_rounds.append(rounds)
     hits, misses = cache.state()[1:]
     cache.close()
-    return n_rounds, hits, misses
+    return n_rounds, hits, misses, n_pref
 
 
 def test_slot_cache_tiny_rounds():
     say("slot cache tiny E=8 S=3")
-    n_rounds, hits, misses = run_slot_steps(synth.TINY, 3, 6, 16)
+    n_rounds, hits, misses, _ = run_slot_steps(synth.TINY, 3, 6, 16)
     assert max(n_rounds) >= 2
 
 
 def test_slot_cache_olmoe_zipf_16_slots():
     say("slot cache olmoe zipf S=16")
-    n_rounds, hits, misses = run_slot_steps(synth.OLMOE_SLOT, 16, 6, 16)
+    n_rounds, hits, misses, _ = run_slot_steps(synth.OLMOE_SLOT, 16, 6, 16)
     say(f"  rounds {n_rounds} hits {hits} misses {misses}")
     assert hits > 0 and misses > 0
 
 
 def test_slot_cache_prefetch_olmoe_zipf_16_slots():
     say("slot cache prefetch olmoe zipf S=16")
-    n_rounds, hits, misses = run_slot_steps(synth.OLMOE_SLOT, 16, 6, 16, prefetch=True)
-    say(f"  rounds {n_rounds} hits {hits} misses {misses}")
+    n_rounds, hits, misses, n_pref = run_slot_steps(synth.OLMOE_SLOT, 16, 6, 16, prefetch="prev",
+                                                    check_oracle=False)
+    say(f"  rounds {n_rounds} hits {hits} misses {misses} prefetched {n_pref}")
     assert hits > 0
+
+
+@pytest.mark.parametrize("wl,S,T", [(synth.TINY, 3, 2), (synth.OLMOE_SLOT, 16, 16)])
+def test_slot_cache_prefetch_next_step_copies(wl, S, T):
+    # the next step's experts copied after a step's last round: the prefetch path
+    # really moves data (the LRU simulator makes 2 copies at the tiny shape and 11
+    # at the OLMoE shape over these 6 steps), and the next step's rounds find
+    # those experts resident
+    say(f"slot cache next-step prefetch {wl.name} S={S} T={T}")
+    n_rounds, hits, misses, n_pref = run_slot_steps(wl, S, 6, T, prefetch="next")
+    say(f"  rounds {n_rounds} hits {hits} misses {misses} prefetched {n_pref}")
+    assert n_pref > 0
 
 
 def test_slot_cache_injected_copy_failure(monkeypatch):

@@ -192,6 +192,32 @@ int64_t moe_ffn_workspace_bytes(int T, int d, int I, int E, int k, int mode);
 int moe_w4a16_grouped_ffn(const moe_ffn_args* args, void* stream);
 
 /*
+ * moe_w4a16_grouped_ffn_noalloc -- moe_w4a16_grouped_ffn without a caller
+ * workspace, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * workspace comes from a static device array of MOE_NOALLOC_SCRATCH_BYTES that
+ * every GPU the library runs on holds until the process ends; the call makes no
+ * allocation of any kind.
+ *
+ *  args  as for moe_w4a16_grouped_ffn, with workspace = NULL and
+ *        workspace_bytes = 0 (MOE_ERR_INVALID_ARG otherwise).  Results are those
+ *        of moe_w4a16_grouped_ffn on the same arguments (the same kernels on the
+ *        same workspace layout), including combine = 0 rounds whose per-pair
+ *        results stay in the scratch for a later call with combine = 1.
+ *  Runs on the calling thread's current device; `stream` must belong to it.
+ *  Errors: MOE_ERR_WORKSPACE when moe_ffn_workspace_bytes(T, d, I, E, k, mode)
+ *  exceeds MOE_NOALLOC_SCRATCH_BYTES (checked on the host before anything is
+ *  enqueued; e.g. OLMoE-shaped decode steps use under 6 MiB, prefill steps fit up
+ *  to about 800 tokens), MOE_ERR_HIP when the scratch address cannot be
+ *  obtained, else those of moe_w4a16_grouped_ffn.
+ *  All calls on one GPU share its scratch, which keeps the last call's contents:
+ *  calls that overlap on one GPU (concurrent streams or threads) race and give
+ *  undefined results; order them on one stream or by events.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (64ll << 20)
+int moe_w4a16_grouped_ffn_noalloc(const moe_ffn_args* args, void* stream);
+
+/*
  * moe_decode_layer -- one decode step of the whole layer (router, top-k,
  * grouped gate/up + SwiGLU, grouped down, routing-weighted combine) for at most
  * 16 tokens, in two launches (ExactMoE, Abstract: the BF16 router with its

@@ -151,3 +151,19 @@ def test_decode_layer_host_checks(L):
     ws = L.moe_decode_layer_workspace_bytes(16, 2048, 1024, 64, 8)
     assert ws >= 16 * 8 * 1024 * 2 + (2048 // 32) * 32 * 512 * 4
     assert L.moe_decode_layer_workspace_bytes(-1, 2048, 1024, 64, 8) == -1
+
+
+def test_noalloc_host_checks(L):
+    """moe_w4a16_grouped_ffn_noalloc: a caller workspace or a step whose workspace
+    exceeds the scratch is refused on the host, before any device call."""
+    from w4a16_grouped_expert_amd import _lib
+    assert L.moe_w4a16_grouped_ffn_noalloc(None, None) == 1
+    a = _lib.FfnArgs()
+    a.T, a.d, a.I, a.E, a.k, a.mode = 4096, 2048, 1024, 64, 8, 2
+    a.workspace, a.workspace_bytes = 256, 1 << 20
+    assert L.moe_w4a16_grouped_ffn_noalloc(ctypes.byref(a), None) == 1   # caller workspace given
+    a.workspace, a.workspace_bytes = None, 0
+    assert L.moe_w4a16_grouped_ffn_noalloc(ctypes.byref(a), None) == 3   # needs more than the scratch
+    assert b"scratch" in L.moe_last_error()
+    a.T = 0
+    assert L.moe_w4a16_grouped_ffn_noalloc(ctypes.byref(a), None) == 0   # T = 0: no-op

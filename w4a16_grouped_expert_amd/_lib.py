@@ -71,6 +71,7 @@ SIGNATURES = {
                                 c_vp, c_vp, c_vp, c_vp, c_vp]),
     "moe_ffn_workspace_bytes": (c_i64, [c_int, c_int, c_int, c_int, c_int, c_int]),
     "moe_w4a16_grouped_ffn": (c_int, [ctypes.POINTER(FfnArgs), c_vp]),
+    "moe_w4a16_grouped_ffn_noalloc": (c_int, [ctypes.POINTER(FfnArgs), c_vp]),
     "moe_bf16_expert_bytes": (c_i64, [c_int, c_int]),
     "moe_bf16_pack": (c_int, [c_vp, c_vp, c_int, c_int, c_int, c_vp, c_i64, c_vp]),
     "moe_bf16_grouped_ffn": (c_int, [ctypes.POINTER(FfnArgs), c_vp]),

@@ -183,13 +183,12 @@ def alloc_workspace(T, d, I, E, k, mode=MODE_AUTO, device="cuda") -> torch.Tenso
     return torch.empty(max(ffn_workspace_bytes(T, d, I, E, k, mode), 256), dtype=torch.uint8, device=device)
 
 
-def moe_w4a16_grouped_ffn_into(x, route: RouteOut, al: AlignOut, bank: torch.Tensor, I: int, out: torch.Tensor,
-                               workspace: torch.Tensor, mode=MODE_AUTO, combine=True,
-                               slot_of_expert: Optional[torch.Tensor] = None, bank_stride: Optional[int] = None,
-                               stream=None):
+def _ffn_args(x, route: RouteOut, al: AlignOut, bank: torch.Tensor, I: int, out, workspace, mode, combine,
+              slot_of_expert, bank_stride):
     _need(x, torch.bfloat16, "x")
     _need(bank, torch.uint8, "bank")
-    _need(workspace, torch.uint8, "workspace")
+    if workspace is not None:
+        _need(workspace, torch.uint8, "workspace")
     if combine:
         _need(out, torch.bfloat16, "out")
     if slot_of_expert is not None:
@@ -208,8 +207,33 @@ def moe_w4a16_grouped_ffn_into(x, route: RouteOut, al: AlignOut, bank: torch.Ten
     a.slot_of_expert = slot_of_expert.data_ptr() if slot_of_expert is not None else None
     a.mode, a.combine = mode, int(bool(combine))
     a.out = out.data_ptr() if out is not None else None
-    a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
+    a.workspace = workspace.data_ptr() if workspace is not None else None
+    a.workspace_bytes = workspace.numel() if workspace is not None else 0
+    return a
+
+
+def moe_w4a16_grouped_ffn_into(x, route: RouteOut, al: AlignOut, bank: torch.Tensor, I: int, out: torch.Tensor,
+                               workspace: torch.Tensor, mode=MODE_AUTO, combine=True,
+                               slot_of_expert: Optional[torch.Tensor] = None, bank_stride: Optional[int] = None,
+                               stream=None):
+    if workspace is None:
+        raise ValueError("workspace is required (moe_w4a16_grouped_ffn_noalloc_into uses the library's scratch)")
+    a = _ffn_args(x, route, al, bank, I, out, workspace, mode, combine, slot_of_expert, bank_stride)
     check("moe_w4a16_grouped_ffn", lib().moe_w4a16_grouped_ffn(ctypes.byref(a), _stream(stream)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES in w4a16_moe.h
+
+
+def moe_w4a16_grouped_ffn_noalloc_into(x, route: RouteOut, al: AlignOut, bank: torch.Tensor, I: int,
+                                       out: torch.Tensor, mode=MODE_AUTO, combine=True,
+                                       slot_of_expert: Optional[torch.Tensor] = None,
+                                       bank_stride: Optional[int] = None, stream=None):
+    """moe_w4a16_grouped_ffn with the library's per-GPU scratch as its workspace
+    (no workspace argument, no allocation); calls on one GPU must not overlap."""
+    a = _ffn_args(x, route, al, bank, I, out, None, mode, combine, slot_of_expert, bank_stride)
+    check("moe_w4a16_grouped_ffn_noalloc", lib().moe_w4a16_grouped_ffn_noalloc(ctypes.byref(a), _stream(stream)))
     return out
 
 

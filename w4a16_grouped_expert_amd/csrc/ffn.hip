@@ -7,6 +7,8 @@
 // y [ksplit][T*k][d] fp32 (down-projection partials, expert-sorted rows).
 // The combine reads y through pair_pos, sums the K-split partials in a fixed
 // order and the k routed outputs in slot order, in fp32, and rounds once to bf16.
+#include <mutex>
+
 #include "ffn_common.hpp"
 
 namespace moe {
@@ -213,4 +215,67 @@ extern "C" int moe_w4a16_grouped_ffn(const moe_ffn_args* a, void* stream) {
   if (rc) return rc;
   if (a->combine && !fused) rc = launch_combine(f, w.y, w.ksplit, a->topk_weights, a->out, s);
   return rc;
+}
+
+// ---------------------------------------------------------------- no-allocation variant
+//
+// moe_w4a16_grouped_ffn_noalloc: the same pass with its workspace taken from a
+// file-scope device array instead of a caller buffer, for callers that cannot
+// allocate.  Each GPU the library runs on holds its own copy of the array until the
+// process ends; host code addresses it only through the device pointer that
+// hipGetSymbolAddress returns for that device (the array's name is a host-side
+// stand-in).  Nothing in the workspace has to be zero when a call starts: the
+// gate/up kernels clear the down pass's stripe counters on every call.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxScratchDevices] = {};
+
+// device address of this device's scratch copy, looked up once per device
+int scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) {
+    set_error("moe_w4a16_grouped_ffn_noalloc: no usable current device (%s, device %d)", hipGetErrorString(e), dev);
+    return MOE_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      set_error("moe_w4a16_grouped_ffn_noalloc: hipGetSymbolAddress of the scratch array failed on device %d: %s",
+                dev, hipGetErrorString(e));
+      return MOE_ERR_HIP;
+    }
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return MOE_OK;
+}
+}  // namespace
+
+extern "C" int moe_w4a16_grouped_ffn_noalloc(const moe_ffn_args* a, void* stream) {
+  clear_error();
+  MOE_CHECK_ARG(a != nullptr, MOE_ERR_INVALID_ARG, "moe_w4a16_grouped_ffn_noalloc: args is NULL");
+  MOE_CHECK_ARG(a->workspace == nullptr && a->workspace_bytes == 0, MOE_ERR_INVALID_ARG,
+                "moe_w4a16_grouped_ffn_noalloc: workspace must be NULL with 0 bytes (the call uses its own scratch)");
+  MOE_CHECK_ARG(a->T >= 0 && a->d > 0 && a->I > 0 && a->E > 0 && a->k > 0 && a->mode >= 0 && a->mode <= 2,
+                MOE_ERR_INVALID_ARG, "moe_w4a16_grouped_ffn_noalloc: bad sizes T=%d d=%d I=%d E=%d k=%d mode=%d",
+                a->T, a->d, a->I, a->E, a->k, a->mode);
+  const int64_t need = moe_ffn_workspace_bytes(a->T, a->d, a->I, a->E, a->k, a->mode);
+  MOE_CHECK_ARG(need >= 0 && need <= (int64_t)MOE_NOALLOC_SCRATCH_BYTES, MOE_ERR_WORKSPACE,
+                "moe_w4a16_grouped_ffn_noalloc: this step needs %lld bytes of workspace, above the %lld-byte scratch "
+                "(use moe_w4a16_grouped_ffn with a caller buffer)",
+                (long long)need, (long long)MOE_NOALLOC_SCRATCH_BYTES);
+  if (a->T == 0) return moe_w4a16_grouped_ffn(a, stream);
+  void* ws = nullptr;
+  const int rc = scratch_for_current_device(&ws);
+  if (rc) return rc;
+  moe_ffn_args b = *a;
+  b.workspace = ws;
+  b.workspace_bytes = (int64_t)MOE_NOALLOC_SCRATCH_BYTES;
+  return moe_w4a16_grouped_ffn(&b, stream);
 }

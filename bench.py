@@ -548,13 +548,45 @@ def run_large(Ts, reps=10, warmup=3):
                         "whole-step time (route + align + grouped FFN + combine) per T", **res}
 
 
-def run_slot_cache(steps, warmup=8, T=16, variants=((16, False), (16, True), (64, False))):
-    """Expert slot cache (OLMoE shape, 16 layers, Zipf(1.2) popularity with AR(1)
-    step locality): experts in pinned host memory, S device slots per layer, misses
-    copied by hipMemcpyAsync on a side stream before each FFN round.  Variants
-    (S, prefetch): with prefetch, while layer l runs, the experts layer l+1 needed
-    at the previous step are copied into its slots (the copy stream stays busy
-    through the route / read-back / compute phases)."""
+def h2d_ceiling(store, slots, streams=2, reps=3):
+    """Pinned host -> device copies of whole expert blobs, back to back, alternating
+    over `streams` copy streams: the host-link rate the slot cache can reach."""
+    import torch
+    n = store.shape[0]
+    ss = [torch.cuda.Stream() for _ in range(streams)]
+    best = 1e9
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n):
+            with torch.cuda.stream(ss[i % streams]):
+                slots[i % slots.shape[0]].copy_(store[i], non_blocking=True)
+        torch.cuda.synchronize()
+        best = min(best, time.perf_counter() - t0)
+    return n * store.shape[1] / best / 1e9
+
+
+SLOT_VARIANTS = (
+    # name, slots, policy (0 LRU, 1 cost-aware), copy streams, next-layer prefetch copies per layer
+    ("S=16 lru 1-stream", 16, 0, 1, 0),
+    ("S=16 lru 2-streams", 16, 0, 2, 0),
+    ("S=16 cost-aware 2-streams", 16, 1, 2, 0),
+    ("S=16 cost-aware 2-streams next-layer-prefetch", 16, 1, 2, 1),
+    ("S=32 cost-aware 2-streams", 32, 1, 2, 0),
+    ("S=32 cost-aware 2-streams next-layer-prefetch", 32, 1, 2, 4),
+    ("S=64", 64, 0, 2, 0),
+)
+
+
+def run_slot_cache(steps, warmup=8, T=16, variants=SLOT_VARIANTS):
+    """Expert slot cache (OLMoE shape, 16 layers, Zipf(1.2) popularity, AR(1) step
+    locality and layer inputs correlated along the residual stream): experts in
+    pinned host memory, S device slots per layer, misses copied by hipMemcpyAsync
+    on one or two copy streams before each FFN round.  Variants: replacement policy
+    (LRU / cost-aware), copy streams, and the next-layer prefetch: layer l+1's
+    router applied to layer l's input predicts its experts (read back with layer
+    l's routing in one sync) and up to N of them are copied into layer l+1's slots
+    while layer l runs."""
     import torch
     import synth
     import w4a16_grouped_expert_amd as moe
@@ -571,47 +603,62 @@ def run_slot_cache(steps, warmup=8, T=16, variants=((16, False), (16, True), (64
         del bank
         stores.append((store, synth.router_weight(wl, l).cuda()))
     torch.cuda.empty_cache()
+    probe_slots = torch.empty((16, B), dtype=torch.uint8, device="cuda")
+    ceiling = {"one_stream_gbps": round(h2d_ceiling(stores[0][0], probe_slots, 1), 2),
+               "two_streams_gbps": round(h2d_ceiling(stores[0][0], probe_slots, 2), 2)}
+    del probe_slots
     route = moe.alloc_route(T, s.E, s.k, "cuda")
+    pred = moe.alloc_route(T, s.E, s.k, "cuda")
     al = moe.alloc_align(T, s.k, s.E, "cuda")
     counter = moe.alloc_counter("cuda")
     ws = moe.alloc_workspace(T, s.d, s.I, s.E, s.k, moe.MODE_DECODE)
     out = torch.empty((T, s.d), dtype=torch.bfloat16, device="cuda")
-    seqs = [[x.cuda() for x in synth.ar1_activation_sequence(wl, T, l, warmup + steps, device="cpu")]
-            for l in range(wl.layers)]
+    seqs = [[x.cuda() for x in row] for row in synth.residual_stream_sequence(wl, T, warmup + steps)]
     main = torch.cuda.current_stream()
     copy = torch.cuda.Stream()
     probe = []
 
-    def one(S, prefetch):
+    def one(S, policy, n_streams, n_pref, capture_probe):
         torch.cuda.synchronize()
         base = torch.cuda.memory_allocated()
         torch.cuda.reset_peak_memory_stats()
         layers = []
         for store, wr in stores:
             slots = torch.zeros((S, B), dtype=torch.uint8, device="cuda")
-            layers.append({"wr": wr, "slots": slots, "cache": moe.SlotCache(s.E, S, B, store, slots),
+            cache = moe.SlotCache(s.E, S, B, store, slots)
+            cache.configure(policy, 0.9, n_streams)
+            layers.append({"wr": wr, "slots": slots, "cache": cache,
                            "table": torch.full((s.E,), -1, dtype=torch.int32, device="cuda"),
-                           "ffn_done": torch.cuda.Event(), "prev": set()})
+                           "ffn_done": torch.cuda.Event()})
         done = torch.cuda.Event()
         for L in layers:
             L["ffn_done"].record(main)
-        L_ = len(layers)
+        n_layers = len(layers)
 
         def step(st, capture=False):
             rounds = misses = pref = floor = 0
             for l, L in enumerate(layers):
-                x = seqs[l][st]
+                x = seqs[st][l]
                 moe.moe_route_align_into(x, L["wr"], s.k, route, al, counter)
-                need = {w[0] for w in moe.active_experts(al)}  # the one D2H sync per layer
+                if n_pref and l + 1 < n_layers:
+                    # the next layer's router on this layer's input: its predicted experts
+                    moe.moe_route_into(x, layers[l + 1]["wr"], s.k, pred)
+                    both = torch.cat([al.active, pred.ids.reshape(-1)]).cpu()  # the one D2H sync per layer
+                    U = int(both[0])
+                    need = {int(v) for v in both[4:4 + 4 * U:4]}
+                    predicted = {int(v) for v in both[4 + 4 * s.E:]}
+                else:
+                    need = {w[0] for w in moe.active_experts(al)}  # the one D2H sync per layer
+                    predicted = None
                 floor += max(0, len(need) - S)  # copies no policy avoids: the rounds cycle the needed set
+                L["cache"].begin_step(need)
                 pending = set(need)
                 first = True
                 while pending:
                     got, nh, nm = L["cache"].load(pending, L["table"], copy, L["ffn_done"], done)
-                    if first and prefetch:
-                        nxt = layers[(l + 1) % L_]
-                        if nxt["prev"]:
-                            pref += nxt["cache"].prefetch(nxt["prev"], S, copy, nxt["ffn_done"])
+                    if first and predicted is not None:
+                        nxt = layers[l + 1]
+                        pref += nxt["cache"].prefetch(predicted, n_pref, copy, nxt["ffn_done"])
                     first = False
                     main.wait_event(done)
                     pending -= got
@@ -620,7 +667,6 @@ def run_slot_cache(steps, warmup=8, T=16, variants=((16, False), (16, True), (64
                     L["ffn_done"].record(main)
                     rounds += 1
                     misses += nm
-                L["prev"] = need
                 if capture and l == 0:
                     probe.append((x, out.clone(), route.ids[:T].clone()))
             return rounds, misses, pref, floor
@@ -632,7 +678,7 @@ def run_slot_cache(steps, warmup=8, T=16, variants=((16, False), (16, True), (64
         t0 = time.perf_counter()
         rounds = misses = pref = floor = 0
         for st in range(warmup, warmup + steps):
-            r, m, p, fl = step(st, capture=(st == warmup + steps - 1 and S == 16 and not prefetch))
+            r, m, p, fl = step(st, capture=(capture_probe and st == warmup + steps - 1))
             rounds += r
             misses += m
             pref += p
@@ -647,24 +693,28 @@ def run_slot_cache(steps, warmup=8, T=16, variants=((16, False), (16, True), (64
             L["cache"].close()
         del layers
         torch.cuda.empty_cache()
+        gbps = (miss + pref) * B / sec / 1e9
         return {"tokens_per_s": round(steps * T * wl.layers / sec, 1), "ms_per_step": round(1e3 * sec / steps, 3),
                 "hit_rate": round(hits / max(1, hits + miss), 4), "misses_per_step": round(miss / steps, 2),
                 "miss_floor_per_step": round(floor / steps, 2),
                 "prefetches_per_step": round(pref / steps, 2),
+                "copies_per_step": round((miss + pref) / steps, 2),
                 "rounds_per_layer": round(rounds / (steps * wl.layers), 3),
-                "h2d_gbps": round((miss + pref) * B / sec / 1e9, 2),
+                "h2d_gbps": round(gbps, 2), "h2d_frac_of_ceiling": round(gbps / ceiling["two_streams_gbps"], 3),
                 "slot_bytes_per_layer": S * B, "slot_bytes_total": S * B * wl.layers,
                 "peak_device_bytes_during_run": int(peak)}
 
     res = {"workload": f"olmoe_slot: 16 MoE layers, d=2048, E=64, top-8, I=1024, W4 g128; 64 experts per layer in "
-                       f"pinned host memory, S device slots per layer, Zipf(1.2) popularity, AR(1) locality, T={T}",
+                       f"pinned host memory, S device slots per layer, Zipf(1.2) popularity, AR(1) step locality "
+                       f"(0.9), layer inputs correlated along the residual stream (0.9), T={T}",
            "resident_bytes_all_experts": s.E * B * wl.layers,
+           "h2d_ceiling": {**ceiling, "what": "back-to-back pinned copies of whole expert blobs (3.24 MB)"},
            "timing": "wall clock over the timed steps (host round trip per layer for the needed set included)"}
-    for S, pf in variants:
-        res[f"S={S}" + (" prefetch" if pf else "")] = one(S, pf)
+    for name, S, policy, n_streams, n_pref in variants:
+        res[name] = one(S, policy, n_streams, n_pref, capture_probe=(name == variants[0][0]))
     del stores
     torch.cuda.empty_cache()
-    # layer 0 of the last timed S=16 step (input, output, routing) for the parity check
+    # layer 0 of the last timed step of the first variant (input, output, routing) for the parity check
     probe = [(x.cpu(), o.cpu(), ids.cpu().numpy()) for x, o, ids in probe[:1]]
     return res, (probe[0] if probe else None)
 
@@ -826,7 +876,7 @@ def parity_verdicts(args, threads, slot_probe=None):
         wl = synth.OLMOE_SLOT
         x, out, ids = slot_probe
         bank_o = _oracle_bank(wl, 0, set(ids.reshape(-1).tolist()), threads)
-        verdict("olmoe_slot S=16 (last timed step, layer 0)", wl, bank_o, x, synth.router_weight(wl, 0), out,
+        verdict("olmoe_slot S=16 lru (last timed step, layer 0)", wl, bank_o, x, synth.router_weight(wl, 0), out,
                 torch.from_numpy(ids))
     torch.cuda.empty_cache()
     return res, dec_bank

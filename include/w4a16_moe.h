@@ -333,9 +333,10 @@ int moe_mat_grouped_ffn(const moe_ffn_args* args, float tau, void* stream);
  *   tables for the expert->slot map; nothing is allocated afterwards.
  * slot_cache_load: one round for the pending experts (host bitmask, ceil(E/64)
  *   words).  Takes the pending experts already resident (hits), then missing ones
- *   in ascending id until the S slots are full; each miss replaces the least
- *   recently used slot not holding a hit (empty slots first, ties to the lower
- *   slot).  On copy_stream, after wait_event (may be NULL; record it after the
+ *   until the S slots are full; each miss replaces a slot not holding a hit.
+ *   LRU policy (the default): misses in ascending id, victims least recently
+ *   used (empty slots first, ties to the lower slot); moe_slot_cache_configure
+ *   selects the cost-aware order instead.  On copy_stream, after wait_event (may be NULL; record it after the
  *   last kernel that read the slots), it enqueues the H2D copies of the misses,
  *   then the copy of the round's expert->slot table into slot_table_dev ([E]
  *   int32: slot of each expert of this round, -1 for every other expert), and
@@ -368,6 +369,35 @@ int slot_cache_load(moe_slot_cache* cache, const uint64_t* pending_mask, uint64_
  */
 int slot_cache_prefetch(moe_slot_cache* cache, const uint64_t* predicted_mask, int max_copies,
                         int32_t* n_copies, void* copy_stream, void* wait_event);
+
+/*
+ * moe_slot_cache_configure -- replacement policy and copy streams of a cache
+ * (page "MoE-APEX: An Efficient MoE Inference System with Adaptive Precision
+ * Expert Offloading", "Why it works": prefetching hides the transfer, a
+ * cost-aware cache keeps the right experts resident).
+ *  policy  MOE_SLOT_POLICY_LRU (the default, as described above) or
+ *          MOE_SLOT_POLICY_COST: every expert carries an average u of "needed in
+ *          a step" over the sequence (u <- decay * u + (1 - decay) * [needed],
+ *          updated by slot_cache_begin_step); victims are empty slots first, then
+ *          the lowest expected reload cost (u times the slot's bytes, the same for
+ *          every slot), then least recently used, then the lower slot; misses enter
+ *          a round in increasing u (ties ascending id) and prefetches in
+ *          decreasing u (ties ascending id).
+ *  decay   in [0, 1).
+ *  copy_streams  1, or 2: the cache creates one stream of its own (default
+ *          priority) and alternates the copies of a call between the caller's
+ *          copy stream and it (two DMA engines share the host link); before its
+ *          copies the second stream waits for wait_event, and the caller's copy
+ *          stream waits for them before the slot table copy and done_event, so
+ *          the ordering seen by the caller is unchanged.
+ *  Errors: MOE_ERR_INVALID_ARG, MOE_ERR_HIP (stream or event creation).
+ * slot_cache_begin_step -- the needed experts of a new step (host bitmask,
+ *  ceil(E/64) words), before its first slot_cache_load: updates the usage
+ *  averages (every policy keeps them; only MOE_SLOT_POLICY_COST uses them).
+ */
+enum moe_slot_policy { MOE_SLOT_POLICY_LRU = 0, MOE_SLOT_POLICY_COST = 1 };
+int moe_slot_cache_configure(moe_slot_cache* cache, int policy, double decay, int copy_streams);
+int slot_cache_begin_step(moe_slot_cache* cache, const uint64_t* needed_mask);
 /* Current slot contents ([S] expert id or -1) and cumulative hit / miss counts. */
 int moe_slot_cache_state(const moe_slot_cache* cache, int32_t* slot_expert,
                          int64_t* hits, int64_t* misses);

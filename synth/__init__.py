@@ -175,6 +175,31 @@ def ar1_activation_sequence(wl: Workload, T: int, layer: int, steps: int, device
     return out
 
 
+def residual_stream_sequence(wl: Workload, T: int, steps: int, rho_layer: float = 0.9, device="cpu"):
+    """Decode steps of every layer's MoE input, [steps][layers] of [T, d] bf16, with
+    locality across steps and across layers: each layer has its own AR(1) sequence
+    a (ar1_activation_sequence, coefficient ar_rho over steps), and
+    x[s][0] = a_0[s], x[s][l+1] = rho_layer * x[s][l] + sqrt(1 - rho_layer^2) * a_{l+1}[s]
+    (consecutive layers see correlated inputs, as along a residual stream; every
+    x[.][l] keeps unit variance and step coefficient ar_rho).  Mixed in float32,
+    each input rounded once to bf16; channel 0 is the bias channel (1.0) when the
+    workload uses Zipf-biased routing."""
+    per = [ar1_activation_sequence(wl, T, l, steps, device) for l in range(wl.layers)]
+    c = math.sqrt(1.0 - rho_layer * rho_layer)
+    out = []
+    for st in range(steps):
+        prev = per[0][st].to(torch.float32)
+        row = [per[0][st]]
+        for l in range(1, wl.layers):
+            cur = rho_layer * prev + c * per[l][st].to(torch.float32)
+            if wl.router == "zipf":
+                cur[:, 0] = 1.0
+            row.append(cur.to(torch.bfloat16))
+            prev = cur
+        out.append(row)
+    return out
+
+
 def random_topk_ids(T: int, E: int, k: int, seed: int) -> torch.Tensor:
     """Distinct expert ids per token (uniform), int32 [T, k]; used for permutation tests."""
     g = _gen(seed, "cpu")

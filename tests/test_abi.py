@@ -115,6 +115,8 @@ def test_host_side_argument_checks(L):
     assert L.moe_slot_cache_create(0, 16, 100, vp, vp, ctypes.byref(h)) == 1
     assert L.moe_slot_cache_create(64, 16, 100, None, vp, ctypes.byref(h)) == 1
     assert L.slot_cache_load(None, None, None, None, None, None, None, None, None) == 1
+    assert L.moe_slot_cache_configure(None, 0, 0.9, 1) == 1
+    assert L.slot_cache_begin_step(None, None) == 1
     assert L.moe_timing_read(99, None, None) == 1
 
 

@@ -10,7 +10,7 @@ import torch
 import synth
 import w4a16_grouped_expert_amd as moe
 from oracle import ffn as offn
-from oracle.slot_cache import LRUSlotCache
+from oracle.slot_cache import POLICY_COST, POLICY_LRU, SlotCacheSim
 
 from gpu_helpers import bits, check_layer_out, oracle_bank, say, warm_bank
 
@@ -18,7 +18,8 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def run_slot_steps(wl, S, steps, T, seed_layer=0, prefetch=None, check_oracle=True):
+def run_slot_steps(wl, S, steps, T, seed_layer=0, prefetch=None, check_oracle=True, policy=POLICY_LRU,
+                   copy_streams=1, decay=0.9):
     """Decode steps through an S-slot cache.  prefetch: None, "prev" (at the start of
     a step, the previous step's experts) or "next" (after a step's last round, the
     next step's experts from its routing: a predictor that can differ from the
@@ -34,7 +35,8 @@ def run_slot_steps(wl, S, steps, T, seed_layer=0, prefetch=None, check_oracle=Tr
     store.copy_(bank.cpu())
     slots = torch.zeros((S, B), dtype=torch.uint8, device=DEV)
     cache = moe.SlotCache(s.E, S, B, store, slots)
-    sim = LRUSlotCache(s.E, S)
+    cache.configure(policy, decay, copy_streams)
+    sim = SlotCacheSim(s.E, S, policy, decay)
     table = torch.full((s.E,), -1, dtype=torch.int32, device=DEV)
     main = torch.cuda.current_stream()
     copy = torch.cuda.Stream()
@@ -63,6 +65,7 @@ def run_slot_steps(wl, S, steps, T, seed_layer=0, prefetch=None, check_oracle=Tr
             n_pref += n
         x, r, a, need = route(st)
         prev = need
+        cache.begin_step(need)
         expect = sim.step(need)
         pending = set(need)
         out = torch.empty((T, s.d), dtype=torch.bfloat16, device=DEV)
@@ -154,3 +157,16 @@ def test_slot_cache_injected_copy_failure(monkeypatch):
     # the first two copies went through, the third failed: its slot is empty, never half-loaded
     assert slot_state[:2] == [0, 1] and slot_state[2] == -1
     cache.close()
+
+
+@pytest.mark.parametrize("wl,S,T,pf", [(synth.TINY, 3, 16, None), (synth.OLMOE_SLOT, 16, 16, None),
+                                       (synth.OLMOE_SLOT, 16, 16, "next")])
+def test_slot_cache_cost_aware_two_copy_streams(wl, S, T, pf):
+    # the cost-aware policy (usage averages, victims by expected reload cost) with
+    # the copies spread over two streams: sequence equal to the simulator's,
+    # outputs equal to the resident path and within the tolerance of the oracle
+    say(f"slot cache cost-aware, 2 copy streams, {wl.name} S={S} T={T} prefetch={pf}")
+    n_rounds, hits, misses, n_pref = run_slot_steps(wl, S, 6, T, prefetch=pf, policy=POLICY_COST,
+                                                    copy_streams=2, decay=0.5)
+    say(f"  rounds {n_rounds} hits {hits} misses {misses} prefetched {n_pref}")
+    assert misses > 0

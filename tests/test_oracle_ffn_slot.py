@@ -10,7 +10,7 @@ import math
 import numpy as np
 
 from oracle import bf16, ffn, quant, route
-from oracle.slot_cache import LRUSlotCache
+from oracle.slot_cache import POLICY_COST, LRUSlotCache, SlotCacheSim
 
 
 def rand_bits(shape, std, seed):
@@ -167,3 +167,53 @@ def test_lru_never_evicts_a_hit_and_covers_all_needed():
             covered |= set(subset)
             pending -= set(subset)
         assert covered == need
+
+
+def test_cost_aware_hand_traced():
+    # decay 0.5: usage values are dyadic fractions, exact in float64
+    c = SlotCacheSim(num_experts=8, num_slots=3, policy=POLICY_COST, decay=0.5)
+    # step 1 {5, 1}: u1 = u5 = 0.5; misses by (u, id) -> [1, 5] into the empty slots 0, 1
+    assert c.step({5, 1}) == [([1, 5], [], [(1, 0), (5, 1)])]
+    # step 2 {1, 2, 7}: u1 = .75, u2 = u7 = .5, u5 = .25; hit 1; 2 -> empty slot 2, 7 -> slot 1 (expert 5)
+    assert c.step({1, 2, 7}) == [([1, 2, 7], [1], [(2, 2), (7, 1)])]
+    assert c.usage[1] == 0.75 and c.usage[5] == 0.25 and c.usage[7] == 0.5
+    # step 3 {0, 2, 3, 4, 6}: u0 = u3 = u4 = u6 = .5, u1 = .375, u7 = .25, u2 = .75; round 1: hit 2,
+    # misses 0, 3 (u ties, by id); victims by usage: slot 1 (expert 7, .25) before slot 0
+    # (expert 1, .375) -- LRU would take slot 0 first (equal stamps, lower slot)
+    # round 2: 4, 6 evict slots 0 (expert 3, .5, lower slot) and 1 (expert 0, .5); expert 2 (.75) stays
+    assert c.step({0, 3, 4, 2, 6}) == [([0, 2, 3], [2], [(0, 1), (3, 0)]), ([4, 6], [], [(4, 0), (6, 1)])]
+    assert c.slot_expert == [4, 6, 2]
+    # step 4 {1, 2}: hit 2; 1 -> slot 0 (experts 4 and 6 tie on usage .25 and stamp: lower slot)
+    assert c.step({1, 2}) == [([1, 2], [2], [(1, 0)])]
+    assert c.slot_expert == [1, 6, 2]
+    # a later round evicts the finished expert with the lower usage
+    d = SlotCacheSim(num_experts=8, num_slots=2, policy=POLICY_COST, decay=0.5)
+    d.step({0})                                      # u0 = .5
+    r = d.step({0, 3, 5})                            # u0 = .75, u3 = u5 = .5: hit 0, then 3 (id order)
+    assert r[0] == ([0, 3], [0], [(3, 1)])
+    assert r[1] == ([5], [], [(5, 1)])               # 5 evicts expert 3 (u .5) rather than 0 (u .75)
+    assert d.slot_expert == [0, 5]
+
+
+def test_cost_aware_prefetch_hand_traced():
+    c = SlotCacheSim(num_experts=8, num_slots=3, policy=POLICY_COST, decay=0.5)
+    c.step({5, 1})
+    c.step({1, 2, 7})                                # slots [1, 7, 2]; u1 .75, u2 = u7 .5, u5 .25
+    # predicted {2, 5, 6}: 2 resident (kept); wanted 5 (u .25) before 6 (u 0); one copy into the
+    # lowest-usage unpredicted slot: slot 1 (expert 7, .5) before slot 0 (expert 1, .75)
+    assert c.prefetch({2, 5, 6}, 1) == [(5, 1)]
+    assert c.slot_expert == [1, 5, 2]
+
+
+def test_policies_cover_every_needed_expert_once_per_step():
+    rng = np.random.default_rng(11)
+    for policy in (0, POLICY_COST):
+        c = SlotCacheSim(num_experts=64, num_slots=16, policy=policy, decay=0.9)
+        for _ in range(150):
+            need = set(rng.choice(64, size=rng.integers(1, 40), replace=False).tolist())
+            rounds = c.step(need)
+            got = [e for sub, _, _ in rounds for e in sub]
+            assert sorted(got) == sorted(need)               # each needed expert in exactly one round
+            copies = [e for _, _, cp in rounds for e, _ in cp]
+            assert len(copies) == len(set(copies))           # never copied twice in a step
+            assert all(len(sub) <= 16 for sub, _, _ in rounds)

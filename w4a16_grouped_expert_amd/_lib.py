@@ -85,6 +85,8 @@ SIGNATURES = {
     "slot_cache_load": (c_int, [c_vp, c_u64p, c_u64p, c_vp, c_i32p, c_i32p, c_vp, c_vp, c_vp]),
     "moe_slot_cache_state": (c_int, [c_vp, c_i32p, c_i64p, c_i64p]),
     "slot_cache_prefetch": (c_int, [c_vp, c_u64p, c_int, c_i32p, c_vp, c_vp]),
+    "moe_slot_cache_configure": (c_int, [c_vp, c_int, c_double, c_int]),
+    "slot_cache_begin_step": (c_int, [c_vp, c_u64p]),
     "moe_timing_enable": (c_int, [c_int]),
     "moe_timing_reset": (c_int, []),
     "moe_timing_read": (c_int, [c_int, ctypes.POINTER(c_double), c_i64p]),

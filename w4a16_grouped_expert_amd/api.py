@@ -486,6 +486,23 @@ class SlotCache:
         got = {e for e in range(self.E) if (rm[e >> 6] >> (e & 63)) & 1}
         return got, nh.value, nm.value
 
+    POLICY_LRU, POLICY_COST = 0, 1
+
+    def configure(self, policy: int = 0, decay: float = 0.9, copy_streams: int = 1):
+        """Replacement policy (POLICY_LRU / POLICY_COST), usage decay and 1 or 2 copy streams."""
+        check("moe_slot_cache_configure", lib().moe_slot_cache_configure(self._h, int(policy), float(decay),
+                                                                         int(copy_streams)))
+
+    def _mask(self, experts):
+        m = (ctypes.c_uint64 * self.words)()
+        for e in experts:
+            m[e >> 6] |= 1 << (e & 63)
+        return m
+
+    def begin_step(self, needed: set):
+        """The needed experts of a new step (usage averages of the cost-aware policy)."""
+        check("slot_cache_begin_step", lib().slot_cache_begin_step(self._h, self._mask(needed)))
+
     def prefetch(self, predicted: set, max_copies: int, copy_stream, wait_event=None) -> int:
         """Copy predicted experts ahead of their round; returns the number of copies."""
         if wait_event is not None and wait_event.cuda_event == 0:

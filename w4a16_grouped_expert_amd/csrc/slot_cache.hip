@@ -2,9 +2,18 @@
 // "Every Expert Counts: ExactMoE for Memory-Efficient W4A16 Inference",
 // Abstract: quantised experts stored in pinned host memory and executed through
 // a configurable GPU-resident slot cache).  Host-side bookkeeping only: the
-// policy (hits first, then misses in ascending id; victims = empty slots, then
-// least recently used, ties to the lower slot) runs on the CPU and the data
-// moves by hipMemcpyAsync on the caller's copy stream.
+// policy runs on the CPU and the data moves by hipMemcpyAsync on the caller's
+// copy stream (and, when configured, a second stream of the cache's own, so two
+// copy engines share the host link).
+// Policies: LRU (hits first, then misses in ascending id; victims = empty slots,
+// then least recently used, ties to the lower slot) and cost-aware (page
+// "MoE-APEX: An Efficient MoE Inference System with Adaptive Precision Expert
+// Offloading", "Why it works": a sequence-level cache keeps resident the experts
+// whose reload would cost most): every expert carries an exponential average of
+// "needed in this step" over the sequence; victims go by expected reload cost
+// (that average times the slot's bytes), then least recently used, then lower
+// slot; misses enter a round in increasing expected cost, so the experts likely
+// needed again are loaded last and stay.
 #include <cstdlib>
 #include <cstring>
 #include <vector>
@@ -20,6 +29,11 @@ struct moe_slot_cache {
   std::vector<int64_t> slot_stamp; // [S] last round that used the slot, -1 if never
   std::vector<int> expert_slot;    // [E] slot of expert or -1
   int64_t clock = 0, hits = 0, misses = 0, prefetches = 0;
+  int policy = MOE_SLOT_POLICY_LRU;
+  double decay = 0.9;
+  std::vector<double> usage;       // [E] cost-aware: average of "needed in a step"
+  hipStream_t aux = nullptr;       // second copy stream (copy_streams = 2)
+  hipEvent_t aux_done = nullptr;   // the aux stream's copies, joined into the caller's copy stream
   // ring of pinned staging tables for the per-round expert->slot map
   static constexpr int kRing = 8;
   int32_t* tables = nullptr;       // [kRing][E], pinned
@@ -48,6 +62,7 @@ extern "C" int moe_slot_cache_create(int E, int S, int64_t blob_bytes, const voi
   c->slot_expert.assign(S, -1);
   c->slot_stamp.assign(S, -1);
   c->expert_slot.assign(E, -1);
+  c->usage.assign(E, 0.0);
   if (hipHostMalloc(reinterpret_cast<void**>(&c->tables), sizeof(int32_t) * E * moe_slot_cache::kRing,
                     hipHostMallocDefault) != hipSuccess) {
     delete c;
@@ -75,10 +90,105 @@ extern "C" int moe_slot_cache_destroy(moe_slot_cache* c) {
     if (c->table_used[i]) (void)hipEventSynchronize(c->table_ev[i]);
     (void)hipEventDestroy(c->table_ev[i]);
   }
+  if (c->aux) {
+    (void)hipStreamSynchronize(c->aux);
+    (void)hipStreamDestroy(c->aux);
+    (void)hipEventDestroy(c->aux_done);
+  }
   (void)hipHostFree(c->tables);
   delete c;
   return MOE_OK;
 }
+
+extern "C" int moe_slot_cache_configure(moe_slot_cache* c, int policy, double decay, int copy_streams) {
+  clear_error();
+  MOE_CHECK_ARG(c != nullptr, MOE_ERR_INVALID_ARG, "moe_slot_cache_configure: cache is NULL");
+  MOE_CHECK_ARG(policy == MOE_SLOT_POLICY_LRU || policy == MOE_SLOT_POLICY_COST, MOE_ERR_INVALID_ARG,
+                "moe_slot_cache_configure: unknown policy %d", policy);
+  MOE_CHECK_ARG(decay >= 0.0 && decay < 1.0, MOE_ERR_INVALID_ARG, "moe_slot_cache_configure: decay %g not in [0, 1)",
+                decay);
+  MOE_CHECK_ARG(copy_streams == 1 || copy_streams == 2, MOE_ERR_INVALID_ARG,
+                "moe_slot_cache_configure: copy_streams must be 1 or 2, got %d", copy_streams);
+  if (copy_streams == 2 && !c->aux) {
+    if (hipStreamCreateWithFlags(&c->aux, hipStreamNonBlocking) != hipSuccess) {
+      c->aux = nullptr;
+      set_error("moe_slot_cache_configure: stream creation failed");
+      return MOE_ERR_HIP;
+    }
+    if (hipEventCreateWithFlags(&c->aux_done, hipEventDisableTiming) != hipSuccess) {
+      (void)hipStreamDestroy(c->aux);
+      c->aux = nullptr;
+      set_error("moe_slot_cache_configure: event creation failed");
+      return MOE_ERR_HIP;
+    }
+  } else if (copy_streams == 1 && c->aux) {
+    (void)hipStreamSynchronize(c->aux);
+    (void)hipStreamDestroy(c->aux);
+    (void)hipEventDestroy(c->aux_done);
+    c->aux = nullptr;
+    c->aux_done = nullptr;
+  }
+  c->policy = policy;
+  c->decay = decay;
+  return MOE_OK;
+}
+
+extern "C" int slot_cache_begin_step(moe_slot_cache* c, const uint64_t* needed_mask) {
+  clear_error();
+  MOE_CHECK_ARG(c && needed_mask, MOE_ERR_INVALID_ARG, "slot_cache_begin_step: null argument");
+  for (int e = 0; e < c->E; ++e) {
+    const double need = ((needed_mask[e >> 6] >> (e & 63)) & 1ull) ? 1.0 : 0.0;
+    c->usage[e] = c->decay * c->usage[e] + (1.0 - c->decay) * need;
+  }
+  return MOE_OK;
+}
+
+namespace {
+
+// victim order over the candidate slots: empty first; cost-aware: expected reload
+// cost (usage; every slot reloads the same bytes), then last use, then slot;
+// LRU: last use, then slot
+void order_victims(const moe_slot_cache* c, std::vector<int>& v) {
+  if (c->policy == MOE_SLOT_POLICY_COST) {
+    std::sort(v.begin(), v.end(), [&](int a, int b) {
+      const int ea = c->slot_expert[a], eb = c->slot_expert[b];
+      if ((ea >= 0) != (eb >= 0)) return ea < 0;
+      if (ea >= 0 && c->usage[ea] != c->usage[eb]) return c->usage[ea] < c->usage[eb];
+      if (c->slot_stamp[a] != c->slot_stamp[b]) return c->slot_stamp[a] < c->slot_stamp[b];
+      return a < b;
+    });
+  } else {
+    std::stable_sort(v.begin(), v.end(), [&](int a, int b) { return c->slot_stamp[a] < c->slot_stamp[b]; });
+  }
+}
+
+// the copy of expert e into slot sl: the i-th copy of a call goes to the caller's
+// stream (even i) or the cache's second stream (odd i, when configured)
+hipError_t copy_expert(moe_slot_cache* c, int e, int sl, int i, hipStream_t s) {
+  if (c->fail_after == 0) return hipErrorInvalidValue;
+  if (c->fail_after > 0) --c->fail_after;
+  hipStream_t cs = (c->aux && (i & 1)) ? c->aux : s;
+  return hipMemcpyAsync(c->device_slots + (int64_t)sl * c->blob_bytes, c->host_store + (int64_t)e * c->blob_bytes,
+                        c->blob_bytes, hipMemcpyHostToDevice, cs);
+}
+
+// before the copies: the second stream waits for what the caller's stream waits for
+hipError_t aux_wait(moe_slot_cache* c, hipStream_t s, void* wait_event) {
+  if (!c->aux) return hipSuccess;
+  if (wait_event) return hipStreamWaitEvent(c->aux, (hipEvent_t)wait_event, 0);
+  // no event: order the aux stream after the work already on the caller's stream
+  hipError_t e = hipEventRecord(c->aux_done, s);
+  return e == hipSuccess ? hipStreamWaitEvent(c->aux, c->aux_done, 0) : e;
+}
+
+// after the copies: the caller's stream waits for the second stream's copies
+hipError_t aux_join(moe_slot_cache* c, hipStream_t s, int n_copies) {
+  if (!c->aux || n_copies < 2) return hipSuccess;
+  hipError_t e = hipEventRecord(c->aux_done, c->aux);
+  return e == hipSuccess ? hipStreamWaitEvent(s, c->aux_done, 0) : e;
+}
+
+}  // namespace
 
 extern "C" int slot_cache_load(moe_slot_cache* c, const uint64_t* pending_mask, uint64_t* round_mask,
                                int32_t* slot_table_dev, int32_t* n_hits, int32_t* n_misses, void* copy_stream,
@@ -97,20 +207,25 @@ extern "C" int slot_cache_load(moe_slot_cache* c, const uint64_t* pending_mask, 
     else
       miss_all.push_back(e);
   }
+  if (c->policy == MOE_SLOT_POLICY_COST)
+    std::stable_sort(miss_all.begin(), miss_all.end(), [&](int a, int b) { return c->usage[a] < c->usage[b]; });
   const int n_m = std::min<int>((int)miss_all.size(), S - (int)hits.size());
   std::vector<char> hit_slot(S, 0);
   for (int e : hits) hit_slot[c->expert_slot[e]] = 1;
   std::vector<int> victims;
   for (int sl = 0; sl < S; ++sl)
     if (!hit_slot[sl]) victims.push_back(sl);
-  std::stable_sort(victims.begin(), victims.end(),
-                   [&](int a, int b) { return c->slot_stamp[a] < c->slot_stamp[b]; });
+  order_victims(c, victims);
 
   if (wait_event) {
     if (hipStreamWaitEvent(s, (hipEvent_t)wait_event, 0) != hipSuccess) {
       set_error("slot_cache_load: hipStreamWaitEvent failed");
       return MOE_ERR_HIP;
     }
+  }
+  if (n_m > 1 && aux_wait(c, s, wait_event) != hipSuccess) {
+    set_error("slot_cache_load: second copy stream could not be ordered");
+    return MOE_ERR_HIP;
   }
   std::vector<int> loaded;
   int rc = MOE_OK;
@@ -120,14 +235,7 @@ extern "C" int slot_cache_load(moe_slot_cache* c, const uint64_t* pending_mask, 
     if (old >= 0) c->expert_slot[old] = -1;
     c->slot_expert[sl] = -1;
     c->slot_stamp[sl] = -1;
-    hipError_t err = hipSuccess;
-    if (c->fail_after == 0) {
-      err = hipErrorInvalidValue;
-    } else {
-      if (c->fail_after > 0) --c->fail_after;
-      err = hipMemcpyAsync(c->device_slots + (int64_t)sl * c->blob_bytes, c->host_store + (int64_t)e * c->blob_bytes,
-                           c->blob_bytes, hipMemcpyHostToDevice, s);
-    }
+    const hipError_t err = copy_expert(c, e, sl, i, s);
     if (err != hipSuccess) {
       set_error("slot_cache_load: H2D copy of expert %d into slot %d failed: %s", e, sl, hipGetErrorString(err));
       rc = MOE_ERR_HIP;
@@ -136,6 +244,10 @@ extern "C" int slot_cache_load(moe_slot_cache* c, const uint64_t* pending_mask, 
     c->slot_expert[sl] = e;
     c->expert_slot[e] = sl;
     loaded.push_back(e);
+  }
+  if (aux_join(c, s, (int)loaded.size()) != hipSuccess && !rc) {
+    set_error("slot_cache_load: second copy stream could not be joined");
+    rc = MOE_ERR_HIP;
   }
   if (rc) return rc;
 
@@ -185,14 +297,19 @@ extern "C" int slot_cache_prefetch(moe_slot_cache* c, const uint64_t* predicted_
     else
       want.push_back(e);
   }
+  if (c->policy == MOE_SLOT_POLICY_COST)
+    std::stable_sort(want.begin(), want.end(), [&](int a, int b) { return c->usage[a] > c->usage[b]; });
   std::vector<int> victims;
   for (int sl = 0; sl < S; ++sl)
     if (!keep[sl]) victims.push_back(sl);
-  std::stable_sort(victims.begin(), victims.end(),
-                   [&](int a, int b) { return c->slot_stamp[a] < c->slot_stamp[b]; });
+  order_victims(c, victims);
   const int n = std::min<int>(std::min<int>((int)want.size(), (int)victims.size()), max_copies);
   if (n > 0 && wait_event && hipStreamWaitEvent(s, (hipEvent_t)wait_event, 0) != hipSuccess) {
     set_error("slot_cache_prefetch: hipStreamWaitEvent failed");
+    return MOE_ERR_HIP;
+  }
+  if (n > 1 && aux_wait(c, s, wait_event) != hipSuccess) {
+    set_error("slot_cache_prefetch: second copy stream could not be ordered");
     return MOE_ERR_HIP;
   }
   c->clock += 1;
@@ -203,16 +320,10 @@ extern "C" int slot_cache_prefetch(moe_slot_cache* c, const uint64_t* predicted_
     if (old >= 0) c->expert_slot[old] = -1;
     c->slot_expert[sl] = -1;
     c->slot_stamp[sl] = -1;
-    hipError_t err = hipSuccess;
-    if (c->fail_after == 0) {
-      err = hipErrorInvalidValue;
-    } else {
-      if (c->fail_after > 0) --c->fail_after;
-      err = hipMemcpyAsync(c->device_slots + (int64_t)sl * c->blob_bytes, c->host_store + (int64_t)e * c->blob_bytes,
-                           c->blob_bytes, hipMemcpyHostToDevice, s);
-    }
+    const hipError_t err = copy_expert(c, e, sl, i, s);
     if (err != hipSuccess) {
       set_error("slot_cache_prefetch: H2D copy of expert %d into slot %d failed: %s", e, sl, hipGetErrorString(err));
+      (void)aux_join(c, s, done);
       if (n_copies) *n_copies = done;
       return MOE_ERR_HIP;
     }
@@ -220,6 +331,11 @@ extern "C" int slot_cache_prefetch(moe_slot_cache* c, const uint64_t* predicted_
     c->expert_slot[e] = sl;
     c->slot_stamp[sl] = c->clock;
     ++done;
+  }
+  if (aux_join(c, s, done) != hipSuccess) {
+    set_error("slot_cache_prefetch: second copy stream could not be joined");
+    if (n_copies) *n_copies = done;
+    return MOE_ERR_HIP;
   }
   c->prefetches += done;
   if (n_copies) *n_copies = done;

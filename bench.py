@@ -567,14 +567,17 @@ def h2d_ceiling(store, slots, streams=2, reps=3):
 
 
 SLOT_VARIANTS = (
-    # name, slots, policy (0 LRU, 1 cost-aware), copy streams, next-layer prefetch copies per layer
-    ("S=16 lru 1-stream", 16, 0, 1, 0),
-    ("S=16 lru 2-streams", 16, 0, 2, 0),
-    ("S=16 cost-aware 2-streams", 16, 1, 2, 0),
-    ("S=16 cost-aware 2-streams next-layer-prefetch", 16, 1, 2, 1),
-    ("S=32 cost-aware 2-streams", 32, 1, 2, 0),
-    ("S=32 cost-aware 2-streams next-layer-prefetch", 32, 1, 2, 4),
-    ("S=64", 64, 0, 2, 0),
+    # name, slots, policy (0 LRU, 1 cost-aware), copy streams, next-layer prefetch copies per layer,
+    # tau of the two-bit misses (None: four-bit experts only)
+    ("S=16 lru 1-stream", 16, 0, 1, 0, None),
+    ("S=16 lru 2-streams", 16, 0, 2, 0, None),
+    ("S=16 cost-aware 2-streams", 16, 1, 2, 0, None),
+    ("S=16 cost-aware 2-streams next-layer-prefetch", 16, 1, 2, 1, None),
+    ("S=16 cost-aware 2-streams two-bit-misses tau=0.1", 16, 1, 2, 0, 0.1),
+    ("S=16 cost-aware 2-streams two-bit-misses tau=0.14", 16, 1, 2, 0, 0.14),
+    ("S=32 cost-aware 2-streams", 32, 1, 2, 0, None),
+    ("S=32 cost-aware 2-streams next-layer-prefetch", 32, 1, 2, 4, None),
+    ("S=64", 64, 0, 2, 0, None),
 )
 
 
@@ -586,13 +589,19 @@ def run_slot_cache(steps, warmup=8, T=16, variants=SLOT_VARIANTS):
     (LRU / cost-aware), copy streams, and the next-layer prefetch: layer l+1's
     router applied to layer l's input predicts its experts (read back with layer
     l's routing in one sync) and up to N of them are copied into layer l+1's slots
-    while layer l runs."""
+    while layer l runs; and two-bit misses (page "MoE-APEX: An Efficient MoE
+    Inference System with Adaptive Precision Expert Offloading", "This paper's
+    idea"): the store holds nested two/four-bit blobs, an expert whose largest
+    routing weight in the step is below tau is loaded as its two-bit prefix and run
+    at two bits."""
+    import numpy as np
     import torch
     import synth
     import w4a16_grouped_expert_amd as moe
     wl = synth.OLMOE_SLOT
     s = wl.shape
-    stores = []
+    need_mat = any(v[5] is not None for v in variants)
+    stores, mat_stores = [], []
     for l in range(wl.layers):
         w13, w2 = synth.expert_weights(wl, l, device="cuda")
         bank, lay = moe.pack_experts(w13, w2)
@@ -600,9 +609,14 @@ def run_slot_cache(steps, warmup=8, T=16, variants=SLOT_VARIANTS):
         B = lay["blob_bytes"]
         store = torch.empty((s.E, B), dtype=torch.uint8, pin_memory=True)
         store.copy_(bank)
+        if need_mat:
+            mstore = torch.empty((s.E, B), dtype=torch.uint8, pin_memory=True)
+            mstore.copy_(moe.mat_from_w4(bank, s.d, s.I))
+            mat_stores.append(mstore)
         del bank
         stores.append((store, synth.router_weight(wl, l).cuda()))
     torch.cuda.empty_cache()
+    prefix = moe.mat_layout(s.d, s.I)["two_bit_bytes"]
     probe_slots = torch.empty((16, B), dtype=torch.uint8, device="cuda")
     ceiling = {"one_stream_gbps": round(h2d_ceiling(stores[0][0], probe_slots, 1), 2),
                "two_streams_gbps": round(h2d_ceiling(stores[0][0], probe_slots, 2), 2)}
@@ -618,15 +632,21 @@ def run_slot_cache(steps, warmup=8, T=16, variants=SLOT_VARIANTS):
     copy = torch.cuda.Stream()
     probe = []
 
-    def one(S, policy, n_streams, n_pref, capture_probe):
+    def one(S, policy, n_streams, n_pref, tau, capture_probe):
         torch.cuda.synchronize()
         base = torch.cuda.memory_allocated()
         torch.cuda.reset_peak_memory_stats()
+        mixed = tau is not None
+        tau32 = float(np.float32(tau)) if mixed else 0.0
         layers = []
-        for store, wr in stores:
+        copied = [0]
+        deviation = []
+        for li, (store, wr) in enumerate(stores):
             slots = torch.zeros((S, B), dtype=torch.uint8, device="cuda")
-            cache = moe.SlotCache(s.E, S, B, store, slots)
+            cache = moe.SlotCache(s.E, S, B, mat_stores[li] if mixed else store, slots)
             cache.configure(policy, 0.9, n_streams)
+            if mixed:
+                cache.set_prefix(prefix)
             layers.append({"wr": wr, "slots": slots, "cache": cache,
                            "table": torch.full((s.E,), -1, dtype=torch.int32, device="cuda"),
                            "ffn_done": torch.cuda.Event()})
@@ -640,6 +660,7 @@ def run_slot_cache(steps, warmup=8, T=16, variants=SLOT_VARIANTS):
             for l, L in enumerate(layers):
                 x = seqs[st][l]
                 moe.moe_route_align_into(x, L["wr"], s.k, route, al, counter)
+                full = None
                 if n_pref and l + 1 < n_layers:
                     # the next layer's router on this layer's input: its predicted experts
                     moe.moe_route_into(x, layers[l + 1]["wr"], s.k, pred)
@@ -647,6 +668,17 @@ def run_slot_cache(steps, warmup=8, T=16, variants=SLOT_VARIANTS):
                     U = int(both[0])
                     need = {int(v) for v in both[4:4 + 4 * U:4]}
                     predicted = {int(v) for v in both[4 + 4 * s.E:]}
+                elif mixed:
+                    # routing ids and weights too: an expert runs at four bits when its
+                    # largest routing weight reaches tau (the rule of the nested kernels)
+                    both = torch.cat([al.active, route.ids[:T].reshape(-1),
+                                      route.weights[:T].reshape(-1).view(torch.int32)]).cpu()
+                    U = int(both[0])
+                    need = {int(v) for v in both[4:4 + 4 * U:4]}
+                    ids_h = both[4 + 4 * s.E:4 + 4 * s.E + T * s.k].numpy()
+                    w_h = both[4 + 4 * s.E + T * s.k:].numpy().view(np.float32)
+                    full = {e for e in need if np.max(w_h[ids_h == e]) >= np.float32(tau)}
+                    predicted = None
                 else:
                     need = {w[0] for w in moe.active_experts(al)}  # the one D2H sync per layer
                     predicted = None
@@ -655,20 +687,38 @@ def run_slot_cache(steps, warmup=8, T=16, variants=SLOT_VARIANTS):
                 pending = set(need)
                 first = True
                 while pending:
-                    got, nh, nm = L["cache"].load(pending, L["table"], copy, L["ffn_done"], done)
+                    if mixed:
+                        got, nh, nm, nb = L["cache"].load_precision(pending, full, L["table"], copy, L["ffn_done"],
+                                                                    done)
+                        copied[0] += nb
+                    else:
+                        got, nh, nm = L["cache"].load(pending, L["table"], copy, L["ffn_done"], done)
+                        copied[0] += nm * B
                     if first and predicted is not None:
                         nxt = layers[l + 1]
-                        pref += nxt["cache"].prefetch(predicted, n_pref, copy, nxt["ffn_done"])
+                        n = nxt["cache"].prefetch(predicted, n_pref, copy, nxt["ffn_done"])
+                        pref += n
+                        copied[0] += n * B
                     first = False
                     main.wait_event(done)
                     pending -= got
-                    moe.moe_w4a16_grouped_ffn_into(x, route, al, L["slots"], s.I, out, ws, moe.MODE_DECODE,
-                                                   not pending, L["table"])
+                    if mixed:
+                        moe.moe_mat_grouped_ffn_into(x, route, al, L["slots"], s.I, out, ws, tau32, not pending,
+                                                     L["table"])
+                    else:
+                        moe.moe_w4a16_grouped_ffn_into(x, route, al, L["slots"], s.I, out, ws, moe.MODE_DECODE,
+                                                       not pending, L["table"])
                     L["ffn_done"].record(main)
                     rounds += 1
                     misses += nm
-                if capture and l == 0:
+                if capture and capture_probe and l == 0:
                     probe.append((x, out.clone(), route.ids[:T].clone()))
+                if capture and mixed and l == 0:
+                    # kept for the comparison with the four-bit layer after the timed steps
+                    deviation.append((x, out.clone(), moe.RouteOut(route.logits[:T].clone(), route.ids[:T].clone(),
+                                                                   route.weights[:T].clone()),
+                                      moe.AlignOut(al.offsets.clone(), al.sorted_pairs.clone(),
+                                                   al.pair_pos.clone(), al.active.clone(), None, 0)))
             return rounds, misses, pref, floor
 
         for st in range(warmup):
@@ -678,7 +728,9 @@ def run_slot_cache(steps, warmup=8, T=16, variants=SLOT_VARIANTS):
         t0 = time.perf_counter()
         rounds = misses = pref = floor = 0
         for st in range(warmup, warmup + steps):
-            r, m, p, fl = step(st, capture=(capture_probe and st == warmup + steps - 1))
+            if st == warmup:
+                copied[0] = 0
+            r, m, p, fl = step(st, capture=((capture_probe or mixed) and st == warmup + steps - 1))
             rounds += r
             misses += m
             pref += p
@@ -689,20 +741,35 @@ def run_slot_cache(steps, warmup=8, T=16, variants=SLOT_VARIANTS):
         hits = sum(b[0] - a[0] for a, b in zip(h0, h1))
         miss = sum(b[1] - a[1] for a, b in zip(h0, h1))
         peak = torch.cuda.max_memory_allocated() - base
+        up = sum(L["cache"].planes()[1] for L in layers) if mixed else 0
         for L in layers:
             L["cache"].close()
         del layers
         torch.cuda.empty_cache()
-        gbps = (miss + pref) * B / sec / 1e9
+        gbps = copied[0] / sec / 1e9
+        extra = {}
+        if mixed:
+            diff = None
+            if deviation:
+                # layer 0 of the last timed step at four bits (all-resident bank), untimed
+                x0, o0, r0, a0 = deviation[0]
+                w4 = torch.empty((s.E, B), dtype=torch.uint8, device="cuda")
+                w4.copy_(stores[0][0])
+                ref = moe.moe_w4a16_grouped_ffn(x0, r0, a0, w4, s.I, moe.MODE_DECODE).float()
+                diff = float((o0.float() - ref).abs().max() / ref.abs().max())
+                del w4
+            extra = {"tau": tau, "low_plane_completions_total": int(up),
+                     "layer0_last_step_rel_diff_vs_four_bit": round(diff, 5) if diff is not None else None}
         return {"tokens_per_s": round(steps * T * wl.layers / sec, 1), "ms_per_step": round(1e3 * sec / steps, 3),
                 "hit_rate": round(hits / max(1, hits + miss), 4), "misses_per_step": round(miss / steps, 2),
                 "miss_floor_per_step": round(floor / steps, 2),
                 "prefetches_per_step": round(pref / steps, 2),
                 "copies_per_step": round((miss + pref) / steps, 2),
                 "rounds_per_layer": round(rounds / (steps * wl.layers), 3),
+                "h2d_mb_per_step": round(copied[0] / steps / 1e6, 1),
                 "h2d_gbps": round(gbps, 2), "h2d_frac_of_ceiling": round(gbps / ceiling["two_streams_gbps"], 3),
                 "slot_bytes_per_layer": S * B, "slot_bytes_total": S * B * wl.layers,
-                "peak_device_bytes_during_run": int(peak)}
+                "peak_device_bytes_during_run": int(peak), **extra}
 
     res = {"workload": f"olmoe_slot: 16 MoE layers, d=2048, E=64, top-8, I=1024, W4 g128; 64 experts per layer in "
                        f"pinned host memory, S device slots per layer, Zipf(1.2) popularity, AR(1) step locality "
@@ -710,9 +777,9 @@ def run_slot_cache(steps, warmup=8, T=16, variants=SLOT_VARIANTS):
            "resident_bytes_all_experts": s.E * B * wl.layers,
            "h2d_ceiling": {**ceiling, "what": "back-to-back pinned copies of whole expert blobs (3.24 MB)"},
            "timing": "wall clock over the timed steps (host round trip per layer for the needed set included)"}
-    for name, S, policy, n_streams, n_pref in variants:
-        res[name] = one(S, policy, n_streams, n_pref, capture_probe=(name == variants[0][0]))
-    del stores
+    for name, S, policy, n_streams, n_pref, tau in variants:
+        res[name] = one(S, policy, n_streams, n_pref, tau, capture_probe=(name == variants[0][0]))
+    del stores, mat_stores
     torch.cuda.empty_cache()
     # layer 0 of the last timed step of the first variant (input, output, routing) for the parity check
     probe = [(x.cpu(), o.cpu(), ids.cpu().numpy()) for x, o, ids in probe[:1]]

@@ -299,10 +299,13 @@ int moe_bf16_grouped_ffn(const moe_ffn_args* args, void* stream);
  * of each tile: 32-bit words j = 0..3 with K steps 2j, 2j+1 of row L % 16,
  * columns 32 i + 8 (L / 16) + m; element m of K step 2j + t has its 2-bit field
  * at bit (5 + 2 (4t + m/2) + 16 (m % 2)) mod 32.  Expert blob: w13 high plane |
- * w13 low plane | w13 scales | w2 high | w2 low | w2 scales, each 256-byte
- * aligned (moe_mat_layout_get; same blob size as layout v1).
+ * w13 scales | w2 high plane | w2 scales | w13 low plane | w2 low plane, each
+ * 256-byte aligned (moe_mat_layout_get; same blob size as layout v1): the first
+ * two_bit_bytes hold everything an expert reads at two bits, so a two-bit load
+ * of an expert is one copy of that prefix.
  *
- * moe_mat_layout_get: section offsets and blob bytes for d, I (multiples of 256).
+ * moe_mat_layout_get: section offsets, blob bytes and the two-bit prefix for d, I
+ *   (multiples of 256).
  * moe_mat_from_w4: rewrite E four-bit blobs (layout v1, from pack_w4_g128) as
  *   layout-m1 blobs (device to device on `stream`; same codes and scales).
  * moe_mat_grouped_ffn: the grouped pass with a per-expert precision: an expert
@@ -316,6 +319,7 @@ int moe_bf16_grouped_ffn(const moe_ffn_args* args, void* stream);
  */
 typedef struct {
   int64_t w13_hi, w13_lo, w13_scales, w2_hi, w2_lo, w2_scales, blob_bytes;
+  int64_t two_bit_bytes;  /* the two-bit part: bytes [0, two_bit_bytes) of the blob */
 } moe_mat_layout;
 int moe_mat_layout_get(int d, int I, moe_mat_layout* out);
 int moe_mat_from_w4(const uint8_t* w4_bank, int64_t w4_stride, int E, int d, int I, uint8_t* mat_bank,
@@ -398,6 +402,34 @@ int slot_cache_prefetch(moe_slot_cache* cache, const uint64_t* predicted_mask, i
 enum moe_slot_policy { MOE_SLOT_POLICY_LRU = 0, MOE_SLOT_POLICY_COST = 1 };
 int moe_slot_cache_configure(moe_slot_cache* cache, int policy, double decay, int copy_streams);
 int slot_cache_begin_step(moe_slot_cache* cache, const uint64_t* needed_mask);
+
+/*
+ * Precision-aware loads (page "MoE-APEX: An Efficient MoE Inference System with
+ * Adaptive Precision Expert Offloading", "This paper's idea": a cache-miss expert
+ * that is less critical for the current tokens is loaded as a smaller
+ * low-precision variant).  For stores of nested two/four-bit blobs (layout m1,
+ * whose first two_bit_bytes hold everything an expert reads at two bits).
+ * moe_slot_cache_set_prefix: declare that prefix (0 switches it off) while the
+ *   cache is empty.  A slot then holds an expert's whole blob or only its prefix.
+ * slot_cache_load_precision: slot_cache_load with full_mask (host bitmask,
+ *   ceil(E/64) words): the pending experts needed at four bits (the others at two
+ *   bits; moe_mat_grouped_ffn makes the same choice from the routing weights and
+ *   tau, so the caller passes the experts whose largest routing weight in the step
+ *   reaches tau).  Hits keep their slot; a resident expert holding only its
+ *   prefix that is needed at four bits gets the rest of its blob copied into its
+ *   slot; a miss copies the prefix (two bits) or the whole blob (four bits).  The
+ *   cost-aware policy weighs usage by the bytes a slot holds.  bytes_copied (host
+ *   out, may be NULL): bytes this round moved.  Errors: those of slot_cache_load,
+ *   MOE_ERR_INVALID_ARG without a prefix.
+ * moe_slot_cache_planes: [S] 1 where the slot holds the whole blob, the number of
+ *   low-plane completions so far, and all bytes copied so far (outputs may be NULL).
+ */
+int moe_slot_cache_set_prefix(moe_slot_cache* cache, int64_t prefix_bytes);
+int slot_cache_load_precision(moe_slot_cache* cache, const uint64_t* pending_mask, const uint64_t* full_mask,
+                              uint64_t* round_mask, int32_t* slot_table_dev, int32_t* n_hits, int32_t* n_misses,
+                              int64_t* bytes_copied, void* copy_stream, void* wait_event, void* done_event);
+int moe_slot_cache_planes(const moe_slot_cache* cache, int32_t* slot_full, int64_t* upgrades,
+                          int64_t* bytes_copied);
 /* Current slot contents ([S] expert id or -1) and cumulative hit / miss counts. */
 int moe_slot_cache_state(const moe_slot_cache* cache, int32_t* slot_expert,
                          int64_t* hits, int64_t* misses);

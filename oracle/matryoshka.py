@@ -108,16 +108,30 @@ def unpack_plane(plane, N, K, gateup_interleave=False):
 
 
 def blob_layout_m1(d, I, align=256):
-    """Byte offsets of one expert's sections in layout m1: w13 hi, w13 lo, w13 scales,
-    w2 hi, w2 lo, w2 scales (each on an ``align``-byte boundary) and the blob size."""
+    """Byte offsets of one expert's sections in layout m1, returned in the order
+    (w13 hi, w13 lo, w13 scales, w2 hi, w2 lo, w2 scales), and the blob size.  The
+    sections are placed as w13 hi, w13 scales, w2 hi, w2 scales, w13 lo, w2 lo
+    (each on an ``align``-byte boundary): everything a two-bit expert reads is one
+    prefix of the blob, and the low planes follow it (page "MoE-APEX: An
+    Efficient MoE Inference System with Adaptive Precision Expert Offloading",
+    "This paper's idea": a less critical expert that misses the cache is loaded at
+    low precision, so only that prefix moves)."""
     def up(v):
         return (v + align - 1) // align * align
-    sizes = (2 * I * d // 4, 2 * I * d // 4, 2 * I * (d // 128) * 2, d * I // 4, d * I // 4, d * (I // 128) * 2)
-    offs, o = [], 0
-    for sz in sizes:
-        offs.append(o)
-        o = up(o + sz)
-    return tuple(offs), o
+    size = {"hi13": 2 * I * d // 4, "lo13": 2 * I * d // 4, "sc13": 2 * I * (d // 128) * 2,
+            "hi2": d * I // 4, "lo2": d * I // 4, "sc2": d * (I // 128) * 2}
+    at, o = {}, 0
+    for key in ("hi13", "sc13", "hi2", "sc2", "lo13", "lo2"):
+        at[key] = o
+        o = up(o + size[key])
+    return tuple(at[key] for key in ("hi13", "lo13", "sc13", "hi2", "lo2", "sc2")), o
+
+
+def two_bit_prefix_m1(d, I, align=256):
+    """Bytes of the two-bit part at the start of a layout-m1 blob (high planes and
+    scales): where the low planes begin."""
+    offs, _ = blob_layout_m1(d, I, align)
+    return offs[1]
 
 
 def pack_expert_blob_m1(w13_bits, w2_bits):

@@ -169,3 +169,16 @@ def test_noalloc_host_checks(L):
     assert b"scratch" in L.moe_last_error()
     a.T = 0
     assert L.moe_w4a16_grouped_ffn_noalloc(ctypes.byref(a), None) == 0   # T = 0: no-op
+
+
+def test_mat_layout_matches_oracle(L):
+    """Layout m1 on the host: section offsets, blob size and the two-bit prefix equal
+    the oracle's (the prefix holds the high planes and scales, the low planes follow)."""
+    from oracle import matryoshka as omat
+    from w4a16_grouped_expert_amd import _lib
+    for d, I in ((256, 512), (2048, 1024), (4096, 14336)):
+        lay = _lib.MatLayout()
+        assert L.moe_mat_layout_get(d, I, ctypes.byref(lay)) == 0
+        offs, total = omat.blob_layout_m1(d, I)
+        assert (lay.w13_hi, lay.w13_lo, lay.w13_scales, lay.w2_hi, lay.w2_lo, lay.w2_scales) == offs
+        assert lay.blob_bytes == total and lay.two_bit_bytes == omat.two_bit_prefix_m1(d, I)

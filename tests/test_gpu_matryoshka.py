@@ -42,6 +42,7 @@ def test_mat_blobs_bit_exact(d, I, E):
     offs, total = omat.blob_layout_m1(d, I)
     assert lay["blob_bytes"] == total
     assert [lay[k] for k in ("w13_hi", "w13_lo", "w13_scales", "w2_hi", "w2_lo", "w2_scales")] == list(offs)
+    assert lay["two_bit_bytes"] == omat.two_bit_prefix_m1(d, I)
     got = bank.cpu().numpy()
     for e in range(E):
         ref = omat.pack_expert_blob_m1(bits(w13[e]), bits(w2[e]))

@@ -170,3 +170,87 @@ def test_slot_cache_cost_aware_two_copy_streams(wl, S, T, pf):
                                                     copy_streams=2, decay=0.5)
     say(f"  rounds {n_rounds} hits {hits} misses {misses} prefetched {n_pref}")
     assert misses > 0
+
+
+def run_precision_steps(wl, S, steps, T, tau, policy, copy_streams=2, decay=0.5, seed_layer=0):
+    """Slot-cache steps over nested two/four-bit blobs: an expert whose largest routing
+    weight in the step is below tau is loaded (and run) at two bits."""
+    from oracle import matryoshka as omat
+    s = wl.shape
+    tau32 = float(np.float32(tau))
+    w13, w2 = synth.expert_weights(wl, seed_layer, device=DEV)
+    wr = synth.router_weight(wl, seed_layer).to(DEV)
+    w4, _ = moe.pack_experts(w13, w2)
+    bank = moe.mat_from_w4(w4, s.d, s.I)
+    del w4
+    lay = moe.mat_layout(s.d, s.I)
+    B, P = lay["blob_bytes"], lay["two_bit_bytes"]
+    ob = omat.MatBank(lambda e: bits(w13[e]), lambda e: bits(w2[e]))
+    store = torch.empty((s.E, B), dtype=torch.uint8, pin_memory=True)
+    store.copy_(bank.cpu())
+    slots = torch.zeros((S, B), dtype=torch.uint8, device=DEV)
+    cache = moe.SlotCache(s.E, S, B, store, slots)
+    cache.configure(policy, decay, copy_streams)
+    cache.set_prefix(P)
+    sim = SlotCacheSim(s.E, S, policy, decay, prefix_bytes=P, blob_bytes=B)
+    table = torch.full((s.E,), -1, dtype=torch.int32, device=DEV)
+    main = torch.cuda.current_stream()
+    copy = torch.cuda.Stream()
+    done, ffn_done = torch.cuda.Event(), torch.cuda.Event()
+    ffn_done.record(main)
+    ws = moe.alloc_workspace(T, s.d, s.I, s.E, s.k, moe.MODE_DECODE)
+    ident = torch.arange(s.E, dtype=torch.int32, device=DEV)
+    xs = synth.ar1_activation_sequence(wl, T, seed_layer, steps, device="cpu")
+    n_two = n_need = upgrades = 0
+    for st in range(steps):
+        x = xs[st].to(DEV)
+        r = moe.moe_route(x, wr, s.k)
+        a = moe.moe_align(r.ids, s.E)
+        ids, w = r.ids.cpu().numpy(), r.weights.cpu().numpy()
+        need = set(np.unique(ids).tolist())
+        full = {e for e in need if np.max(w[ids == e]) >= np.float32(tau)}
+        n_two += len(need - full)
+        n_need += len(need)
+        cache.begin_step(need)
+        expect = sim.step(need, full)
+        pending = set(need)
+        out = torch.empty((T, s.d), dtype=torch.bfloat16, device=DEV)
+        rounds = 0
+        while pending:
+            got, nh, nm, nb = cache.load_precision(pending, full, table, copy, ffn_done, done)
+            esub, ehits, ecopies = expect[rounds]
+            assert sorted(got) == esub and nh == len(ehits), (st, rounds)
+            assert nm == sum(1 for c in ecopies if c[2] != "lo"), (st, rounds)
+            assert nb == sim.copy_bytes(ecopies), (st, rounds)
+            upgrades += sum(1 for c in ecopies if c[2] == "lo")
+            main.wait_event(done)
+            pending -= got
+            moe.moe_mat_grouped_ffn_into(x, r, a, slots, s.I, out, ws, tau32, not pending, table)
+            ffn_done.record(main)
+            rounds += 1
+        assert rounds == len(expect)
+        slot_state, _, _ = cache.state()
+        assert slot_state == sim.slot_expert
+        assert [bool(v) for v in cache.planes()[0]] == sim.slot_full
+        ref_out = torch.empty_like(out)
+        moe.moe_mat_grouped_ffn_into(x, r, a, bank, s.I, ref_out, ws, tau32, True, ident)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out), f"step {st}"
+        ref = omat.moe_layer(bits(x), bits(wr), ob, s.k, tau32)
+        assert np.array_equal(ids, ref["ids"])
+        check_layer_out(f"step {st} ({rounds} rounds, {len(need - full)}/{len(need)} experts at two bits)",
+                        out.float().cpu().numpy(), ref["out"])
+    _, hits, misses = cache.state()
+    cache.close()
+    return n_two, n_need, upgrades, hits, misses
+
+
+@pytest.mark.parametrize("wl,S,tau,policy", [(synth.TINY, 3, 0.55, POLICY_LRU), (synth.OLMOE_SLOT, 16, 0.14, POLICY_COST),
+                                             (synth.OLMOE_SLOT, 16, 0.1, POLICY_LRU)])
+def test_slot_cache_precision_on_miss(wl, S, tau, policy):
+    # misses of experts below tau copy only the two-bit prefix of their nested blob and
+    # run at two bits; a resident two-bit expert needed at four bits gets its low planes
+    say(f"slot cache precision on miss {wl.name} S={S} tau={tau} policy={policy}")
+    n_two, n_need, upgrades, hits, misses = run_precision_steps(wl, S, 6, 16, tau, policy)
+    say(f"  {n_two}/{n_need} experts at two bits, {upgrades} low-plane completions, hits {hits} misses {misses}")
+    assert 0 < n_two < n_need

@@ -217,3 +217,34 @@ def test_policies_cover_every_needed_expert_once_per_step():
             copies = [e for _, _, cp in rounds for e, _ in cp]
             assert len(copies) == len(set(copies))           # never copied twice in a step
             assert all(len(sub) <= 16 for sub, _, _ in rounds)
+
+
+def test_precision_aware_hand_traced():
+    # blobs of 100 bytes whose first 40 are the two-bit part; LRU
+    c = SlotCacheSim(num_experts=8, num_slots=3, prefix_bytes=40, blob_bytes=100)
+    # step 1 {1, 5}, four bits for 5 only: 1 copies its prefix, 5 its whole blob
+    r = c.step({1, 5}, full={5})
+    assert r == [([1, 5], [], [(1, 0, "hi"), (5, 1, "all")])]
+    assert c.slot_full == [False, True, False] and c.copy_bytes(r[0][2]) == 140
+    # step 2 {1, 2}, four bits for 1: 1 stays in slot 0 and gets its low planes; 2 (two
+    # bits) takes the empty slot 2
+    r = c.step({1, 2}, full={1})
+    assert r == [([1, 2], [1], [(1, 0, "lo"), (2, 2, "hi")])]
+    assert c.slot_full == [True, True, False] and c.copy_bytes(r[0][2]) == 100
+    # step 3 {2, 6, 7}, four bits for 6: 2 is a plain hit (two bits needed, two bits held);
+    # 6 and 7 evict slots 1 (expert 5, older) and 0 (expert 1)
+    r = c.step({2, 6, 7}, full={6})
+    assert r == [([2, 6, 7], [2], [(6, 1, "all"), (7, 0, "hi")])]
+    assert c.slot_expert == [7, 6, 2] and c.slot_full == [False, True, False]
+    # a whole-blob request (full=None) completes a two-bit resident
+    r = c.step({7})
+    assert r == [([7], [7], [(7, 0, "lo")])] and c.slot_full[0]
+
+
+def test_precision_aware_cost_weighs_reload_bytes():
+    c = SlotCacheSim(num_experts=8, num_slots=2, policy=POLICY_COST, decay=0.5, prefix_bytes=40, blob_bytes=100)
+    assert c.step({0, 1}, full={0}) == [([0, 1], [], [(0, 0, "all"), (1, 1, "hi")])]
+    # step 2 {2} at four bits: u0 = u1 = .25; reload costs .25 * 100 (slot 0, whole blob) and
+    # .25 * 40 (slot 1, prefix): the cheaper reload goes (LRU would evict slot 0)
+    assert c.step({2}, full={2}) == [([2], [], [(2, 1, "all")])]
+    assert c.slot_expert == [0, 2] and c.slot_full == [True, True]

@@ -93,7 +93,12 @@ def test_blob_layout_m1_has_the_v1_sizes():
         offs, total = mat.blob_layout_m1(d, I)
         v1offs, v1total = quant.blob_layout(d, I)
         assert total == v1total                # the two planes together are the nibble codes
-        assert offs[1] - offs[0] == 2 * I * d // 4
+        hi13, lo13, sc13, hi2, lo2, sc2 = offs
+        # two-bit part first (w13 hi, w13 scales, w2 hi, w2 scales), then the low planes
+        assert hi13 == 0 and sc13 == hi13 + 2 * I * d // 4 and hi2 >= sc13 + 2 * I * (d // 128) * 2
+        assert sc2 == hi2 + d * I // 4 and lo13 >= sc2 + d * (I // 128) * 2 and lo2 == lo13 + 2 * I * d // 4
+        assert mat.two_bit_prefix_m1(d, I) == lo13
+        assert total - lo13 == 3 * I * d // 4    # the low planes: half of the code bytes
 
 
 def layer_inputs(T, d, E, k, I, seed):

@@ -34,7 +34,7 @@ class ExpertLayout(ctypes.Structure):
 
 class MatLayout(ctypes.Structure):
     _fields_ = [("w13_hi", c_i64), ("w13_lo", c_i64), ("w13_scales", c_i64), ("w2_hi", c_i64), ("w2_lo", c_i64),
-                ("w2_scales", c_i64), ("blob_bytes", c_i64)]
+                ("w2_scales", c_i64), ("blob_bytes", c_i64), ("two_bit_bytes", c_i64)]
 
 
 class FfnArgs(ctypes.Structure):
@@ -87,6 +87,10 @@ SIGNATURES = {
     "slot_cache_prefetch": (c_int, [c_vp, c_u64p, c_int, c_i32p, c_vp, c_vp]),
     "moe_slot_cache_configure": (c_int, [c_vp, c_int, c_double, c_int]),
     "slot_cache_begin_step": (c_int, [c_vp, c_u64p]),
+    "moe_slot_cache_set_prefix": (c_int, [c_vp, c_i64]),
+    "slot_cache_load_precision": (c_int, [c_vp, c_u64p, c_u64p, c_u64p, c_vp, c_i32p, c_i32p, c_i64p, c_vp, c_vp,
+                                          c_vp]),
+    "moe_slot_cache_planes": (c_int, [c_vp, c_i32p, c_i64p, c_i64p]),
     "moe_timing_enable": (c_int, [c_int]),
     "moe_timing_reset": (c_int, []),
     "moe_timing_read": (c_int, [c_int, ctypes.POINTER(c_double), c_i64p]),

@@ -503,6 +503,35 @@ class SlotCache:
         """The needed experts of a new step (usage averages of the cost-aware policy)."""
         check("slot_cache_begin_step", lib().slot_cache_begin_step(self._h, self._mask(needed)))
 
+    def set_prefix(self, prefix_bytes: int):
+        """Precision-aware loads: the blobs' first prefix_bytes are their two-bit part."""
+        check("moe_slot_cache_set_prefix", lib().moe_slot_cache_set_prefix(self._h, int(prefix_bytes)))
+
+    def load_precision(self, pending: set, full: set, slot_table_dev: torch.Tensor, copy_stream, wait_event,
+                       done_event):
+        """One round with per-expert precision (full: experts needed at four bits):
+        returns (round experts set, hits, misses, bytes copied)."""
+        if done_event.cuda_event == 0:
+            done_event.record(copy_stream)
+        if wait_event is not None and wait_event.cuda_event == 0:
+            wait_event.record(torch.cuda.current_stream())
+        rm = (ctypes.c_uint64 * self.words)()
+        nh, nm, nb = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
+        check("slot_cache_load_precision", lib().slot_cache_load_precision(
+            self._h, self._mask(pending), self._mask(full), rm, _ptr(slot_table_dev), ctypes.byref(nh),
+            ctypes.byref(nm), ctypes.byref(nb), ctypes.c_void_p(copy_stream.cuda_stream),
+            ctypes.c_void_p(wait_event.cuda_event) if wait_event is not None else None,
+            ctypes.c_void_p(done_event.cuda_event)))
+        got = {e for e in range(self.E) if (rm[e >> 6] >> (e & 63)) & 1}
+        return got, nh.value, nm.value, nb.value
+
+    def planes(self):
+        """([S] 1 where the slot holds the whole blob, low-plane completions, bytes copied so far)."""
+        sf = (ctypes.c_int32 * self.S)()
+        up, nb = ctypes.c_int64(), ctypes.c_int64()
+        check("moe_slot_cache_planes", lib().moe_slot_cache_planes(self._h, sf, ctypes.byref(up), ctypes.byref(nb)))
+        return list(sf), up.value, nb.value
+
     def prefetch(self, predicted: set, max_copies: int, copy_stream, wait_event=None) -> int:
         """Copy predicted experts ahead of their round; returns the number of copies."""
         if wait_event is not None and wait_event.cuda_event == 0:

@@ -334,21 +334,24 @@ __global__ __launch_bounds__(256) void k_mat_down(FfnDev f, MatOffsets mo, float
   }
 }
 
+// Sections of an m1 blob: the two-bit part first (w13 high plane, w13 scales, w2
+// high plane, w2 scales), then the low planes (w13, w2), each 256-byte aligned, so
+// loading an expert at two bits moves one prefix of the blob.
 static MatOffsets mat_offsets(int d, int I) {
   auto up = [](int64_t v) { return (v + 255) / 256 * 256; };
   MatOffsets m;
   int64_t o = 0;
   m.hi13 = o;
   o = up(o + (int64_t)2 * I * d / 4);
-  m.lo13 = o;
-  o = up(o + (int64_t)2 * I * d / 4);
   m.sc13 = o;
   o = up(o + (int64_t)2 * I * (d / kGroup) * 2);
   m.hi2 = o;
   o = up(o + (int64_t)d * I / 4);
-  m.lo2 = o;
-  o = up(o + (int64_t)d * I / 4);
   m.sc2 = o;
+  o = up(o + (int64_t)d * (I / kGroup) * 2);
+  m.lo13 = o;
+  o = up(o + (int64_t)2 * I * d / 4);
+  m.lo2 = o;
   return m;
 }
 
@@ -382,7 +385,8 @@ extern "C" int moe_mat_layout_get(int d, int I, moe_mat_layout* out) {
   out->w2_hi = m.hi2;
   out->w2_lo = m.lo2;
   out->w2_scales = m.sc2;
-  out->blob_bytes = (m.sc2 + (int64_t)d * (I / kGroup) * 2 + 255) / 256 * 256;
+  out->blob_bytes = (m.lo2 + (int64_t)d * I / 4 + 255) / 256 * 256;
+  out->two_bit_bytes = m.lo13;
   return MOE_OK;
 }
 

@@ -32,6 +32,9 @@ struct moe_slot_cache {
   int policy = MOE_SLOT_POLICY_LRU;
   double decay = 0.9;
   std::vector<double> usage;       // [E] cost-aware: average of "needed in a step"
+  int64_t prefix_bytes = 0;        // > 0: precision-aware, a blob's first prefix_bytes are its two-bit part
+  std::vector<char> slot_full;     // [S] the slot holds the whole blob (else only the prefix)
+  int64_t upgrades = 0, bytes_copied = 0;
   hipStream_t aux = nullptr;       // second copy stream (copy_streams = 2)
   hipEvent_t aux_done = nullptr;   // the aux stream's copies, joined into the caller's copy stream
   // ring of pinned staging tables for the per-round expert->slot map
@@ -63,6 +66,7 @@ extern "C" int moe_slot_cache_create(int E, int S, int64_t blob_bytes, const voi
   c->slot_stamp.assign(S, -1);
   c->expert_slot.assign(E, -1);
   c->usage.assign(E, 0.0);
+  c->slot_full.assign(S, 0);
   if (hipHostMalloc(reinterpret_cast<void**>(&c->tables), sizeof(int32_t) * E * moe_slot_cache::kRing,
                     hipHostMallocDefault) != hipSuccess) {
     delete c;
@@ -150,10 +154,16 @@ namespace {
 // LRU: last use, then slot
 void order_victims(const moe_slot_cache* c, std::vector<int>& v) {
   if (c->policy == MOE_SLOT_POLICY_COST) {
+    // precision-aware: usage times the bytes the slot holds (its reload would copy them)
+    auto cost = [&](int sl) {
+      const int e = c->slot_expert[sl];
+      if (c->prefix_bytes <= 0) return c->usage[e];
+      return c->usage[e] * (double)(c->slot_full[sl] ? c->blob_bytes : c->prefix_bytes);
+    };
     std::sort(v.begin(), v.end(), [&](int a, int b) {
       const int ea = c->slot_expert[a], eb = c->slot_expert[b];
       if ((ea >= 0) != (eb >= 0)) return ea < 0;
-      if (ea >= 0 && c->usage[ea] != c->usage[eb]) return c->usage[ea] < c->usage[eb];
+      if (ea >= 0 && cost(a) != cost(b)) return cost(a) < cost(b);
       if (c->slot_stamp[a] != c->slot_stamp[b]) return c->slot_stamp[a] < c->slot_stamp[b];
       return a < b;
     });
@@ -164,12 +174,14 @@ void order_victims(const moe_slot_cache* c, std::vector<int>& v) {
 
 // the copy of expert e into slot sl: the i-th copy of a call goes to the caller's
 // stream (even i) or the cache's second stream (odd i, when configured)
-hipError_t copy_expert(moe_slot_cache* c, int e, int sl, int i, hipStream_t s) {
+hipError_t copy_expert(moe_slot_cache* c, int e, int sl, int i, hipStream_t s, int64_t off = 0, int64_t bytes = -1) {
+  if (bytes < 0) bytes = c->blob_bytes - off;
   if (c->fail_after == 0) return hipErrorInvalidValue;
   if (c->fail_after > 0) --c->fail_after;
   hipStream_t cs = (c->aux && (i & 1)) ? c->aux : s;
-  return hipMemcpyAsync(c->device_slots + (int64_t)sl * c->blob_bytes, c->host_store + (int64_t)e * c->blob_bytes,
-                        c->blob_bytes, hipMemcpyHostToDevice, cs);
+  c->bytes_copied += bytes;
+  return hipMemcpyAsync(c->device_slots + (int64_t)sl * c->blob_bytes + off,
+                        c->host_store + (int64_t)e * c->blob_bytes + off, bytes, hipMemcpyHostToDevice, cs);
 }
 
 // before the copies: the second stream waits for what the caller's stream waits for
@@ -190,22 +202,25 @@ hipError_t aux_join(moe_slot_cache* c, hipStream_t s, int n_copies) {
 
 }  // namespace
 
-extern "C" int slot_cache_load(moe_slot_cache* c, const uint64_t* pending_mask, uint64_t* round_mask,
-                               int32_t* slot_table_dev, int32_t* n_hits, int32_t* n_misses, void* copy_stream,
-                               void* wait_event, void* done_event) {
-  clear_error();
-  MOE_CHECK_ARG(c && pending_mask && round_mask && slot_table_dev && done_event, MOE_ERR_INVALID_ARG,
-                "slot_cache_load: null argument");
-  hipStream_t s = (hipStream_t)copy_stream;
+// One round (slot_cache_load / slot_cache_load_precision).  full_mask NULL: every
+// pending expert needs its whole blob.
+static int load_round(moe_slot_cache* c, const uint64_t* pending_mask, const uint64_t* full_mask,
+                      uint64_t* round_mask, int32_t* slot_table_dev, int32_t* n_hits, int32_t* n_misses,
+                      int64_t* bytes_out, hipStream_t s, void* wait_event, void* done_event, const char* fn) {
   const int E = c->E, S = c->S, words = (E + 63) / 64;
+  const bool mixed = c->prefix_bytes > 0;
+  auto needs_full = [&](int e) { return !mixed || !full_mask || ((full_mask[e >> 6] >> (e & 63)) & 1ull); };
+  const int64_t bytes0 = c->bytes_copied;
 
-  std::vector<int> hits, miss_all;
+  std::vector<int> hits, miss_all, upgrade;
   for (int e = 0; e < E; ++e) {
     if (!((pending_mask[e >> 6] >> (e & 63)) & 1ull)) continue;
-    if (c->expert_slot[e] >= 0)
+    if (c->expert_slot[e] >= 0) {
       hits.push_back(e);
-    else
+      if (needs_full(e) && !c->slot_full[c->expert_slot[e]]) upgrade.push_back(e);
+    } else {
       miss_all.push_back(e);
+    }
   }
   if (c->policy == MOE_SLOT_POLICY_COST)
     std::stable_sort(miss_all.begin(), miss_all.end(), [&](int a, int b) { return c->usage[a] < c->usage[b]; });
@@ -217,36 +232,56 @@ extern "C" int slot_cache_load(moe_slot_cache* c, const uint64_t* pending_mask, 
     if (!hit_slot[sl]) victims.push_back(sl);
   order_victims(c, victims);
 
+  const int n_copies = (int)upgrade.size() + n_m;
+  // also with nothing to copy: the slot table copy below must not overtake the
+  // kernels that still read the previous table
   if (wait_event) {
     if (hipStreamWaitEvent(s, (hipEvent_t)wait_event, 0) != hipSuccess) {
-      set_error("slot_cache_load: hipStreamWaitEvent failed");
+      set_error("%s: hipStreamWaitEvent failed", fn);
       return MOE_ERR_HIP;
     }
   }
-  if (n_m > 1 && aux_wait(c, s, wait_event) != hipSuccess) {
-    set_error("slot_cache_load: second copy stream could not be ordered");
+  if (n_copies > 1 && aux_wait(c, s, wait_event) != hipSuccess) {
+    set_error("%s: second copy stream could not be ordered", fn);
     return MOE_ERR_HIP;
   }
+  int rc = MOE_OK, issued = 0;
+  // resident two-bit experts needed at four bits: their low planes into the same slot
+  for (int e : upgrade) {
+    const int sl = c->expert_slot[e];
+    const hipError_t err = copy_expert(c, e, sl, issued, s, c->prefix_bytes);
+    if (err != hipSuccess) {
+      set_error("%s: H2D copy of expert %d's low planes into slot %d failed: %s", fn, e, sl, hipGetErrorString(err));
+      rc = MOE_ERR_HIP;
+      break;
+    }
+    ++issued;
+    c->slot_full[sl] = 1;
+    ++c->upgrades;
+  }
   std::vector<int> loaded;
-  int rc = MOE_OK;
-  for (int i = 0; i < n_m; ++i) {
+  for (int i = 0; i < n_m && !rc; ++i) {
     const int e = miss_all[i], sl = victims[i];
     const int old = c->slot_expert[sl];
     if (old >= 0) c->expert_slot[old] = -1;
     c->slot_expert[sl] = -1;
     c->slot_stamp[sl] = -1;
-    const hipError_t err = copy_expert(c, e, sl, i, s);
+    c->slot_full[sl] = 0;
+    const bool full = needs_full(e);
+    const hipError_t err = copy_expert(c, e, sl, issued, s, 0, full ? c->blob_bytes : c->prefix_bytes);
     if (err != hipSuccess) {
-      set_error("slot_cache_load: H2D copy of expert %d into slot %d failed: %s", e, sl, hipGetErrorString(err));
+      set_error("%s: H2D copy of expert %d into slot %d failed: %s", fn, e, sl, hipGetErrorString(err));
       rc = MOE_ERR_HIP;
       break;
     }
+    ++issued;
     c->slot_expert[sl] = e;
     c->expert_slot[e] = sl;
+    c->slot_full[sl] = full ? 1 : 0;
     loaded.push_back(e);
   }
-  if (aux_join(c, s, (int)loaded.size()) != hipSuccess && !rc) {
-    set_error("slot_cache_load: second copy stream could not be joined");
+  if (aux_join(c, s, issued) != hipSuccess && !rc) {
+    set_error("%s: second copy stream could not be joined", fn);
     rc = MOE_ERR_HIP;
   }
   if (rc) return rc;
@@ -273,12 +308,59 @@ extern "C" int slot_cache_load(moe_slot_cache* c, const uint64_t* pending_mask, 
   }
   if (hipMemcpyAsync(slot_table_dev, table, sizeof(int32_t) * E, hipMemcpyHostToDevice, s) != hipSuccess ||
       hipEventRecord(c->table_ev[slot_idx], s) != hipSuccess || hipEventRecord((hipEvent_t)done_event, s) != hipSuccess) {
-    set_error("slot_cache_load: slot table copy failed");
+    set_error("%s: slot table copy failed", fn);
     return MOE_ERR_HIP;
   }
   c->table_used[slot_idx] = true;
   if (n_hits) *n_hits = (int32_t)hits.size();
   if (n_misses) *n_misses = (int32_t)loaded.size();
+  if (bytes_out) *bytes_out = c->bytes_copied - bytes0;
+  return MOE_OK;
+}
+
+extern "C" int slot_cache_load(moe_slot_cache* c, const uint64_t* pending_mask, uint64_t* round_mask,
+                               int32_t* slot_table_dev, int32_t* n_hits, int32_t* n_misses, void* copy_stream,
+                               void* wait_event, void* done_event) {
+  clear_error();
+  MOE_CHECK_ARG(c && pending_mask && round_mask && slot_table_dev && done_event, MOE_ERR_INVALID_ARG,
+                "slot_cache_load: null argument");
+  return load_round(c, pending_mask, nullptr, round_mask, slot_table_dev, n_hits, n_misses, nullptr,
+                    (hipStream_t)copy_stream, wait_event, done_event, "slot_cache_load");
+}
+
+extern "C" int slot_cache_load_precision(moe_slot_cache* c, const uint64_t* pending_mask, const uint64_t* full_mask,
+                                         uint64_t* round_mask, int32_t* slot_table_dev, int32_t* n_hits,
+                                         int32_t* n_misses, int64_t* bytes_copied, void* copy_stream,
+                                         void* wait_event, void* done_event) {
+  clear_error();
+  MOE_CHECK_ARG(c && pending_mask && full_mask && round_mask && slot_table_dev && done_event, MOE_ERR_INVALID_ARG,
+                "slot_cache_load_precision: null argument");
+  MOE_CHECK_ARG(c->prefix_bytes > 0, MOE_ERR_INVALID_ARG,
+                "slot_cache_load_precision: the cache has no two-bit prefix (moe_slot_cache_set_prefix)");
+  return load_round(c, pending_mask, full_mask, round_mask, slot_table_dev, n_hits, n_misses, bytes_copied,
+                    (hipStream_t)copy_stream, wait_event, done_event, "slot_cache_load_precision");
+}
+
+extern "C" int moe_slot_cache_set_prefix(moe_slot_cache* c, int64_t prefix_bytes) {
+  clear_error();
+  MOE_CHECK_ARG(c != nullptr, MOE_ERR_INVALID_ARG, "moe_slot_cache_set_prefix: cache is NULL");
+  MOE_CHECK_ARG(prefix_bytes >= 0 && prefix_bytes < c->blob_bytes, MOE_ERR_INVALID_ARG,
+                "moe_slot_cache_set_prefix: prefix %lld not in [0, %lld)", (long long)prefix_bytes,
+                (long long)c->blob_bytes);
+  for (int sl = 0; sl < c->S; ++sl)
+    MOE_CHECK_ARG(c->slot_expert[sl] < 0, MOE_ERR_INVALID_ARG, "moe_slot_cache_set_prefix: the cache is not empty");
+  c->prefix_bytes = prefix_bytes;
+  return MOE_OK;
+}
+
+extern "C" int moe_slot_cache_planes(const moe_slot_cache* c, int32_t* slot_full, int64_t* upgrades,
+                                     int64_t* bytes_copied) {
+  clear_error();
+  MOE_CHECK_ARG(c != nullptr, MOE_ERR_INVALID_ARG, "moe_slot_cache_planes: cache is NULL");
+  if (slot_full)
+    for (int sl = 0; sl < c->S; ++sl) slot_full[sl] = c->slot_full[sl];
+  if (upgrades) *upgrades = c->upgrades;
+  if (bytes_copied) *bytes_copied = c->bytes_copied;
   return MOE_OK;
 }
 
@@ -320,6 +402,7 @@ extern "C" int slot_cache_prefetch(moe_slot_cache* c, const uint64_t* predicted_
     if (old >= 0) c->expert_slot[old] = -1;
     c->slot_expert[sl] = -1;
     c->slot_stamp[sl] = -1;
+    c->slot_full[sl] = 0;
     const hipError_t err = copy_expert(c, e, sl, i, s);
     if (err != hipSuccess) {
       set_error("slot_cache_prefetch: H2D copy of expert %d into slot %d failed: %s", e, sl, hipGetErrorString(err));
@@ -330,6 +413,7 @@ extern "C" int slot_cache_prefetch(moe_slot_cache* c, const uint64_t* predicted_
     c->slot_expert[sl] = e;
     c->expert_slot[e] = sl;
     c->slot_stamp[sl] = c->clock;
+    c->slot_full[sl] = 1;
     ++done;
   }
   if (aux_join(c, s, done) != hipSuccess) {

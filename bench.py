@@ -35,9 +35,10 @@ HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 # HBM counters of the roofline kernel (routing + grouped gate/up of moe_decode_layer)
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "routing_gateup_decode_olmoe_t16_hbm_counters.txt")
-COUNTED_SOURCES = ["w4a16_grouped_expert_amd/csrc/ffn_layer.hip", "w4a16_grouped_expert_amd/csrc/ffn_common.hpp",
-                   "w4a16_grouped_expert_amd/csrc/common.hpp", "w4a16_grouped_expert_amd/csrc/align_block.hpp",
-                   "w4a16_grouped_expert_amd/csrc/route_rank.hpp"]
+COUNTED_SOURCES = ["w4a16_grouped_expert_amd/csrc/layer_gateup.hpp", "w4a16_grouped_expert_amd/csrc/ffn_layer.hip",
+                   "w4a16_grouped_expert_amd/csrc/ffn_common.hpp", "w4a16_grouped_expert_amd/csrc/common.hpp",
+                   "w4a16_grouped_expert_amd/csrc/align_block.hpp", "w4a16_grouped_expert_amd/csrc/route_rank.hpp",
+                   "w4a16_grouped_expert_amd/csrc/mat_format.hpp", "w4a16_grouped_expert_amd/csrc/down_combine.hpp"]
 
 
 def parse():
@@ -115,9 +116,10 @@ class Decoder:
         self.moe, self.torch = moe, torch
         s = wl.shape
         self.wl, self.s, self.bf16, self.mat, self.tau = wl, s, bf16, mat, 0.0
-        # steps of at most 16 tokens on four-bit experts: the whole layer in two
-        # launches (moe_decode_layer); else moe_route_align + the grouped FFN call
-        self.fused = fused and not bf16 and not mat
+        # steps of at most 16 tokens on four-bit or nested experts: the whole layer
+        # in two launches (moe_decode_layer, moe_mat_decode_layer); else
+        # moe_route_align + the grouped FFN call
+        self.fused = fused and not bf16
         self.layers = []
         for l in range(wl.layers):
             w13, w2 = synth.expert_weights(wl, l, device=device)
@@ -168,7 +170,11 @@ class Decoder:
         wr, bank = self.layers[l]
         r = moe.RouteOut(self.route.logits[:T], self.route.ids[:T], self.route.weights[:T])
         if self.uses_layer(T):
-            moe.moe_decode_layer_into(x, wr, bank, s.I, s.k, r, self.out[l][:T], self.lws, self.lctr)
+            if self.mat:
+                moe.moe_mat_decode_layer_into(x, wr, bank, s.I, s.k, r, self.out[l][:T], self.lws, self.lctr,
+                                              self.tau)
+            else:
+                moe.moe_decode_layer_into(x, wr, bank, s.I, s.k, r, self.out[l][:T], self.lws, self.lctr)
             return None
         a = moe.AlignOut(self.align.offsets, self.align.sorted_pairs[:T * s.k], self.align.pair_pos[:T * s.k],
                          self.align.active, None, 0)
@@ -314,18 +320,20 @@ def run_mat_compare(Ts, taus, steps, warmup, x_sets, w4_tokens_per_s):
         xs = [[synth.activations(wl, T, l, step=st, device="cuda") for l in range(wl.layers)] for st in range(x_sets)]
         for tau in taus:
             dec.tau = tau
-            r = run_decode(dec, T, steps, warmup, x_sets, timed_kernels=("gateup_mat", "down_mat", "combine", "route"))
+            kern = ("gateup_decode", "down_decode") if dec.uses_layer(T) else ("gateup_mat", "down_mat", "combine",
+                                                                                  "route")
+            r = run_decode(dec, T, steps, warmup, x_sets, timed_kernels=kern)
             # share of the step's experts at four bits (same decision as the kernels, from the routing weights)
             n4 = n = 0
             for xl in xs[:2]:
                 for l, x in enumerate(xl):
-                    a = dec.layer(l, x)
-                    U = int(a.active[0])
-                    act = a.active[4:4 + 4 * U].view(U, 4)[:, 0].long()
+                    dec.layer(l, x)
+                    ids = dec.route.ids[:T].reshape(-1).long()
+                    act = torch.unique(ids)
                     wmax = torch.zeros(s.E, device="cuda").scatter_reduce(
-                        0, dec.route.ids[:T].reshape(-1).long(), dec.route.weights[:T].reshape(-1), "amax")
+                        0, ids, dec.route.weights[:T].reshape(-1), "amax")
                     n4 += int((wmax[act] >= tau).sum())
-                    n += U
+                    n += int(act.numel())
             frac4 = n4 / max(1, n)
             res[f"T={T} tau={tau}"] = {
                 "tokens_per_s": round(r["tokens_per_s"], 1), "ms_per_step": round(r["ms_per_step"], 4),
@@ -334,9 +342,10 @@ def run_mat_compare(Ts, taus, steps, warmup, x_sets, w4_tokens_per_s):
                 "vs_w4": round(r["tokens_per_s"] / w4_tokens_per_s[T], 3)}
     del dec
     torch.cuda.empty_cache()
-    return {"workload": "olmoe_decode with nested two/four-bit experts (layout m1, same route/align/combine); "
-                        "four bits when an expert's largest routing weight in the step reaches tau, else two "
-                        "bits (high plane only, floor plus compensation)", **res}
+    return {"workload": "olmoe_decode with nested two/four-bit experts (layout m1) through the fused two-launch "
+                        "decode layer (moe_mat_decode_layer, as the four-bit path); four bits when an expert's "
+                        "largest routing weight in the step reaches tau, else two bits (high plane only, floor "
+                        "plus compensation)", **res}
 
 
 def expert_section_bytes(d, I):

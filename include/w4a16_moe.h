@@ -327,6 +327,20 @@ int moe_mat_from_w4(const uint8_t* w4_bank, int64_t w4_stride, int E, int d, int
 int moe_mat_grouped_ffn(const moe_ffn_args* args, float tau, void* stream);
 
 /*
+ * moe_mat_decode_layer: one decode step of the whole layer as moe_decode_layer
+ *   (router, top-k, gate/up + SwiGLU, down, combine in two launches, same
+ *   arguments, workspace, counters and limits) with `bank` holding layout-m1
+ *   blobs (stride >= their blob bytes) and each expert's precision chosen as in
+ *   moe_mat_grouped_ffn: four bits when the largest routing weight of its pairs
+ *   in this step is >= tau, else two bits.  tau <= 0 puts every expert at four
+ *   bits (out then equals moe_decode_layer on the layout-v1 blobs the nested ones
+ *   were made from, bit for bit), tau > 1 every expert at two bits.  Limits: those
+ *   of moe_decode_layer, with d and I multiples of 256; MOE_ERR_INVALID_ARG for a
+ *   NaN tau.
+ */
+int moe_mat_decode_layer(const moe_decode_layer_args* args, float tau, void* stream);
+
+/*
  * Expert slot cache (ExactMoE, Abstract: quantised experts in pinned host
  * memory, executed from a configurable GPU-resident slot cache).
  *

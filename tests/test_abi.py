@@ -155,6 +155,31 @@ def test_decode_layer_host_checks(L):
     assert L.moe_decode_layer_workspace_bytes(-1, 2048, 1024, 64, 8) == -1
 
 
+def test_mat_decode_layer_host_checks(L):
+    """moe_mat_decode_layer: argument errors are reported before anything is enqueued."""
+    from w4a16_grouped_expert_amd import _lib
+    vp = 256
+    assert L.moe_mat_decode_layer(None, 0.0, None) == 1
+    a = _lib.LayerArgs()
+    a.T, a.d, a.I, a.E, a.k, a.renormalize = 17, 256, 512, 8, 2, 1
+    assert L.moe_mat_decode_layer(ctypes.byref(a), 0.0, None) == 2       # T > 16
+    a.T, a.d = 4, 384
+    assert L.moe_mat_decode_layer(ctypes.byref(a), 0.0, None) == 2       # d not a multiple of 256
+    a.d = 256
+    assert L.moe_mat_decode_layer(ctypes.byref(a), float("nan"), None) == 1  # NaN tau
+    assert L.moe_mat_decode_layer(ctypes.byref(a), 0.5, None) == 1       # null pointers
+    for f in ("x", "w_router", "bank", "logits", "topk_ids", "topk_weights", "out", "workspace", "counters"):
+        setattr(a, f, vp)
+    a.bank_stride = 202752
+    a.workspace_bytes = 16
+    assert L.moe_mat_decode_layer(ctypes.byref(a), 2.0, None) == 3       # workspace too small
+    a.workspace_bytes = L.moe_decode_layer_workspace_bytes(4, 256, 512, 8, 2)
+    a.bank_stride = 1000
+    assert L.moe_mat_decode_layer(ctypes.byref(a), 0.0, None) == 1       # stride below one blob
+    a.T = 0
+    assert L.moe_mat_decode_layer(ctypes.byref(a), 0.1, None) == 0       # T = 0: no-op
+
+
 def test_noalloc_host_checks(L):
     """moe_w4a16_grouped_ffn_noalloc: a caller workspace or a step whose workspace
     exceeds the scratch is refused on the host, before any device call."""

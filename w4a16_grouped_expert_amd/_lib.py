@@ -80,6 +80,7 @@ SIGNATURES = {
     "moe_mat_grouped_ffn": (c_int, [ctypes.POINTER(FfnArgs), ctypes.c_float, c_vp]),
     "moe_decode_layer_workspace_bytes": (c_i64, [c_int, c_int, c_int, c_int, c_int]),
     "moe_decode_layer": (c_int, [ctypes.POINTER(LayerArgs), c_vp]),
+    "moe_mat_decode_layer": (c_int, [ctypes.POINTER(LayerArgs), ctypes.c_float, c_vp]),
     "moe_slot_cache_create": (c_int, [c_int, c_int, c_i64, c_vp, c_vp, ctypes.POINTER(c_vp)]),
     "moe_slot_cache_destroy": (c_int, [c_vp]),
     "slot_cache_load": (c_int, [c_vp, c_u64p, c_u64p, c_vp, c_i32p, c_i32p, c_vp, c_vp, c_vp]),

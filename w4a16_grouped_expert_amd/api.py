@@ -252,11 +252,7 @@ def decode_layer_workspace_bytes(T, d, I, E, k) -> int:
     return int(lib().moe_decode_layer_workspace_bytes(T, d, I, E, k))
 
 
-def moe_decode_layer_into(x, w_router, bank: torch.Tensor, I: int, k: int, route: RouteOut, out: torch.Tensor,
-                          workspace: torch.Tensor, counters: torch.Tensor, renormalize=True,
-                          bank_stride: Optional[int] = None, stream=None):
-    """Router, top-k, grouped gate/up, down and combine of one decode step (T <= 16)
-    in two launches; outputs bit-identical to moe_route_align + moe_w4a16_grouped_ffn."""
+def _layer_args(x, w_router, bank, I, k, route, out, workspace, counters, renormalize, bank_stride, name):
     _need(x, torch.bfloat16, "x")
     _need(w_router, torch.bfloat16, "w_router")
     _need(bank, torch.uint8, "bank")
@@ -264,7 +260,7 @@ def moe_decode_layer_into(x, w_router, bank: torch.Tensor, I: int, k: int, route
     _need(workspace, torch.uint8, "workspace")
     _need(counters, torch.int32, "counters")
     if counters.numel() < DECODE_LAYER_COUNTERS:
-        raise ValueError(f"moe_decode_layer needs {DECODE_LAYER_COUNTERS} counters, got {counters.numel()}")
+        raise ValueError(f"{name} needs {DECODE_LAYER_COUNTERS} counters, got {counters.numel()}")
     T, d = x.shape
     E = w_router.shape[0]
     a = _lib.LayerArgs()
@@ -276,7 +272,28 @@ def moe_decode_layer_into(x, w_router, bank: torch.Tensor, I: int, k: int, route
     a.out = out.data_ptr()
     a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
     a.counters = counters.data_ptr()
+    return a
+
+
+def moe_decode_layer_into(x, w_router, bank: torch.Tensor, I: int, k: int, route: RouteOut, out: torch.Tensor,
+                          workspace: torch.Tensor, counters: torch.Tensor, renormalize=True,
+                          bank_stride: Optional[int] = None, stream=None):
+    """Router, top-k, grouped gate/up, down and combine of one decode step (T <= 16)
+    in two launches; outputs bit-identical to moe_route_align + moe_w4a16_grouped_ffn."""
+    a = _layer_args(x, w_router, bank, I, k, route, out, workspace, counters, renormalize, bank_stride,
+                    "moe_decode_layer")
     check("moe_decode_layer", lib().moe_decode_layer(ctypes.byref(a), _stream(stream)))
+    return out
+
+
+def moe_mat_decode_layer_into(x, w_router, bank: torch.Tensor, I: int, k: int, route: RouteOut, out: torch.Tensor,
+                              workspace: torch.Tensor, counters: torch.Tensor, tau: float, renormalize=True,
+                              bank_stride: Optional[int] = None, stream=None):
+    """moe_decode_layer_into on nested two/four-bit blobs (layout m1, from mat_from_w4):
+    each expert at four bits when the largest routing weight of its pairs reaches tau."""
+    a = _layer_args(x, w_router, bank, I, k, route, out, workspace, counters, renormalize, bank_stride,
+                    "moe_mat_decode_layer")
+    check("moe_mat_decode_layer", lib().moe_mat_decode_layer(ctypes.byref(a), float(tau), _stream(stream)))
     return out
 
 

@@ -7,6 +7,12 @@
 
 namespace moe {
 
+// Weight formats and precisions of the fused decode passes: four-bit blobs of
+// layout v1, or nested two/four-bit blobs of layout m1 with every expert at four
+// bits (tau <= 0), every expert at two bits (tau > 1), or each expert at four
+// bits when the largest routing weight of its pairs reaches tau.
+enum LayerPrec { kPrecW4 = 0, kPrecAll4 = 1, kPrecAll2 = 2, kPrecMixed = 3 };
+
 struct FfnDev {
   const uint16_t* x;  // [T][d] bf16
   int T, d, I, E, k;
@@ -22,7 +28,10 @@ struct FfnDev {
   const uint8_t* bank;
   int64_t bank_stride;
   const int32_t* slot_of_expert;
+  // layout v1: codes and scales; layout m1: high planes (as codes), scales and low planes
   int64_t off_w13_codes, off_w13_scales, off_w2_codes, off_w2_scales;
+  int64_t off_w13_lo = 0, off_w2_lo = 0;
+  float tau = 0.f;  // layout m1, mixed precision: an expert runs at four bits when a pair's weight reaches it
   // counters of the fused down + combine pass, zeroed by the gate/up pass before it
   int32_t* zero_ctr = nullptr;
   int n_zero_ctr = 0;

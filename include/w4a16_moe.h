@@ -187,7 +187,10 @@ typedef struct {
  * added in a fixed order): the output is deterministic but is not bit-identical
  * to the two-pass combine, and no per-pair results are left in the workspace.
  * Calls with a slot table keep the two passes, so subsets of the experts can run
- * in separate calls with combine = 0 and the last one combines. */
+ * in separate calls with combine = 0 and the last one combines.  The per-pair
+ * results of the two-pass combine are fp32 (decode mode) or rounded once to bf16
+ * (prefill mode, which halves their write and read); the combine sums each
+ * token's k rows in fp32 in slot order and rounds once to bf16. */
 int64_t moe_ffn_workspace_bytes(int T, int d, int I, int E, int k, int mode);
 int moe_w4a16_grouped_ffn(const moe_ffn_args* args, void* stream);
 

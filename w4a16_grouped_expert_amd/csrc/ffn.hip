@@ -61,6 +61,42 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, in
   *reinterpret_cast<u32x2_t*>(out + t * d + n) = o;
 }
 
+// The combine of the prefill path: per-pair rows in bf16, one K part.  Same
+// order and arithmetic as k_combine: the k routed outputs in slot order, fp32,
+// one bf16 rounding.
+__global__ __launch_bounds__(256) void k_combine_bf16(const uint16_t* __restrict__ y, int d, int k,
+                                                      const int32_t* __restrict__ pair_pos,
+                                                      const float* __restrict__ w, uint16_t* __restrict__ out,
+                                                      int nchunks) {
+  const int64_t t = blockIdx.x / nchunks;
+  const int n = ((blockIdx.x % nchunks) * 256 + threadIdx.x) * 4;
+  if (n >= d) return;
+  int64_t pos[MOE_MAX_TOPK];
+  float wj[MOE_MAX_TOPK];
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+    pos[j] = j < k ? pair_pos[t * k + j] : -1;  // -1: pair dropped by moe_align (expert id out of range)
+    wj[j] = j < k ? w[t * k + j] : 0.f;
+  }
+  u32x2_t v[MOE_MAX_TOPK];
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j)
+    v[j] = pos[j] >= 0 ? __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(y + pos[j] * d + n))
+                       : u32x2_t{0u, 0u};
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+    if (pos[j] < 0) continue;
+    const float r4[4] = {__uint_as_float(v[j][0] << 16), __uint_as_float(v[j][0] & 0xFFFF0000u),
+                         __uint_as_float(v[j][1] << 16), __uint_as_float(v[j][1] & 0xFFFF0000u)};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = fmaf(wj[j], r4[r], acc[r]);
+  }
+  u32x2_t o = {f32_to_bf16_bits(acc[0]) | (f32_to_bf16_bits(acc[1]) << 16),
+               f32_to_bf16_bits(acc[2]) | (f32_to_bf16_bits(acc[3]) << 16)};
+  *reinterpret_cast<u32x2_t*>(out + t * d + n) = o;
+}
+
 static int resolve_mode(int T, int E, int k, int mode) {
   if (mode == MOE_MODE_DECODE || mode == MOE_MODE_PREFILL) return mode;
   const double per_expert = (double)T * k / E;  // expected pairs per expert
@@ -93,7 +129,8 @@ static WsLayout ws_layout(int T, int d, int I, int E, int k, int mode) {
   WsLayout L;
   L.h_off = 0;
   L.y_off = align256(P * I * 2);
-  L.xsum_off = L.y_off + align256((int64_t)ks * P * d * 4);
+  // per-pair outputs: fp32 K parts (decode), bf16 rows (prefill)
+  L.xsum_off = L.y_off + align256(mode == MOE_MODE_PREFILL ? P * d * 2 : (int64_t)ks * P * d * 4);
   L.hsum_off = L.xsum_off;
   L.total = L.xsum_off;
   L.dc_part_off = L.dc_ctr_off = -1;
@@ -121,6 +158,15 @@ FfnWorkspace ffn_workspace(int T, int d, int I, int E, int k, int mode, void* ws
   w.dc_counters = L.dc_ctr_off >= 0 ? reinterpret_cast<int32_t*>(b + L.dc_ctr_off) : nullptr;
   w.ksplit = down_ksplit(T, d, I, E, k, mode);
   return w;
+}
+
+int launch_combine_bf16(const FfnDev& f, const uint16_t* y, const float* weights, uint16_t* out, hipStream_t s) {
+  const int nchunks = (int)ceil_div(f.d, 1024);
+  timing_begin(K_COMBINE, s);
+  hipLaunchKernelGGL(k_combine_bf16, dim3((unsigned)(f.T * (int64_t)nchunks)), dim3(256), 0, s, y, f.d, f.k,
+                     f.pair_pos, weights, out, nchunks);
+  timing_end(K_COMBINE, s);
+  return check_launch("combine");
 }
 
 int launch_combine(const FfnDev& f, const float* y, int ksplit, const float* weights, uint16_t* out, hipStream_t s) {
@@ -210,10 +256,15 @@ extern "C" int moe_w4a16_grouped_ffn(const moe_ffn_args* a, void* stream) {
     rc = launch_decode(f, w.h, w.y, w.ksplit, per_expert <= 8.0 ? 1 : 2, s, fused ? a->out : nullptr, w.dc_part,
                        w.dc_counters);
   } else {
-    rc = launch_prefill(f, w.h, w.y, w.xsum, w.hsum, s);
+    rc = launch_prefill(f, w.h, reinterpret_cast<uint16_t*>(w.y), w.xsum, w.hsum, s);
   }
   if (rc) return rc;
-  if (a->combine && !fused) rc = launch_combine(f, w.y, w.ksplit, a->topk_weights, a->out, s);
+  if (a->combine && !fused) {
+    if (mode == MOE_MODE_PREFILL)
+      rc = launch_combine_bf16(f, reinterpret_cast<const uint16_t*>(w.y), a->topk_weights, a->out, s);
+    else
+      rc = launch_combine(f, w.y, w.ksplit, a->topk_weights, a->out, s);
+  }
   return rc;
 }
 

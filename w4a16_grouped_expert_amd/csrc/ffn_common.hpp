@@ -50,9 +50,10 @@ __device__ __forceinline__ void zero_down_counters(const FfnDev& f) {
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
 
-// Workspace of one call: h [T*k][I] bf16, y [ksplit][T*k][d] fp32, for the
-// prefill variant the group sums of x and h, and for steps of at most 16 tokens
-// the partial sums and stripe counters of the fused down + combine pass.
+// Workspace of one call: h [T*k][I] bf16, y [ksplit][T*k][d] fp32 (prefill:
+// [T*k][d] bf16), for the prefill variant the group sums of x and h, and for
+// steps of at most 16 tokens the partial sums and stripe counters of the fused
+// down + combine pass.
 struct FfnWorkspace {
   uint16_t* h;
   float* y;
@@ -76,7 +77,9 @@ void launch_down_combine(const FfnDev& f, const uint16_t* h, uint16_t* out, floa
                          int32_t* route_ctr, int n_route_ctr, hipStream_t s, bool pair);
 // Units per wavefront of the fused down + combine pass, 0 if the step is too large for it.
 int dc_units_per_wave(int umax, int G, int stripes);
-int launch_prefill(const FfnDev& f, uint16_t* h, float* y, float* xsum, float* hsum, hipStream_t s);
+// y: the per-pair outputs [P][d] in bf16 (combined by launch_combine_bf16)
+int launch_prefill(const FfnDev& f, uint16_t* h, uint16_t* y, float* xsum, float* hsum, hipStream_t s);
+int launch_combine_bf16(const FfnDev& f, const uint16_t* y, const float* weights, uint16_t* out, hipStream_t s);
 int64_t prefill_extra_bytes(int T, int d, int I, int k);
 
 }  // namespace moe

@@ -132,7 +132,7 @@ __device__ __forceinline__ float silu_fast(float z) { return z * __builtin_amdgc
 template <bool GATEUP>
 __global__ __launch_bounds__(kPThreads) void k_prefill(
     FfnDev f, const uint16_t* __restrict__ act, const float* __restrict__ asum, uint16_t* __restrict__ hout,
-    float* __restrict__ hsum_out, float* __restrict__ yout) {
+    float* __restrict__ hsum_out, uint16_t* __restrict__ yout) {
   const int K = GATEUP ? f.d : f.I;
   const int N = GATEUP ? 2 * f.I : f.d;
   const int G = K / kGroup;
@@ -521,6 +521,7 @@ __global__ __launch_bounds__(kPThreads) void k_prefill(
         if (r < n_e) hsum_out[(int64_t)(row0 + r) * GH + nt] = (s_hs[0][tid] + s_hs[1][tid]) + (s_hs[2][tid] + s_hs[3][tid]);
       }
     } else {
+      // the pair's output row in bf16 (the combine sums the k rows in fp32)
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int r = wt * 64 + b * 16 + col;
@@ -529,7 +530,9 @@ __global__ __launch_bounds__(kPThreads) void k_prefill(
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             const int n = nt * kPBN + wr * 64 + t * 16 + 4 * kq;
-            if (n < N) *reinterpret_cast<f32x4_t*>(yout + (int64_t)pos * f.d + n) = acc[t][b];
+            const u32x2_t o = {f32_to_bf16_bits(acc[t][b][0]) | (f32_to_bf16_bits(acc[t][b][1]) << 16),
+                               f32_to_bf16_bits(acc[t][b][2]) | (f32_to_bf16_bits(acc[t][b][3]) << 16)};
+            if (n < N) *reinterpret_cast<u32x2_t*>(yout + (int64_t)pos * f.d + n) = o;
           }
         }
       }
@@ -558,7 +561,7 @@ int64_t prefill_extra_bytes(int T, int d, int I, int k) {
   return (int64_t)T * (d / kGroup) * 4 + P * (I / kGroup) * 4 + 512;
 }
 
-int launch_prefill(const FfnDev& f, uint16_t* h, float* y, float* xsum, float* hsum, hipStream_t s) {
+int launch_prefill(const FfnDev& f, uint16_t* h, uint16_t* y, float* xsum, float* hsum, hipStream_t s) {
   // the kernels address x, h and the group sums with 32-bit byte offsets
   if ((int64_t)f.T * f.d * 2 >= (int64_t(1) << 32) || f.P * f.I * 2 >= (int64_t(1) << 32)) {
     set_error("moe_w4a16_grouped_ffn: prefill needs T * d * 2 and T * k * I * 2 below 4 GiB (T=%d d=%d I=%d k=%d)", f.T,
@@ -578,7 +581,7 @@ int launch_prefill(const FfnDev& f, uint16_t* h, float* y, float* xsum, float* h
   const int64_t grid_dn = std::min<int64_t>(prefill_grid(kdn, 1), tiles_dn);
   timing_begin(K_GATEUP_PREFILL, s);
   hipLaunchKernelGGL(kgu, dim3((unsigned)grid_gu), dim3(kPThreads), 0, s, f, f.x, (const float*)xsum, h, hsum,
-                     (float*)nullptr);
+                     (uint16_t*)nullptr);
   timing_end(K_GATEUP_PREFILL, s);
   rc = check_launch("grouped gate/up (prefill)");
   if (rc) return rc;

@@ -350,6 +350,9 @@ __global__ __launch_bounds__(kPThreads) void k_prefill(
     bool next_ready = false;
 
     f32x4_t acc[4][4];
+    // this wavefront's token half holds tokens of the tile (else it skips the
+    // products of every group: the last tile of an expert is often half empty)
+    const bool live = __builtin_amdgcn_readfirstlane(mt * kPBM + 64 * wt < n_e ? 1 : 0) != 0;
     float e_next = 1.f;  // scale chain of row `tid` (threads 0 .. 255): e of the newest group seen
     f32x4_t rn[4];       // this lane's ratios for the next group
     f32x4_t xsn;         // this lane's group sums for the next group
@@ -417,6 +420,21 @@ __global__ __launch_bounds__(kPThreads) void k_prefill(
       }
 
       const PrefillStage& S = st[(qb + g) % kStages];
+      if (!live) {
+        // a token half without tokens: no products, only its share of the batch's
+        // DMA (its outputs are not stored; acc is set once so that they are defined)
+        if (g == 0) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) acc[t][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        if (g + 2 < G) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) issue_part(g + 2, i, qb);
+        }
+        continue;
+      }
       // acc = acc * (e_{g-1} / e_g) - 1.5 sum_k x   (acc = -1.5 sum_k x for g = 0)
       if (g == 0) {
         const f32x4_t xs = *reinterpret_cast<const f32x4_t*>(&s_xs[qb & 3][64 * wt + 4 * col]);

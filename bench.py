@@ -512,8 +512,10 @@ def run_prefill(T, reps=20, warmup=3):
 
 def run_large(Ts, reps=10, warmup=3):
     """Large-expert shape (d=4096, E=8, top-2, I=14336, 4 layers, all resident): per T
-    the 4-layer step timed with HIP events; HBM fraction on algorithmic bytes (distinct
-    experts x blob + router + activations) and MFMA fraction on flops."""
+    the 4-layer step timed with HIP events (steps of at most 16 tokens through
+    moe_decode_layer, as the OLMoE decode legs; more tokens through route, align,
+    grouped FFN and combine); HBM fraction on algorithmic bytes (distinct experts x
+    blob + router + activations) and MFMA fraction on flops."""
     import torch
     import synth
     import w4a16_grouped_expert_amd as moe
@@ -528,19 +530,38 @@ def run_large(Ts, reps=10, warmup=3):
         layers.append(moe.MoELayer(wr, bank, s.I, s.k, max(Ts)))
     torch.cuda.empty_cache()
     blob = lay["blob_bytes"]
+    t_l = min(16, max(Ts))
+    lws = torch.empty(max(moe.decode_layer_workspace_bytes(t_l, s.d, s.I, s.E, s.k), 256), dtype=torch.uint8,
+                      device="cuda")
+    lctr = moe.alloc_layer_counters("cuda")
     res = {}
     for T in Ts:
         xs = [synth.activations(wl, T, l, device="cuda") for l in range(wl.layers)]
-        for _ in range(warmup):
+
+        def step():
             for L, x in zip(layers, xs):
-                L.forward(x)
+                if T <= 16:
+                    r, _ = L.views(T)
+                    moe.moe_decode_layer_into(x, L.w_router, L.bank, s.I, s.k, r, L.out[:T], lws, lctr)
+                else:
+                    L.forward(x)
+        for _ in range(warmup):
+            step()
         torch.cuda.synchronize()
-        U = [int(L.align.active[0].item()) for L in layers]
+        if T <= 16:
+            if int(lctr[-1].item()):
+                raise SystemExit("bench.py: moe_decode_layer routing wait timed out (large expert); results invalid")
+            U = []
+            for L, x in zip(layers, xs):
+                r, _ = L.views(T)
+                moe.moe_decode_layer_into(x, L.w_router, L.bank, s.I, s.k, r, L.out[:T], lws, lctr)
+                U.append(int(torch.unique(r.ids).numel()))
+        else:
+            U = [int(L.align.active[0].item()) for L in layers]
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0.record()
         for _ in range(reps):
-            for L, x in zip(layers, xs):
-                L.forward(x)
+            step()
         t1.record()
         torch.cuda.synchronize()
         ms = t0.elapsed_time(t1) / reps
@@ -554,7 +575,8 @@ def run_large(Ts, reps=10, warmup=3):
     del layers
     torch.cuda.empty_cache()
     return {"workload": "large_expert: 4 MoE layers, d=4096, E=8, top-2, I=14336, W4 g128 experts resident; "
-                        "whole-step time (route + align + grouped FFN + combine) per T", **res}
+                        "whole-step time per T (T <= 16: moe_decode_layer, two launches per layer; else route + "
+                        "align + grouped FFN + combine)", **res}
 
 
 def h2d_ceiling(store, slots, streams=2, reps=3):

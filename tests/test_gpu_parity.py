@@ -73,7 +73,10 @@ def test_pack_edge_values():
 
 @pytest.mark.parametrize("T,d,E,k", [(16, 256, 8, 2), (1, 2048, 64, 8), (4, 2048, 64, 8), (16, 2048, 64, 8),
                                      (333, 2048, 64, 8), (4096, 2048, 64, 8), (64, 4096, 8, 2), (7, 512, 1024, 16),
-                                     (5, 128, 1, 1), (300, 256, 128, 16), (300, 256, 256, 8)])
+                                     (5, 128, 1, 1), (300, 256, 128, 16), (300, 256, 256, 8),
+                                     # the float64 matrix-core kernel (16-token blocks >= CUs): ragged token
+                                     # tail, experts not a multiple of 16, d not a multiple of 32, E = 128
+                                     (4100, 136, 100, 6), (5000, 512, 128, 8), (4096, 64, 1, 1)])
 def test_route_parity(T, d, E, k):
     say(f"route T={T} d={d} E={E} k={k}")
     g = torch.Generator().manual_seed(T * 7 + d + E)

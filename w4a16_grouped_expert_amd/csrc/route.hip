@@ -6,9 +6,10 @@
 // summed in float64 and rounded once to float32 (on MI355X a non-packed fp64 FMA
 // issues at the fp32 rate, so the near-exact sum costs nothing extra).  The
 // selection orders by (logit desc, index asc); softmax weights in float32.
-// Two launch shapes: one 1024-thread block per token for small T (latency), and
+// Three launch shapes: one 1024-thread block per token for small T (latency),
 // blocks of TB tokens x all experts for large T (router weights reused across
-// the TB tokens; TB = 2 up to 512 tokens, 4 beyond).
+// the TB tokens; TB = 2 up to 512 tokens, 4 beyond), and for E <= 128 once there
+// are as many 16-token blocks as CUs, the float64 matrix-core kernel.
 #include "align_block.hpp"
 #include "route_rank.hpp"
 
@@ -393,9 +394,116 @@ __global__ __launch_bounds__(256) void k_route(const uint16_t* __restrict__ x, c
   topk_wave(s_logit[wave], E, k, renormalize, t0 + wave, ids, weights, s_sv[wave], s_si[wave]);
 }
 
+// Many tokens, E <= 128: the logits of 16 tokens x 16 experts per wavefront on the
+// float64 matrix cores (v_mfma_f64_16x16x4f64: the bf16 values converted exactly,
+// products and sums in float64, rounded once to float32, as in k_route).  Lane l
+// (r = l % 16, q = l / 16) loads 8 consecutive channels of router row eb + r and of
+// token row t0 + r and feeds them to 8 MFMAs as K index q, so each MFMA sums four
+// channels 8 apart; element i of its result is expert eb + q + 4i, token t0 + r.
+// A block is 16 tokens x (4 expert blocks of 16) x KS parts of d; the parts meet
+// in LDS in part order.  Then one wavefront per token runs the top-k.  The float64
+// sums come out the same as k_route's on the evaluated shapes (0 ulp at T = 300 to
+// 4096); both are within an ulp of the oracle's.
+constexpr int kRouteMfmaTB = 16, kRouteMfmaMaxE = 128, kRouteMfmaKS = 4;
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+
+template <int KS>
+__global__ __launch_bounds__(256 * KS) void k_route_mfma(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+                                                         int T, int d, int E, int k, int renormalize,
+                                                         float* __restrict__ logits, int32_t* __restrict__ ids,
+                                                         float* __restrict__ weights) {
+  constexpr int kWaves = 4 * KS;
+  __shared__ float s_logit[kRouteMfmaTB][kRouteMfmaMaxE];
+  __shared__ f64x4_t s_part[KS > 1 ? kWaves : 1][64];
+  __shared__ float s_sv[kWaves][MOE_MAX_TOPK];
+  __shared__ int s_si[kWaves][MOE_MAX_TOPK];
+  const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, q = lane >> 4;
+  const int xb = wave / KS, part = wave % KS;  // expert block (of 4) and part of d
+  const int t0 = blockIdx.x * kRouteMfmaTB;
+  const int nch = (d + 31) / 32;                // 32-channel chunks
+  const int cpp = (nch + KS - 1) / KS;          // chunks per part
+  const int c_lo = min(nch, part * cpp), c_hi = min(nch, c_lo + cpp);
+  const bool t_ok = t0 + r < T;
+  const uint16_t* xrow = x + (int64_t)(t_ok ? t0 + r : 0) * d;
+
+  // every wavefront takes the same number of expert-block rounds (the rounds
+  // hold barriers); a round past E leaves its wavefront's sums at zero
+  const int rounds = (E + 63) / 64;
+  for (int m = 0; m < rounds; ++m) {
+    const int eb = 16 * xb + 64 * m;
+    const bool e_ok = eb + r < E;
+    const uint16_t* wrow = wr + (int64_t)(e_ok ? eb + r : 0) * d;
+    f64x4_t acc = {0.0, 0.0, 0.0, 0.0};
+    constexpr int kRing = 4;
+    u32x4_t bw[kRing], bx[kRing];
+    // chunk c's 16-byte slices (zeros past d, past E or past T)
+    auto load = [&](int j, int c) {
+      const int ch = 32 * c + 8 * q;
+      const bool in = c < c_hi && ch < d;
+      bw[j] = in && e_ok ? *reinterpret_cast<const u32x4_t*>(wrow + ch) : u32x4_t{0u, 0u, 0u, 0u};
+      bx[j] = in && t_ok ? *reinterpret_cast<const u32x4_t*>(xrow + ch) : u32x4_t{0u, 0u, 0u, 0u};
+    };
+    const int c_end = eb < E ? c_hi : c_lo;  // wave-uniform
+#pragma unroll
+    for (int j = 0; j < kRing - 1; ++j) load(j, c_lo + j);
+    for (int c = c_lo; c < c_end; c += kRing) {
+#pragma unroll
+      for (int j = 0; j < kRing; ++j) {
+        load((j + kRing - 1) % kRing, c + j + kRing - 1);
+        const u32x4_t w4 = bw[j], x4 = bx[j];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const uint32_t wb = (m & 1) ? (w4[m >> 1] >> 16) : (w4[m >> 1] & 0xFFFFu);
+          const uint32_t xv = (m & 1) ? (x4[m >> 1] >> 16) : (x4[m >> 1] & 0xFFFFu);
+          acc = __builtin_amdgcn_mfma_f64_16x16x4f64(bf16_to_f64(wb), bf16_to_f64(xv), acc, 0, 0, 0);
+        }
+      }
+    }
+    if constexpr (KS > 1) {
+      s_part[wave][lane] = acc;
+      __syncthreads();
+      if (part == 0) {
+#pragma unroll
+        for (int p = 1; p < KS; ++p) {
+          const f64x4_t o = s_part[wave + p][lane];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[i] += o[i];
+        }
+      }
+      __syncthreads();  // s_part is free for the next expert block
+    }
+    if (part == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = eb + q + 4 * i;
+        if (e < E) s_logit[r][e] = (float)acc[i];
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kRouteMfmaTB * E; i += 64 * kWaves) {
+    const int a = i / E, e = i % E;
+    if (t0 + a < T) logits[(int64_t)(t0 + a) * E + e] = s_logit[a][e];
+  }
+  for (int a = wave; a < kRouteMfmaTB; a += kWaves)
+    if (t0 + a < T) topk_wave(s_logit[a], E, k, renormalize, t0 + a, ids, weights, s_sv[wave], s_si[wave]);
+}
+
 }  // namespace moe
 
 using namespace moe;
+
+static int route_cus() {
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    cus = std::max(cus, 1);
+  }
+  return cus;
+}
 
 extern "C" int moe_route(const uint16_t* x, const uint16_t* w_router, int T, int d, int E, int k,
                          int renormalize, float* logits, int32_t* topk_ids, float* topk_weights, void* stream) {
@@ -414,6 +522,11 @@ extern "C" int moe_route(const uint16_t* x, const uint16_t* w_router, int T, int
   if (T <= 256) {
     hipLaunchKernelGGL(k_route_token, dim3(T), dim3(1024), 0, s, x, w_router, T, d, E, k, renormalize, logits,
                        topk_ids, topk_weights);
+  } else if (E <= kRouteMfmaMaxE && ceil_div(T, kRouteMfmaTB) >= route_cus()) {
+    // float64 matrix cores once every CU has a 16-token block (a block's time is
+    // fixed by its products on one CU, so fewer blocks leave CUs idle)
+    hipLaunchKernelGGL(k_route_mfma<kRouteMfmaKS>, dim3((unsigned)ceil_div(T, kRouteMfmaTB)), dim3(256 * kRouteMfmaKS),
+                       0, s, x, w_router, T, d, E, k, renormalize, logits, topk_ids, topk_weights);
   } else if (T <= 512) {
     // two tokens per block: twice the blocks of the four-token shape, which leaves
     // half the CUs idle below 1024 tokens (measured faster up to 512 tokens)

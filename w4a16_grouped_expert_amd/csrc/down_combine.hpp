@@ -9,7 +9,7 @@
 
 namespace moe {
 
-// fused down + combine: tiles per stripe, prefetch distance in units, wavefronts
+// fused down + combine: tiles per stripe, prefetch distance in groups, wavefronts
 // per workgroup and resident wavefronts per SIMD
 constexpr int kDcRT = 2, kDcD = 2, kDcWaves = 8, kDcOcc = 4;
 

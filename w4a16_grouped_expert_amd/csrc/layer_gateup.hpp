@@ -1,9 +1,11 @@
-// moe_decode_layer: a whole decode step of the W4A16 MoE layer (at most 16
+// The fused decode layer (moe_decode_layer, and moe_mat_decode_layer on nested
+// two/four-bit blobs): a whole decode step of the W4A16 MoE layer (at most 16
 // tokens) in two launches: routing + grouped gate/up + SwiGLU, then the grouped
 // down projection with the routing-weighted combine (ExactMoE, page "Every
 // Expert Counts: ExactMoE for Memory-Efficient W4A16 Inference", Abstract: the
 // BF16 router and its unchanged top-k, every selected expert through fused
-// grouped kernels on four-bit weights).
+// grouped kernels on four-bit weights).  This header holds the first launch's
+// kernel and the host code both entry points share.
 //
 // The first launch is persistent (every workgroup resident).  Each wavefront
 // first issues the weight loads of its first gate/up item when that item is
@@ -20,10 +22,11 @@
 // waits for it (a bounded poll of the ready table) only before its first h
 // store, and skips the items of experts without pairs after that; items over
 // the active experts wait for it before the first item.  The
-// second launch is the fused down + combine pass, which builds the active
-// expert list from the routing table itself.  Routing results are bit-identical
-// to moe_route_align; the arithmetic of every gate/up item and of the down pass
-// is that of moe_w4a16_grouped_ffn's decode kernels with one wavefront per item.
+// second launch is the fused down + combine pass (down_combine.hpp), which builds
+// the active expert list from the routing table itself.  Routing results are
+// bit-identical to moe_route_align; the arithmetic of every gate/up item and of
+// the down pass is that of moe_w4a16_grouped_ffn's decode kernels with one
+// wavefront per item.
 #pragma once
 
 #include "align_block.hpp"

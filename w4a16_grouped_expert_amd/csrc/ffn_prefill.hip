@@ -145,8 +145,9 @@ __global__ __launch_bounds__(kPThreads) void k_prefill(
   __shared__ float s_ratio[2][kPBN];   // e_{g-1} / e_g per row at [g % 2]; 16 e_last at [G % 2]
   __shared__ int s_row[2][kPBM];       // activation rows of this tile and the next (see fill_rows)
   __shared__ int s_pref[MOE_MAX_EXPERTS + 1];
+  __shared__ uint16_t s_lpref[MOE_MAX_EXPERTS + 1];
   __shared__ float s_hs[4][kPBM];      // gate/up: per-token h sums of each row quarter's 32 columns
-  __shared__ int s_wsum[kPWaves];
+  __shared__ int s_wsum[kPWaves], s_wlsum[kPWaves];
 
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -155,26 +156,46 @@ __global__ __launch_bounds__(kPThreads) void k_prefill(
   const int U = f.active[0];
   const i32x4_t* work = reinterpret_cast<const i32x4_t*>(f.active + 4);
 
-  // tiles of active expert u: ceil(count / 128) token tiles x NT row tiles; exclusive prefix in LDS
-  if (tid == 0) s_pref[0] = 0;
+  // Tiles of active expert u: ceil(count / 128) token tiles x NT row tiles.  A
+  // last token tile with at most 64 tokens (one token half busy) is a light tile;
+  // the light tiles of every expert follow all the others, so the blocks that
+  // get one tile more than the rest get light ones.  Exclusive prefixes in LDS:
+  // s_pref of the other tiles, s_lpref of the experts with a light tile.
+  if (tid == 0) {
+    s_pref[0] = 0;
+    s_lpref[0] = 0;
+  }
   for (int base = 0; base < U; base += kPThreads) {
     __syncthreads();
     const int u = base + tid;
     const int n_e = u < U ? work[u][2] : 0;
-    int v = ((n_e + kPBM - 1) / kPBM) * NT;
+    const int rem = n_e % kPBM;
+    const int light = (rem > 0 && rem <= kPBM / 2) ? 1 : 0;
+    int v = ((n_e + kPBM - 1) / kPBM - light) * NT, lv = light;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-      const int o = __shfl_up(v, off);
-      if (lane >= off) v += o;
+      const int o = __shfl_up(v, off), ol = __shfl_up(lv, off);
+      if (lane >= off) {
+        v += o;
+        lv += ol;
+      }
     }
     if (lane == 63) s_wsum[wave] = v;
+    if (lane == 63) s_wlsum[wave] = lv;
     __syncthreads();
-    int add = s_pref[base];
-    for (int w = 0; w < wave; ++w) add += s_wsum[w];
-    if (u < U) s_pref[u + 1] = add + v;
+    int add = s_pref[base], addl = s_lpref[base];
+    for (int w = 0; w < wave; ++w) {
+      add += s_wsum[w];
+      addl += s_wlsum[w];
+    }
+    if (u < U) {
+      s_pref[u + 1] = add + v;
+      s_lpref[u + 1] = (uint16_t)(addl + lv);
+    }
   }
   __syncthreads();
-  const int total = s_pref[U];
+  const int total_main = s_pref[U];
+  const int total = total_main + (int)s_lpref[U] * NT;
 
   // Workgroups are dealt to the XCDs round robin; renumber them so each XCD owns
   // a contiguous run of tile slots (consecutive tiles share an expert).
@@ -183,11 +204,19 @@ __global__ __launch_bounds__(kPThreads) void k_prefill(
 
   const uint32_t kMask = vgpr_const(0x00780078u), kOne = vgpr_const(0x3F803F80u);
 
-  auto active_of = [&](int t) {  // the active expert u with s_pref[u] <= t < s_pref[u + 1]
+  auto active_of = [&](int t) {  // the active expert of tile t
     int lo = 0, hi = U;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (s_pref[mid] <= t) lo = mid; else hi = mid;
+    if (t < total_main) {  // s_pref[u] <= t < s_pref[u + 1]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_pref[mid] <= t) lo = mid; else hi = mid;
+      }
+    } else {  // light tile j: s_lpref[u] <= j < s_lpref[u + 1]
+      const int j = (t - total_main) / NT;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if ((int)s_lpref[mid] <= j) lo = mid; else hi = mid;
+      }
     }
     return lo;
   };
@@ -195,13 +224,17 @@ __global__ __launch_bounds__(kPThreads) void k_prefill(
     int row0, n_e, mt, nt;
     const uint8_t* blob;
   };
+  // token tile of tile t of active expert u with n_e tokens (row tiles fastest:
+  // neighbours share the token tile; a light tile is the expert's last one)
+  auto mt_of = [&](int t, int u, int n_e) {
+    return t < total_main ? (t - s_pref[u]) / NT : (n_e + kPBM - 1) / kPBM - 1;
+  };
   auto tile_of = [&](int t, int u, const i32x4_t& w) {
     Tile tl;
     tl.row0 = w[1];
     tl.n_e = w[2];
-    const int local = t - s_pref[u];
-    tl.mt = local / NT;  // row tiles fastest: neighbours share the token tile
-    tl.nt = local % NT;
+    tl.mt = mt_of(t, u, tl.n_e);
+    tl.nt = t < total_main ? (t - s_pref[u]) % NT : (t - total_main) % NT;
     tl.blob = f.blob(w[0]);
     return tl;
   };
@@ -391,7 +424,7 @@ __global__ __launch_bounds__(kPThreads) void k_prefill(
         stage_wait_barrier<0>();
       }
       if (GATEUP && g == G - 2 && next < total && tid < kPBM) {
-        const int rn_ = ((next - s_pref[un]) / NT) * kPBM + tid;
+        const int rn_ = mt_of(next, un, w4n[2]) * kPBM + tid;
         if (rn_ < w4n[2]) pair_next = f.sorted_pairs[w4n[1] + rn_];
         pair_tile = next;
       }

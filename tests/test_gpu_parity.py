@@ -16,7 +16,7 @@ from oracle import ffn as offn
 from oracle import quant as oquant
 from oracle import route as oroute
 
-from gpu_helpers import bits, oracle_bank, rel_err, say, tol_for_layer
+from gpu_helpers import bits, check_layer_out, oracle_bank, rel_err, say, tol_for_layer
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -300,6 +300,33 @@ def test_layer_skewed_routing_and_ragged_blocks():
         assert set(np.unique(r.ids.cpu().numpy())) == {3, 6}
         ref = offn.moe_layer(bits(x), bits(wr), oracle_bank(w13, w2), s.k)
         assert rel_err(out.float().cpu().numpy(), ref["out"]) <= tol_for_layer()
+
+
+def test_layer_prefill_mixed_tile_loads():
+    # a router bias along one activation channel spreads the per-expert loads: experts
+    # whose last 128-token tile holds at most 64 tokens (ordered after all other tiles),
+    # experts with a fuller last tile, experts with several tiles and one with exactly two;
+    # every token against the oracle
+    say("layer prefill mixed tile loads")
+    g = torch.Generator().manual_seed(31)
+    d, I, E, k, T = 512, 256, 16, 4, 700
+    w13 = (torch.randn((E, 2 * I, d), generator=g) * 0.02).to(torch.bfloat16)
+    w2 = (torch.randn((E, d, I), generator=g) * 0.02).to(torch.bfloat16)
+    wr = torch.randn((E, d), generator=g) * 0.02
+    wr[:, 0] = 0.3 * torch.arange(E, dtype=torch.float32) / E
+    wr = wr.to(torch.bfloat16)
+    x = torch.randn((T, d), generator=g)
+    x[:, 0] = 4.0
+    x = x.to(torch.bfloat16)
+    bank, _ = moe.pack_experts(w13.to(DEV), w2.to(DEV))
+    ref = offn.moe_layer(bits(x), bits(wr), oracle_bank(w13, w2), k)
+    n_e = np.bincount(ref["ids"].reshape(-1), minlength=E)
+    rem = n_e % 128
+    assert np.any((rem > 0) & (rem <= 64)) and np.any(rem > 64) and np.any(n_e > 128), n_e
+    for mode in (moe.MODE_PREFILL, moe.MODE_AUTO):
+        out, r, _ = run_layer(x.to(DEV), wr.to(DEV), bank, I, k, mode)
+        assert np.array_equal(r.ids.cpu().numpy(), ref["ids"])
+        check_layer_out(f"mixed loads mode={mode}", out.float().cpu().numpy(), ref["out"])
 
 
 def test_layer_single_expert_top1():

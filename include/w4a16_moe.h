@@ -210,8 +210,9 @@ int moe_w4a16_grouped_ffn(const moe_ffn_args* args, void* stream);
  *  Runs on the calling thread's current device; `stream` must belong to it.
  *  Errors: MOE_ERR_WORKSPACE when moe_ffn_workspace_bytes(T, d, I, E, k, mode)
  *  exceeds MOE_NOALLOC_SCRATCH_BYTES (checked on the host before anything is
- *  enqueued; e.g. OLMoE-shaped decode steps use under 6 MiB, prefill steps fit up
- *  to about 800 tokens), MOE_ERR_HIP when the scratch address cannot be
+ *  enqueued; e.g. OLMoE-shaped decode steps of 16 tokens use under 6 MiB, and
+ *  OLMoE-shaped steps fit up to 819 tokens in decode mode and 1356 in prefill
+ *  mode), MOE_ERR_HIP when the scratch address cannot be
  *  obtained, else those of moe_w4a16_grouped_ffn.
  *  All calls on one GPU share its scratch, which keeps the last call's contents:
  *  calls that overlap on one GPU (concurrent streams or threads) race and give

@@ -96,7 +96,9 @@ int pack_w4_g128(const uint16_t* w, int E, int N, int K, int gateup_interleave,
  *
  *  x            [T][d] bf16 activations.  w_router [E][d] bf16.
  *  logits       [T][E] float32 output (required): sum_c x[t,c] * w_router[e,c],
- *               products exact, summed in float64, rounded once to float32.
+ *               products exact, summed in float64, rounded once to float32 (the
+ *               order of the float64 sum depends on the kernel T selects, so the
+ *               last bit of a logit may too).
  *  topk_ids     [T][k] int32 output: experts ordered by (logit desc, index asc).
  *  topk_weights [T][k] float32 output: exp(l_j - l_max) / sum over the selected
  *               experts (renormalize = 1) or over all E (renormalize = 0).

@@ -157,6 +157,8 @@ int moe_route_align(const uint16_t* x, const uint16_t* w_router, int T, int d, i
  * all selected experts through fused grouped kernels): gate/up + SwiGLU, down,
  * routing-weighted combine, over the expert-sorted pairs from moe_align.
  */
+/* MOE_MODE_AUTO: the decode kernels up to 20 expected pairs per expert (T k / E),
+ * the MFMA-tiled prefill kernels above. */
 enum moe_ffn_mode { MOE_MODE_AUTO = 0, MOE_MODE_DECODE = 1, MOE_MODE_PREFILL = 2 };
 
 typedef struct {

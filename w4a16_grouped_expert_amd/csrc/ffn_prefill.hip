@@ -18,8 +18,8 @@
 // previous one: its group is all zero codes and adds nothing), the accumulator
 // holds A_g = sum over g' <= g of D_g' e_g' / e_g, i.e.
 //   A_g = A_{g-1} * (e_{g-1} / e_g) - 1.5 * sum_k x + MFMA sum of (1 + c/16) x,
-// one fma per output per group before that group's MFMAs, and the result is
-// 16 e_last A_last.  The ratio of each row is computed once per group by the
+// one fma per output per group, applied behind the last MFMAs of group g - 1
+// (the last group's applies the factor 16 e_last, which gives the result).  The ratio of each row is computed once per group by the
 // thread that owns the row and handed over in LDS.  sum_k x per token and group
 // is precomputed (activations: a small pass; SwiGLU output: written by the
 // gate/up epilogue, whose block covers exactly two groups of h).
@@ -468,7 +468,7 @@ __global__ __launch_bounds__(kPThreads) void k_prefill(
         }
         continue;
       }
-      // acc = acc * (e_{g-1} / e_g) - 1.5 sum_k x   (acc = -1.5 sum_k x for g = 0)
+      // g = 0: acc = -1.5 sum_k x; later groups start from the rescale at the end of the previous one
       if (g == 0) {
         const f32x4_t xs = *reinterpret_cast<const f32x4_t*>(&s_xs[qb & 3][64 * wt + 4 * col]);
 #pragma unroll
@@ -477,22 +477,18 @@ __global__ __launch_bounds__(kPThreads) void k_prefill(
 #pragma unroll
           for (int t = 0; t < 4; ++t) acc[t][b] = f32x4_t{c, c, c, c};
         }
-      } else {
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const float c = -1.5f * xsn[b];
-#pragma unroll
-          for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) acc[t][b][q] = fmaf(acc[t][b][q], rn[t][q], c);
-        }
       }
-      // the next group's ratios (written at the top of g - 1) and group sums (batch g)
-      if (g + 1 < G) {
+      // applied at the end of this group: acc * (e_g / e_{g+1}) - 1.5 sum_k x of group g + 1,
+      // or acc * 16 e_last after the last group (written at the top of g - 1, or of G - 2)
+      float cn[4];
+      {
+        const float* rp = &s_ratio[(qb + g + 1) & 1][64 * wr];
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-          rn[t] = *reinterpret_cast<const f32x4_t*>(&s_ratio[(qb + g + 1) & 1][64 * wr + 16 * t + 4 * kq]);
+        for (int t = 0; t < 4; ++t) rn[t] = *reinterpret_cast<const f32x4_t*>(&rp[16 * t + 4 * kq]);
         xsn = *reinterpret_cast<const f32x4_t*>(&s_xs[(qb + g + 1) & 3][64 * wt + 4 * col]);
+        const bool more = g + 1 < G;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) cn[b] = more ? -1.5f * xsn[b] : 0.f;
       }
 
       u32x4_t cw[4];
@@ -500,38 +496,56 @@ __global__ __launch_bounds__(kPThreads) void k_prefill(
       for (int t = 0; t < 4; ++t) cw[t] = S.w[(wr * 4 + t) * 64 + lane];
       const u32x4_t* xrow = &S.x[(wt * 64 + col) * 16];  // token block b adds 256 slots
       u32x4_t xb[4], xn[4];
+      if (g + 2 < G) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) issue_part(g + 2, i, qb);
+      }
 #pragma unroll
       for (int b = 0; b < 4; ++b) xb[b] = xrow[b * 256 + (kq ^ col)];
+      u32x4_t wa[4], wn[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) wa[t] = decode_word_biased(cw[t][0], kMask, kOne);
+      auto dec1 = [&](uint32_t w, int j) -> uint32_t {
+        const uint32_t v = j == 0 ? w : (j == 3 ? rotr32(w, 12) : (w >> (4 * j)));
+        return (v & kMask) | kOne;
+      };
+      // Four K steps of 16 products.  Behind each product goes one word of the next
+      // step's decode (steps 0 to 2) or the rescale of the product two places back
+      // (step 3), in an order pinned by scheduling barriers: left to itself the
+      // compiler puts the VALU work in front of each step's products, where it
+      // cannot overlap them.
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if (i < 3) {
 #pragma unroll
           for (int b = 0; b < 4; ++b) xn[b] = xrow[b * 256 + ((4 * (i + 1) + kq) ^ col)];
         }
-        if (g + 2 < G) issue_part(g + 2, i, qb);  // spread the DMA issue over the K steps
-        bf16x8_t wa[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) wa[t] = as_bf16x8(decode_word_biased(cw[t][i], kMask, kOne));
+        for (int m = 0; m < 16; ++m) {
+          const int t = m & 3, b = m >> 2;
+          acc[t][b] = mfma16x16x32(as_bf16x8(wa[t]), as_bf16x8(xb[b]), acc[t][b]);
+          if (i < 3) {
+            wn[m >> 2][m & 3] = dec1(cw[m >> 2][i + 1], m & 3);
+          } else if (m >= 2) {
+            const int t2 = (m - 2) & 3, b2 = (m - 2) >> 2;
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-          for (int t = 0; t < 4; ++t) acc[t][b] = mfma16x16x32(wa[t], as_bf16x8(xb[b]), acc[t][b]);
+            for (int q = 0; q < 4; ++q) acc[t2][b2][q] = fmaf(acc[t2][b2][q], rn[t2][q], cn[b2]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
         if (i < 3) {
 #pragma unroll
           for (int b = 0; b < 4; ++b) xb[b] = xn[b];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) wa[t] = wn[t];
         }
       }
-    }
-    // 16 e_last (written at the top of G - 2, or in the prologue) is visible since the last barrier
-    {
-      const float* mult = &s_ratio[(qb + G) & 1][64 * wr];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const f32x4_t m = *reinterpret_cast<const f32x4_t*>(&mult[16 * t + 4 * kq]);
+      for (int m = 14; m < 16; ++m) {
+        const int t2 = m & 3, b2 = m >> 2;
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) acc[t][b][q] *= m[q];
+        for (int q = 0; q < 4; ++q) acc[t2][b2][q] = fmaf(acc[t2][b2][q], rn[t2][q], cn[b2]);
       }
     }
 

@@ -56,11 +56,19 @@ constexpr int kCacheNonTemporal = 2;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// float32 -> bf16 bits, round to nearest even (finite inputs).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+// float32 -> bf16 bits, round to nearest even (the conversion instruction of gfx950,
+// v_cvt_pk_bf16_f32, which also keeps NaNs quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+// two float32 values -> one word of two bf16 (lo in bits 0..15), one conversion instruction
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t){lo, hi}, b2_t));
+}
+// four float32 values -> four bf16 in two words, in order
+__device__ __forceinline__ u32x2_t pack_bf16x4(float a, float b, float c, float d) {
+  return u32x2_t{pack_bf16x2(a, b), pack_bf16x2(c, d)};
 }
 
 __device__ __forceinline__ uint32_t rotr32(uint32_t v, int n) {

@@ -56,8 +56,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, in
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[r] = fmaf(wj[j], v[j][r], acc[r]);
   }
-  u32x2_t o = {f32_to_bf16_bits(acc[0]) | (f32_to_bf16_bits(acc[1]) << 16),
-               f32_to_bf16_bits(acc[2]) | (f32_to_bf16_bits(acc[3]) << 16)};
+  const u32x2_t o = pack_bf16x4(acc[0], acc[1], acc[2], acc[3]);
   *reinterpret_cast<u32x2_t*>(out + t * d + n) = o;
 }
 
@@ -92,8 +91,7 @@ __global__ __launch_bounds__(256) void k_combine_bf16(const uint16_t* __restrict
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[r] = fmaf(wj[j], r4[r], acc[r]);
   }
-  u32x2_t o = {f32_to_bf16_bits(acc[0]) | (f32_to_bf16_bits(acc[1]) << 16),
-               f32_to_bf16_bits(acc[2]) | (f32_to_bf16_bits(acc[3]) << 16)};
+  const u32x2_t o = pack_bf16x4(acc[0], acc[1], acc[2], acc[3]);
   *reinterpret_cast<u32x2_t*>(out + t * d + n) = o;
 }
 

@@ -114,11 +114,11 @@ __global__ __launch_bounds__(256) void k_bf16_ffn(FfnDev f, const uint16_t* __re
         const int c = tb + 16 * b + col;
         if (c >= n_e) continue;
         if (GATEUP) {
-          uint32_t hv[4];
+          float hf[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) hv[q] = f32_to_bf16_bits(silu_f32(acc[0][b][q]) * acc[1][b][q]);
+          for (int q = 0; q < 4; ++q) hf[q] = silu_f32(acc[0][b][q]) * acc[1][b][q];
           const int hcol = kTileRows * stripe + 4 * kq;
-          u32x2_t o = {hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16)};
+          const u32x2_t o = pack_bf16x4(hf[0], hf[1], hf[2], hf[3]);
           *reinterpret_cast<u32x2_t*>(hout + (int64_t)(row0 + c) * f.I + hcol) = o;
         } else {
           float* yout = y + (int64_t)split * f.P * f.d + (int64_t)(row0 + c) * f.d;

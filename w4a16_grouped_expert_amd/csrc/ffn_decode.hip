@@ -203,12 +203,12 @@ __global__ __launch_bounds__(256) void k_decode_persist(FfnDev f, const uint16_t
     if (GATEUP) {
 #pragma unroll
       for (int p = 0; p < RT / 2; ++p) {
-        uint32_t hv[4];
+        float hf[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) hv[q] = f32_to_bf16_bits(silu_f32(tot[2 * p][q]) * tot[2 * p + 1][q]);
+        for (int q = 0; q < 4; ++q) hf[q] = silu_f32(tot[2 * p][q]) * tot[2 * p + 1][q];
         if (valid) {
           const int hcol = kTileRows * ((RT / 2) * stripe + p) + 4 * kq;
-          u32x2_t o = {hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16)};
+          const u32x2_t o = pack_bf16x4(hf[0], hf[1], hf[2], hf[3]);
           *reinterpret_cast<u32x2_t*>(hout + (int64_t)out_row * f.I + hcol) = o;
         }
       }
@@ -371,12 +371,12 @@ __global__ __launch_bounds__(512, 4) void k_gateup_dense(FfnDev f, uint16_t* __r
     e = start_item();
 #pragma unroll
     for (int p = 0; p < RT / 2; ++p) {
-      uint32_t hv[4];
+      float hf[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) hv[q] = f32_to_bf16_bits(silu_f32(tot[2 * p][q]) * tot[2 * p + 1][q]);
+      for (int q = 0; q < 4; ++q) hf[q] = silu_f32(tot[2 * p][q]) * tot[2 * p + 1][q];
       if (routed) {
         const int hcol = kTileRows * ((RT / 2) * cur_stripe + p) + 4 * kq;
-        u32x2_t o = {hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16)};
+        const u32x2_t o = pack_bf16x4(hf[0], hf[1], hf[2], hf[3]);
         *reinterpret_cast<u32x2_t*>(hout + (int64_t)out_row * f.I + hcol) = o;
       }
     }
@@ -536,12 +536,12 @@ __global__ __launch_bounds__(512, 4) void k_gateup_dense_ks2(FfnDev f, uint16_t*
       }
 #pragma unroll
       for (int p = 0; p < RT / 2; ++p) {
-        uint32_t hv[4];
+        float hf[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) hv[q] = f32_to_bf16_bits(silu_f32(tot[2 * p][q]) * tot[2 * p + 1][q]);
+        for (int q = 0; q < 4; ++q) hf[q] = silu_f32(tot[2 * p][q]) * tot[2 * p + 1][q];
         if (routed) {
           const int hcol = kTileRows * ((RT / 2) * cur_stripe + p) + 4 * kq;
-          u32x2_t o = {hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16)};
+          const u32x2_t o = pack_bf16x4(hf[0], hf[1], hf[2], hf[3]);
           *reinterpret_cast<u32x2_t*>(hout + (int64_t)out_row * f.I + hcol) = o;
         }
       }
@@ -687,7 +687,7 @@ __global__ __launch_bounds__(256) void k_ffn_decode(FfnDev f, const uint16_t* __
       for (int combo = wave; combo < (RT / 2) * NB; combo += 4) {
         const int p = combo / NB, b = combo % NB;
         const int c = tb0 + 16 * b + col;
-        uint32_t hv[4];
+        float hf[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           float gsum = 0.f, usum = 0.f;
@@ -696,11 +696,11 @@ __global__ __launch_bounds__(256) void k_ffn_decode(FfnDev f, const uint16_t* __
             gsum += red[w][2 * p][b][q][lane];
             usum += red[w][2 * p + 1][b][q][lane];
           }
-          hv[q] = f32_to_bf16_bits(silu_f32(gsum) * usum);
+          hf[q] = silu_f32(gsum) * usum;
         }
         if (c < n_e) {
           const int hcol = kTileRows * ((RT / 2) * stripe + p) + 4 * kq;
-          u32x2_t o = {hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16)};
+          const u32x2_t o = pack_bf16x4(hf[0], hf[1], hf[2], hf[3]);
           *reinterpret_cast<u32x2_t*>(hout + (int64_t)(row0 + c) * f.I + hcol) = o;
         }
       }

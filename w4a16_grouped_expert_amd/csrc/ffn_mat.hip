@@ -203,12 +203,12 @@ __global__ __launch_bounds__(512, 4) void k_mat_gateup(FfnDev f, MatOffsets mo, 
       mat_stripe<true, RT, NB>(hip, lop, scales, tile_stride_p, tile_stride_s, P2, 0, P2, xfrag, xsum, tot);
     else
       mat_stripe<false, RT, NB>(hip, lop, scales, tile_stride_p, tile_stride_s, P2, 0, P2, xfrag, xsum, tot);
-    uint32_t hv[4];
+    float hf[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) hv[q] = f32_to_bf16_bits(silu_f32(tot[0][q]) * tot[1][q]);
+    for (int q = 0; q < 4; ++q) hf[q] = silu_f32(tot[0][q]) * tot[1][q];
     if (routed) {
       const int hcol = kTileRows * stripe + 4 * kq;
-      u32x2_t o = {hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16)};
+      const u32x2_t o = pack_bf16x4(hf[0], hf[1], hf[2], hf[3]);
       *reinterpret_cast<u32x2_t*>(hout + (int64_t)out_row * f.I + hcol) = o;
     }
   }

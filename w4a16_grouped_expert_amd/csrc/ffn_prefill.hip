@@ -560,15 +560,15 @@ __global__ __launch_bounds__(kPThreads) void k_prefill(
         const bool ok = mt * kPBM + r < n_e;
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-          uint32_t hv[4];
+          float hf[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            hv[q] = f32_to_bf16_bits(silu_fast(acc[2 * p][b][q]) * acc[2 * p + 1][b][q]);
-            hs[b] += __uint_as_float(hv[q] << 16);
-          }
+          for (int q = 0; q < 4; ++q) hf[q] = silu_fast(acc[2 * p][b][q]) * acc[2 * p + 1][b][q];
+          const u32x2_t o = pack_bf16x4(hf[0], hf[1], hf[2], hf[3]);
+#pragma unroll
+          for (int w = 0; w < 2; ++w)  // the sum of the bf16 values that are stored
+            hs[b] += __uint_as_float(o[w] << 16) + __uint_as_float(o[w] & 0xFFFF0000u);
           if (ok) {
             const int hcol = nt * 128 + wr * 32 + 16 * p + 4 * kq;
-            u32x2_t o = {hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16)};
             *reinterpret_cast<u32x2_t*>(hout + (int64_t)pos * f.I + hcol) = o;
           }
         }
@@ -595,8 +595,7 @@ __global__ __launch_bounds__(kPThreads) void k_prefill(
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             const int n = nt * kPBN + wr * 64 + t * 16 + 4 * kq;
-            const u32x2_t o = {f32_to_bf16_bits(acc[t][b][0]) | (f32_to_bf16_bits(acc[t][b][1]) << 16),
-                               f32_to_bf16_bits(acc[t][b][2]) | (f32_to_bf16_bits(acc[t][b][3]) << 16)};
+            const u32x2_t o = pack_bf16x4(acc[t][b][0], acc[t][b][1], acc[t][b][2], acc[t][b][3]);
             if (n < N) *reinterpret_cast<u32x2_t*>(yout + (int64_t)pos * f.d + n) = o;
           }
         }

@@ -504,12 +504,12 @@ __global__ __launch_bounds__(512, 4) void k_layer_gateup(FfnDev f, RouteDev r, u
     for (int j = 0; j < k; ++j) hit = s_ids[col][j] == e ? j : hit;
 #pragma unroll
     for (int p = 0; p < RT / 2; ++p) {
-      uint32_t hv[4];
+      float hf[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) hv[q] = f32_to_bf16_bits(silu_f32(tot[2 * p][q]) * tot[2 * p + 1][q]);
+      for (int q = 0; q < 4; ++q) hf[q] = silu_f32(tot[2 * p][q]) * tot[2 * p + 1][q];
       if (hit >= 0) {
         const int hcol = kTileRows * ((RT / 2) * stripe + p) + 4 * kq;
-        u32x2_t o = {hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16)};
+        const u32x2_t o = pack_bf16x4(hf[0], hf[1], hf[2], hf[3]);
         *reinterpret_cast<u32x2_t*>(hout + (int64_t)(col * k + hit) * f.I + hcol) = o;
       }
     }

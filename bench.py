@@ -30,6 +30,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+_T_START = time.time()
+
+
+def progress(msg):
+    """One line on stderr as each part of the run ends (stdout carries only the JSON line)."""
+    print(f"[bench {time.time() - _T_START:6.1f} s] {msg}", file=sys.stderr, flush=True)
+
+
 METRIC = "MoE-layer tokens/s + achieved HBM GB/s (W4A16, OLMoE shape, T=1..4096)"
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
@@ -905,6 +913,7 @@ def parity_verdicts(args, threads, slot_probe=None):
         res[name] = {"tokens_compared": int(x.shape[0]), "ids_bit_exact": ids_eq, "max_rel_err": round(whole, 6),
                      "worst_token_rel_err": round(tok, 6),
                      "pass": bool(ids_eq and finite and whole <= tol and tok <= tol)}
+        progress(f"parity {name}: {'pass' if res[name]['pass'] else 'FAIL'}")
 
     def used_experts(wl, xs):
         wr = _bits(synth.router_weight(wl, 0))
@@ -996,11 +1005,13 @@ def main():
     Ts = sorted({args.tokens} | {int(t) for t in args.sweep.split(",") if t})
     dec = Decoder(wl, max(Ts), "cuda", fused=not args.two_call)
     head = run_decode(dec, args.tokens, args.steps, args.warmup, args.x_sets)
+    progress(f"decode T={args.tokens}: {head['tokens_per_s']:.0f} tok/s")
     sweep = {}
     for T in Ts:
         if T == args.tokens:
             continue
         r = run_decode(dec, T, args.steps, args.warmup, args.x_sets)
+        progress(f"decode T={T}: {r['tokens_per_s']:.0f} tok/s")
         sweep[f"T={T}"] = {k: r[k] for k in ("tokens_per_s", "hbm_gbps", "ms_per_step", "ms_per_step_eager",
                                              "mean_distinct_experts")}
         if "gateup_decode" in r.get("kernels", {}):
@@ -1051,29 +1062,36 @@ def main():
                     "the host; graph: both replayed from HIP graphs (the pages report 1.97x for their "
                     "fused kernels)",
             **{f"T={T}": run_ablation(dec, T, max(4, args.steps // 5)) for T in (args.tokens, 1)}}
+        progress("fused vs per-expert ablation")
     del dec
     torch.cuda.empty_cache()
     w4 = {args.tokens: head["tokens_per_s"]}
     w4.update({int(k[2:]): v["tokens_per_s"] for k, v in sweep.items()})
     if not args.no_bf16:
         out["bf16_experts"] = run_bf16_compare(sorted(w4), args.steps, args.warmup, args.x_sets, w4)
+        progress("bf16 experts")
     if not args.no_mat:
         out["nested_2_4_bit"] = run_mat_compare([t for t in (args.tokens, 1) if t in w4], (0.0, 0.14, 2.0),
                                                 args.steps, args.warmup, args.x_sets, w4)
+        progress("nested two/four-bit experts")
     if args.prefill_tokens > 0:
         out["prefill"] = run_prefill(args.prefill_tokens)
+        progress(f"prefill T={args.prefill_tokens}")
         extra = {}
         for T in [int(t) for t in args.prefill_sweep.split(",") if t]:
             r = run_prefill(T)
+            progress(f"prefill T={T}")
             extra[f"T={T}"] = {k: r[k] for k in ("tokens_per_s", "ms_per_layer", "kernels_us")}
             extra[f"T={T}"]["gateup_mfma_frac"] = r["roofline"]["frac"]
         if extra:
             out["prefill_sweep"] = extra
     if not args.no_large:
         out["large_expert"] = run_large(synth.LARGE.tokens)
+        progress("large expert")
     slot_probe = None
     if not args.no_slot_cache:
         out["slot_cache"], slot_probe = run_slot_cache(args.slot_steps)
+        progress("slot cache")
     ok = True
     if not args.no_cpu_baseline:
         host = host_facts()
@@ -1085,6 +1103,7 @@ def main():
                                 "dequantised weights); layer 0 of each configuration, every token",
                          "all_pass": ok, "configs": verdicts}
         out["cpu_baseline"] = cpu_baseline(wl, args.tokens, args.cpu_seconds, threads, bank=dec_bank)
+        progress("cpu baseline")
         out["cpu_baseline"]["host"] = host
     print(json.dumps(out))
     if not ok:

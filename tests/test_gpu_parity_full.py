@@ -191,6 +191,30 @@ def test_olmoe_prefill_every_token(olmoe_prefill, T):
                         ref["out"])
 
 
+@pytest.mark.parametrize("T", [48, 160, 168])
+def test_olmoe_around_mode_threshold(olmoe_prefill, T):
+    """Both grouped variants on every token around the automatic choice (decode kernels
+    up to 20 expected pairs per expert, T k / E; T = 48: one 16-token block per pass,
+    T = 160: two, the last step that picks them; T = 168: the MFMA-tiled kernels), and
+    the automatic output bit-identical to the variant the rule names (the kernels are
+    deterministic)."""
+    L = olmoe_prefill
+    s = L.s
+    per_expert = T * s.k / s.E
+    say(f"OLMoE T={T} ({per_expert:.1f} pairs per expert): both variants, every token")
+    x = synth.activations(L.wl, T, L.layer)
+    ref = oracle_step(L, x)
+    xd, wrd = x.to(DEV), L.wr.to(DEV)
+    r, a = route_align(L, xd, wrd)
+    check_route(r, ref)
+    dec = ffn(L, xd, r, a, moe.MODE_DECODE)
+    pre = ffn(L, xd, r, a, moe.MODE_PREFILL)
+    auto = ffn(L, xd, r, a)
+    check_layer_out("decode kernels", dec, ref["out"])
+    check_layer_out("prefill kernels", pre, ref["out"])
+    assert np.array_equal(auto, dec if per_expert <= 20 else pre)
+
+
 # ------------------------------------------------------------------ large expert
 
 @pytest.mark.parametrize("T", [1, 64, 1024])

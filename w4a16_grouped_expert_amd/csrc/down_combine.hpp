@@ -23,8 +23,9 @@ constexpr int kDcRT = 2, kDcD = 2, kDcWaves = 8, kDcOcc = 4;
 // one active expert and one slice of UPW of its K groups (the 16 MFMA columns
 // being the step's tokens, as in the gate/up pass); a workgroup holds WAVES
 // consecutive (expert, slice) items of one stripe, a chunk of the stripe's list.
-// The slice is unrolled completely: the loads of group i + D (weights, scales,
-// the pairs' h fragments) go out before group i is multiplied, in straight-line
+// The slice is unrolled completely: the loads of group i + D (weights and the
+// pairs' h fragments; the slice's scales come in once, at its start, and are
+// read from LDS) go out before group i is multiplied, in straight-line
 // code with no branch, so the compiler counts the loads to wait for exactly and
 // never moves registers that a load in flight will write.  The wavefronts meet
 // in LDS in wavefront order, and the workgroup stores its 16 tokens x 16 RT rows
@@ -79,15 +80,23 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_down_combine(FfnDev f, cons
   i32x4_t rec = (PAIR || SPEC) ? i32x4_t{0, 0, 0, 0}
                                : reinterpret_cast<const i32x4_t*>(f.active + 4)[min(item / n_slices, f.umax - 1)];
 
-  const uint32_t voff_c = 16u * lane, voff_s = 8u * kq;
+  const uint32_t voff_c = 16u * lane;
   const uint32_t soff_c = (uint32_t)(f.off_w2_codes + (int64_t)(RT * stripe) * NU * kTileBytes);
   const uint32_t soff_l = MAT ? (uint32_t)(f.off_w2_lo + (int64_t)(RT * stripe) * NU * kTileBytes) : 0u;
   const uint32_t soff_s = (uint32_t)(f.off_w2_scales + (int64_t)(RT * stripe) * G * kTileRows * 2);
   struct Buf {
     u32x4_t c[RT];            // codes (v1) or high plane (m1)
     u32x4_t l[MAT ? RT : 1];  // low plane (m1)
-    u32x2_t s[RT][kGpu];      // scales of the unit's groups
   };
+  // The slice's scales (per tile its UPW K units' groups x 16 rows of bf16,
+  // contiguous in the blob) come in with the item's first loads, 16 bytes per lane,
+  // and wait in the wavefront's own LDS area for their groups (one LDS read per
+  // tile and group instead of a memory load)
+  constexpr int kSclTile = UPW * kGpu * kTileRows * 2;               // bytes per tile
+  constexpr int kSclLd = (RT * kSclTile + 1023) / 1024;              // 16-byte loads per lane
+  __shared__ u32x4_t s_scl[WAVES][kSclLd * 64];
+  __amdgpu_buffer_rsrc_t scl_res = __builtin_amdgcn_make_buffer_rsrc((void*)f.bank, (short)0, 0, kBufferRsrcWord3);
+  u32x4_t scl_v[kSclLd];
   struct XBuf {
     u32x4_t x[4];
   };
@@ -120,17 +129,29 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_down_combine(FfnDev f, cons
         b.l[r] = __builtin_bit_cast(
             u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
                          lres, voff_c, soff_l + (uint32_t)(r * NU + u) * kTileBytes, kCacheNonTemporal));
-#pragma unroll
-      for (int hg = 0; hg < kGpu; ++hg)
-        b.s[r][hg] = __builtin_bit_cast(
-            u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(
-                         wres, voff_s, soff_s + (uint32_t)(r * G + kGpu * u + hg) * kTileRows * 2, 0));
     }
+  };
+  // chunk c = lane + 64 j of the slice's scales: tile c * 16 / kSclTile, bytes c * 16 % kSclTile
+  // from its first group; past the stripe's scales the loads read zeros
+  auto scl_load = [&]() {
+#pragma unroll
+    for (int j = 0; j < kSclLd; ++j) {
+      const int c = lane + 64 * j, r = c * 16 / kSclTile, within = c * 16 % kSclTile;
+      scl_v[j] = __builtin_bit_cast(
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                       scl_res, (uint32_t)((r * G + kGpu * u0) * kTileRows * 2 + within), 0, 0));
+    }
+  };
+  auto scl_store = [&]() {
+#pragma unroll
+    for (int j = 0; j < kSclLd; ++j) s_scl[wave][lane + 64 * j] = scl_v[j];
   };
   auto set_expert = [&](int e) {
     const int slot = f.slot_of_expert ? f.slot_of_expert[e] : e;
     wres = __builtin_amdgcn_make_buffer_rsrc((void*)(f.bank + (int64_t)slot * f.bank_stride), (short)0, 0x7FFFFFFF,
                                              kBufferRsrcWord3);
+    scl_res = __builtin_amdgcn_make_buffer_rsrc((void*)(f.bank + (int64_t)slot * f.bank_stride + soff_s), (short)0,
+                                                RT * G * kTileRows * 2, kBufferRsrcWord3);
     if constexpr (PREC == kPrecAll4) lres = wres;
     u0 = (item % n_slices) * UPU;
     nu = min(UPU, NU - u0);
@@ -148,6 +169,7 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_down_combine(FfnDev f, cons
     rec[0] = item / n_slices;
     if (!PAIR) rec[1] = f.offsets[rec[0]];
     set_expert(rec[0]);
+    scl_load();
 #pragma unroll
     for (int j = 0; j < NPRO; ++j) wload(PreLo{}, buf[j], j);
   }
@@ -241,7 +263,8 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_down_combine(FfnDev f, cons
       const float xs = xcoef * as[0];  // every row of the ones product holds the column's group sum
 #pragma unroll
       for (int r = 0; r < RT; ++r) {
-        const u32x2_t sw = b.s[r][hg];
+        const int gi = kGpu * min(i / kGpu, nu - 1) + hg;  // the group within the slice
+        const u32x2_t sw = reinterpret_cast<const u32x2_t*>(s_scl[wave])[r * (kSclTile / 8) + gi * 4 + kq];
         const float s4[4] = {__uint_as_float(sw[0] << 16), __uint_as_float(sw[0] & 0xFFFF0000u),
                              __uint_as_float(sw[1] << 16), __uint_as_float(sw[1] & 0xFFFF0000u)};
 #pragma unroll
@@ -250,6 +273,7 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_down_combine(FfnDev f, cons
     };
     XBuf xbuf[DX + 1];
     if (!early) {
+      scl_load();
 #pragma unroll
       for (int j = 0; j < NPRO; ++j) wload(ItemLo{}, buf[j], j);
     } else if constexpr (PREC == kPrecMixed) {
@@ -258,6 +282,7 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_down_combine(FfnDev f, cons
     }
 #pragma unroll
     for (int j = 0; j < DX; ++j) xload(xbuf[j], j);
+    scl_store();
     // the scheduling barriers keep each group's loads ahead of the multiply that
     // precedes their use (the scheduler would otherwise sink them to their users)
     __builtin_amdgcn_sched_barrier(0);

@@ -196,11 +196,26 @@ __global__ __launch_bounds__(512, 4) void k_layer_gateup(FfnDev f, RouteDev r, u
   struct Buf {
     u32x4_t c[RT];            // codes (v1) or high plane (m1)
     u32x4_t l[MAT ? RT : 1];  // low plane (m1)
-    u32x2_t s[RT][kGpu];      // scales of the unit's groups
   };
   Buf buf[NB];
   const uint8_t* codes = nullptr;
-  const uint16_t* scales = nullptr;
+  // The item's scales (RT tiles x G groups x 16 rows of bf16, contiguous in the
+  // blob) come in at the item's start, one 16-byte load per lane, and wait in the
+  // wavefront's own LDS area for their groups (one LDS read per tile and group
+  // instead of a memory load)
+  constexpr int kSclLd = RT * MAXG * 32 / 1024;  // 16-byte loads per lane
+  __shared__ u32x4_t s_scl[kWaves][kSclLd * 64];
+  __amdgpu_buffer_rsrc_t scl_res = __builtin_amdgcn_make_buffer_rsrc((void*)f.bank, (short)0, 0, kBufferRsrcWord3);
+  u32x4_t scl_v[kSclLd];
+  auto scl_load = [&]() {
+#pragma unroll
+    for (int j = 0; j < kSclLd; ++j)
+      scl_v[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(scl_res, 16u * (lane + 64 * j), 0, 0));
+  };
+  auto scl_store = [&]() {
+#pragma unroll
+    for (int j = 0; j < kSclLd; ++j) s_scl[wave][lane + 64 * j] = scl_v[j];
+  };
   // m1: the item's low plane through a buffer resource
   __amdgpu_buffer_rsrc_t lres = __builtin_amdgcn_make_buffer_rsrc((void*)f.bank, (short)0, 0, kBufferRsrcWord3);
   uint32_t lo_off = 0;  // the item's stripe of the low plane in its blob
@@ -225,9 +240,6 @@ __global__ __launch_bounds__(512, 4) void k_layer_gateup(FfnDev f, RouteDev r, u
       b.c[rr] = __builtin_nontemporal_load(
           reinterpret_cast<const u32x4_t*>(codes + rr * tile_stride_c + (int64_t)ul * kTileBytes));
       if constexpr (MAT && LO) lo_load(b, rr, ul);
-#pragma unroll
-      for (int hg = 0; hg < kGpu; ++hg)
-        b.s[rr][hg] = *reinterpret_cast<const u32x2_t*>(scales + rr * tile_stride_s + (kGpu * ul + hg) * kTileRows);
     }
   };
   // the low plane alone, for units whose other loads went out before the item's precision was known
@@ -243,8 +255,9 @@ __global__ __launch_bounds__(512, 4) void k_layer_gateup(FfnDev f, RouteDev r, u
     const int64_t roff = (int64_t)(RT * stripe) * tile_stride_c;
     codes = blob + f.off_w13_codes + roff + 16 * lane;
     if constexpr (MAT) lo_off = (uint32_t)(f.off_w13_lo + roff);
-    scales = reinterpret_cast<const uint16_t*>(blob + f.off_w13_scales) + (int64_t)(RT * stripe) * G * kTileRows +
-             4 * kq;
+    scl_res = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(blob + f.off_w13_scales + (int64_t)(RT * stripe) * tile_stride_s * 2), (short)0, RT * G * 32,
+        kBufferRsrcWord3);
   };
   // the item's precision (m1): the low plane's records and the X coefficient
   auto set_precision = [&](int e, bool full) {
@@ -270,6 +283,7 @@ __global__ __launch_bounds__(512, 4) void k_layer_gateup(FfnDev f, RouteDev r, u
   auto prefetch = [&]() {
     if (prefetched) {
       set_item(item / n_stripes, item % n_stripes);
+      scl_load();
 #pragma unroll
       for (int j = 0; j < NB - 1; ++j) load(std::false_type{}, buf[j], j);
     }
@@ -490,7 +504,7 @@ __global__ __launch_bounds__(512, 4) void k_layer_gateup(FfnDev f, RouteDev r, u
       }
 #pragma unroll
       for (int rr = 0; rr < RT; ++rr) {
-        const u32x2_t sw = b.s[rr][hg];
+        const u32x2_t sw = reinterpret_cast<const u32x2_t*>(s_scl[wave])[rr * G * 4 + g * 4 + kq];
         const float s4[4] = {__uint_as_float(sw[0] << 16), __uint_as_float(sw[0] & 0xFFFF0000u),
                              __uint_as_float(sw[1] << 16), __uint_as_float(sw[1] & 0xFFFF0000u)};
 #pragma unroll
@@ -532,8 +546,10 @@ __global__ __launch_bounds__(512, 4) void k_layer_gateup(FfnDev f, RouteDev r, u
         const int e = s_act[it / n_stripes];
         set_item(e, it % n_stripes);
         set_precision(e, item_full(e));
+        scl_load();
 #pragma unroll
         for (int j = 0; j < NB - 1; ++j) load(ItemLo{}, buf[j], g0 + j);
+        scl_store();
         for (int gc = g0; gc < g_lim; gc += NB) {
 #pragma unroll
           for (int j = 0; j < NB; ++j) {
@@ -581,6 +597,7 @@ __global__ __launch_bounds__(512, 4) void k_layer_gateup(FfnDev f, RouteDev r, u
         if (!have_loads) {
           set_item(e, item % n_stripes);
           set_precision(e, item_full(e));
+          scl_load();
 #pragma unroll
           for (int j = 0; j < NB - 1; ++j) load(ItemLo{}, buf[j], j);
           lo_pending = false;
@@ -592,6 +609,7 @@ __global__ __launch_bounds__(512, 4) void k_layer_gateup(FfnDev f, RouteDev r, u
     int e = start_item(prefetched);
     while (e >= 0) {
       const int stripe = item % n_stripes, cur_e = e;
+      scl_store();  // the item's scales, loaded with its first groups
       f32x4_t tot[RT];
 #pragma unroll
       for (int rr = 0; rr < RT; ++rr) tot[rr] = f32x4_t{0.f, 0.f, 0.f, 0.f};

@@ -577,26 +577,36 @@ __global__ __launch_bounds__(256) void k_ffn_decode(FfnDev f, const uint16_t* __
 
   const uint8_t* codes = blob + (GATEUP ? f.off_w13_codes : f.off_w2_codes) +
                          (int64_t)(RT * stripe) * G * kTileBytes + 16 * lane;
-  const uint16_t* scales = reinterpret_cast<const uint16_t*>(blob + (GATEUP ? f.off_w13_scales : f.off_w2_scales)) +
-                           (int64_t)(RT * stripe) * G * kTileRows + 4 * kq;
+  // a chunk's scales (RT tiles x GPW groups x 16 rows of bf16) in one 16-byte load
+  // per lane: lane c holds half c % 2 of group (c / 2) % GPW of tile c / (2 GPW);
+  // they go through the wavefront's LDS area to the lanes that apply them
+  static_assert(RT * GPW * 2 <= 64, "a chunk's scales in one load per lane");
+  const __amdgpu_buffer_rsrc_t sres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(blob + (GATEUP ? f.off_w13_scales : f.off_w2_scales) + (int64_t)(RT * stripe) * G * kTileRows * 2),
+      (short)0, RT * G * kTileRows * 2, kBufferRsrcWord3);
+  const int sc_r = lane / (2 * GPW), sc_gi = (lane / 2) % GPW, sc_half = lane & 1;
+  __shared__ u32x4_t s_sw[4][64];
+  u32x4_t swv;
   const int64_t tile_stride_c = (int64_t)G * kTileBytes;  // bytes between row tiles
-  const int64_t tile_stride_s = (int64_t)G * kTileRows;   // scales between row tiles
   const u32x4_t ones_w = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   const bf16x8_t ones = as_bf16x8(ones_w);
 
   u32x4_t cw[GPW][RT];
-  u32x2_t sw[GPW][RT];
   auto load_chunk = [&](int gc) {
+    {  // the scales first: waiting for them does not wait for the codes
+      const int g = gc + sc_gi;
+      const uint32_t off = (sc_r < RT && g < g1) ? (uint32_t)((sc_r * G + g) * kTileRows + 8 * sc_half) * 2u
+                                                 : 0x7F000000u;  // else zeros
+      swv = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sres, off, 0, 0));
+    }
 #pragma unroll
     for (int gi = 0; gi < GPW; ++gi) {
       const int g = gc + gi;
       if (g < g1) {
 #pragma unroll
-        for (int r = 0; r < RT; ++r) {
+        for (int r = 0; r < RT; ++r)
           cw[gi][r] = __builtin_nontemporal_load(
               reinterpret_cast<const u32x4_t*>(codes + r * tile_stride_c + (int64_t)g * kTileBytes));
-          sw[gi][r] = *reinterpret_cast<const u32x2_t*>(scales + r * tile_stride_s + g * kTileRows);
-        }
       }
     }
   };
@@ -624,6 +634,7 @@ __global__ __launch_bounds__(256) void k_ffn_decode(FfnDev f, const uint16_t* __
 
     for (int gc = g0; gc < g1; gc += GPW) {
       if (gc != g0 || tb0 != 0) load_chunk(gc);
+      s_sw[wave][lane] = swv;  // the chunk's scales (the wavefront's LDS ops run in order)
       // activation fragments: with one token block the whole chunk's are issued
       // together (they come from L2); with more blocks, group by group (registers)
       constexpr int XG = (NB == 1) ? GPW : 1;
@@ -666,8 +677,9 @@ __global__ __launch_bounds__(256) void k_ffn_decode(FfnDev f, const uint16_t* __
         }
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
-          const float s4[4] = {bf16_bits_to_f32(sw[gi][r][0] & 0xFFFFu), bf16_bits_to_f32(sw[gi][r][0] >> 16),
-                               bf16_bits_to_f32(sw[gi][r][1] & 0xFFFFu), bf16_bits_to_f32(sw[gi][r][1] >> 16)};
+          const u32x2_t sw = reinterpret_cast<const u32x2_t*>(s_sw[wave])[(r * GPW + gi) * 4 + kq];
+          const float s4[4] = {bf16_bits_to_f32(sw[0] & 0xFFFFu), bf16_bits_to_f32(sw[0] >> 16),
+                               bf16_bits_to_f32(sw[1] & 0xFFFFu), bf16_bits_to_f32(sw[1] >> 16)};
 #pragma unroll
           for (int b = 0; b < NB; ++b)
 #pragma unroll

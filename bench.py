@@ -992,8 +992,8 @@ def parity_verdicts(args, threads, slot_probe=None):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the multi-GPU sharding is described, not built)", file=sys.stderr)
+        print(f"bench.py: measures one GPU only; --gpus {args.gpus} is not supported "
+              "(sharding the layer over several GPUs is not implemented)", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()

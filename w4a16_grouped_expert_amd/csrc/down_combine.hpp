@@ -88,11 +88,11 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void k_down_combine(FfnDev f, cons
     u32x4_t c[RT];            // codes (v1) or high plane (m1)
     u32x4_t l[MAT ? RT : 1];  // low plane (m1)
   };
-  // The slice's scales (per tile its UPW K units' groups x 16 rows of bf16,
+  // The slice's scales (per tile its UPW groups x 16 rows of bf16,
   // contiguous in the blob) come in with the item's first loads, 16 bytes per lane,
   // and wait in the wavefront's own LDS area for their groups (one LDS read per
   // tile and group instead of a memory load)
-  constexpr int kSclTile = UPW * kGpu * kTileRows * 2;               // bytes per tile
+  constexpr int kSclTile = UPW * kTileRows * 2;                      // bytes per tile (UPW groups)
   constexpr int kSclLd = (RT * kSclTile + 1023) / 1024;              // 16-byte loads per lane
   __shared__ u32x4_t s_scl[WAVES][kSclLd * 64];
   __amdgpu_buffer_rsrc_t scl_res = __builtin_amdgcn_make_buffer_rsrc((void*)f.bank, (short)0, 0, kBufferRsrcWord3);

@@ -2,7 +2,9 @@
 (moe_decode_layer) and the grouped expert FFN in both variants, each against the
 float64 oracle on every token; and the fused decode layer on nested two/four-bit
 blobs (moe_mat_decode_layer) against the nested oracle at several precision
-thresholds, bit-identical to moe_decode_layer when every expert runs at four bits.
+thresholds, bit-identical to moe_decode_layer when every expert runs at four bits;
+and prefill-sized steps through the MFMA-tiled kernels (ragged token tiles, row
+tiles that overhang the model dimension, many experts).
 
 The shapes reach the corners of the entry points' limits: a single K group each
 way (d or I = 128), k = 1 and k = E, expert counts that are not multiples of 16,
@@ -113,3 +115,34 @@ def test_mat_shape_every_token(T, d, I, E, k, tau):
         out4, _ = moe.moe_decode_layer(xd, wrd, w4, I, k)
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), out4.view(torch.int16))
+
+
+# prefill-sized steps: several 128-token tiles per expert with ragged tails, row
+# tiles that overhang N (d = 384, 640), many experts with light last tiles
+PREFILL_SHAPES = [
+    (600, 384, 384, 20, 4),
+    (333, 640, 256, 130, 6),
+    (1000, 256, 128, 7, 2),
+]
+
+
+@pytest.mark.parametrize("T,d,I,E,k", PREFILL_SHAPES)
+def test_prefill_shape_every_token(T, d, I, E, k):
+    say(f"prefill shape T={T} d={d} I={I} E={E} k={k}")
+    seed = 3000 * E + 10 * k + T
+    w13 = synth.normal_bf16((E, 2 * I, d), 0.05, seed)
+    w2 = synth.normal_bf16((E, d, I), 0.05, seed + 1)
+    wr = synth.normal_bf16((E, d), 0.05, seed + 2)
+    x = synth.normal_bf16((T, d), 1.0, seed + 3)
+    ref = offn.moe_layer(bits(x), bits(wr), oracle_bank(w13, w2), k)
+    bank, _ = moe.pack_experts(w13.to(DEV), w2.to(DEV))
+    xd, wrd = x.to(DEV), wr.to(DEV)
+    r = moe.moe_route(xd, wrd, k)
+    a = moe.moe_align(r.ids, E)
+    torch.cuda.synchronize()
+    assert np.array_equal(r.ids.cpu().numpy(), ref["ids"])
+    for mode, name in ((moe.MODE_PREFILL, "grouped ffn, MFMA-tiled kernels"),
+                       (moe.MODE_AUTO, "grouped ffn, automatic choice")):
+        got = moe.moe_w4a16_grouped_ffn(xd, r, a, bank, I, mode=mode)
+        torch.cuda.synchronize()
+        check_layer_out(name, got.float().cpu().numpy(), ref["out"])

@@ -105,13 +105,23 @@ static int resolve_mode(int T, int E, int k, int mode) {
   return per_expert <= 20.0 ? MOE_MODE_DECODE : MOE_MODE_PREFILL;
 }
 
+// token blocks of 16 per pass of the decode kernels (grouped FFN, more than 16 tokens)
+static int decode_token_blocks(int T, int E, int k) { return (double)T * k / E <= 8.0 ? 1 : 2; }
+
 static int down_ksplit(int T, int d, int I, int E, int k, int mode) {
   if (mode == MOE_MODE_PREFILL) return 1;
   const int64_t umax = std::min<int64_t>(E, (int64_t)T * k);
-  const int64_t blocks = umax * (d / 64);  // down blocks own 64 output rows
-  const int max_split = std::max(1, (I / kGroup) / 4);
+  if (decode_token_blocks(T, E, k) <= 1) {  // down blocks own 64 output rows, a quarter split each wavefront
+    const int64_t blocks = umax * (d / 64);
+    const int max_split = std::max(1, (I / kGroup) / 4);
+    int ks = 1;
+    while (ks * 2 <= max_split && blocks * ks < 2048) ks *= 2;
+    return ks;
+  }
+  const int64_t blocks = umax * ceil_div(d, 256);  // down blocks own 4 x 64 output rows
+  const int max_split = std::max(1, (I / kGroup) / 8);  // more than 8 groups per split
   int ks = 1;
-  while (ks * 2 <= max_split && blocks * ks < 2048) ks *= 2;
+  while (ks * 2 <= max_split && blocks * ks < 1024) ks *= 2;
   return ks;
 }
 
@@ -254,8 +264,7 @@ extern "C" int moe_w4a16_grouped_ffn(const moe_ffn_args* a, void* stream) {
   const bool fused = mode == MOE_MODE_DECODE && a->T <= 16 && a->combine && !a->slot_of_expert && w.dc_part &&
                      a->bank_stride < ((int64_t)1 << 31) && dc_units_per_wave(f.umax, a->I / kGroup, a->d / 32) > 0;
   if (mode == MOE_MODE_DECODE) {
-    const double per_expert = (double)a->T * a->k / a->E;
-    rc = launch_decode(f, w.h, w.y, w.ksplit, per_expert <= 8.0 ? 1 : 2, s, fused ? a->out : nullptr, w.dc_part,
+    rc = launch_decode(f, w.h, w.y, w.ksplit, decode_token_blocks(a->T, a->E, a->k), s, fused ? a->out : nullptr, w.dc_part,
                        w.dc_counters);
   } else {
     rc = launch_prefill(f, w.h, reinterpret_cast<uint16_t*>(w.y), w.xsum, w.hsum, s);

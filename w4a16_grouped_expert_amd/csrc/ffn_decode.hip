@@ -15,13 +15,15 @@
 // scale is applied once per group in fp32, so the arithmetic is that of the
 // dequantised weights q * scale with fp32 accumulation.
 //
-// Work split: a block (4 wavefronts) owns one active expert and a stripe of RT
-// packed 16-row tiles (gate/up: RT/2 gate+up tile pairs, so SwiGLU is applied
-// in the block; down: RT*16 output rows).  The wavefronts split the expert's K
-// groups; each issues the loads of up to GPW groups x RT tiles at once (8-16 KiB
-// per wavefront in flight) before decoding, then the partial sums meet in LDS in
-// a fixed order.  Down may further split K over blocks (partials summed in a
-// fixed order by the combine kernel).
+// Work split: a block (4 wavefronts) owns one active expert and four adjacent
+// stripes of RT packed 16-row tiles, one per wavefront (gate/up: RT/2 gate+up
+// tile pairs, so SwiGLU is applied in the wavefront; down: RT*16 output rows).
+// Each wavefront runs its stripe over the whole K range of the block's split,
+// issuing the loads of up to GPW groups x RT tiles at once before decoding; the
+// four share the token block's activations, which each thread stages into LDS
+// with one load per group instead of every wavefront loading all of them.  Down
+// may further split K over blocks (partials summed in a fixed order by the
+// combine kernel).
 #include "align_block.hpp"
 #include "down_combine.hpp"
 #include "ffn_common.hpp"
@@ -550,8 +552,13 @@ __global__ __launch_bounds__(512, 4) void k_gateup_dense_ks2(FfnDev f, uint16_t*
   }
 }
 
+// One token block (at most 16 pairs per expert): the wavefronts of a block split
+// one stripe's K groups (short chains of loads per wavefront) and add their
+// partial sums in LDS in a fixed order; each loads its own activations.  With so
+// little arithmetic per group, sharing the activations through LDS costs more in
+// barriers than the loads it saves (measured), unlike two token blocks below.
 template <int NB, int RT, int GPW, bool GATEUP>
-__global__ __launch_bounds__(256) void k_ffn_decode(FfnDev f, const uint16_t* __restrict__ hin,
+__global__ __launch_bounds__(256) void k_ffn_decode_ksw(FfnDev f, const uint16_t* __restrict__ hin,
                                                     uint16_t* __restrict__ hout, float* __restrict__ y, int ksplit) {
   const int K = GATEUP ? f.d : f.I;
   const int N = GATEUP ? 2 * f.I : f.d;
@@ -739,14 +746,206 @@ __global__ __launch_bounds__(256) void k_ffn_decode(FfnDev f, const uint16_t* __
   }
 }
 
+// Two token blocks: a block's wavefronts take four adjacent stripes and share
+// the activations through LDS (the work split described at the top of the file).
+template <int NB, int RT, int GPW, bool GATEUP>
+__global__ __launch_bounds__(256) void k_ffn_decode(FfnDev f, const uint16_t* __restrict__ hin,
+                                                    uint16_t* __restrict__ hout, float* __restrict__ y, int ksplit) {
+  const int K = GATEUP ? f.d : f.I;
+  const int N = GATEUP ? 2 * f.I : f.d;
+  const int G = K / kGroup;
+  const int n_stripes = N / (kTileRows * RT);
+  const int n_quads = (n_stripes + 3) / 4;
+  const int per_u = n_quads * ksplit;
+  const int u = blockIdx.x / per_u;
+  const int rem = blockIdx.x % per_u;
+  const int quad = rem / ksplit, split = rem % ksplit;
+  // both loads issued together: one round trip before the weight stream starts
+  const int U = f.active[0];
+  const i32x4_t item = reinterpret_cast<const i32x4_t*>(f.active + 4)[u];  // u < min(E, T*k): in bounds
+  if (u >= U) return;  // uniform over the block, as is the next return
+  const int e = item[0], row0 = item[1], n_e = item[2];
+  const uint8_t* blob = f.blob(e);
+  if (!blob) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = lane_id();
+  const int col = lane & 15, kq = lane >> 4;
+  const int gs_per = (G + ksplit - 1) / ksplit;
+  const int g0 = min(G, split * gs_per), g1 = min(G, g0 + gs_per);
+  // wavefront w owns stripe 4 quad + w; past the last stripe it still stages the
+  // activations and meets the barriers, reading the last stripe's weights (unused)
+  const int stripe = quad * 4 + wave;
+  const bool has_stripe = stripe < n_stripes;
+  const int wstripe = min(stripe, n_stripes - 1);
+
+  const uint8_t* codes = blob + (GATEUP ? f.off_w13_codes : f.off_w2_codes) +
+                         (int64_t)(RT * wstripe) * G * kTileBytes + 16 * lane;
+  // a chunk's scales (RT tiles x GPW groups x 16 rows of bf16) in one 16-byte load
+  // per lane: lane c holds half c % 2 of group (c / 2) % GPW of tile c / (2 GPW);
+  // they go through the wavefront's LDS area to the lanes that apply them
+  static_assert(RT * GPW * 2 <= 64, "a chunk's scales in one load per lane");
+  const __amdgpu_buffer_rsrc_t sres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(blob + (GATEUP ? f.off_w13_scales : f.off_w2_scales) + (int64_t)(RT * wstripe) * G * kTileRows * 2),
+      (short)0, RT * G * kTileRows * 2, kBufferRsrcWord3);
+  const int sc_r = lane / (2 * GPW), sc_gi = (lane / 2) % GPW, sc_half = lane & 1;
+  __shared__ u32x4_t s_sw[4][64];
+  u32x4_t swv;
+  const int64_t tile_stride_c = (int64_t)G * kTileBytes;  // bytes between row tiles
+  const u32x4_t ones_w = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  const bf16x8_t ones = as_bf16x8(ones_w);
+
+  u32x4_t cw[GPW][RT];
+  auto load_chunk = [&](int gc) {
+    {  // the scales first: waiting for them does not wait for the codes
+      const int g = gc + sc_gi;
+      const uint32_t off = (sc_r < RT && g < g1) ? (uint32_t)((sc_r * G + g) * kTileRows + 8 * sc_half) * 2u
+                                                 : 0x7F000000u;  // else zeros
+      swv = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sres, off, 0, 0));
+    }
+#pragma unroll
+    for (int gi = 0; gi < GPW; ++gi) {
+      const int g = gc + gi;
+      if (g < g1) {
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+          cw[gi][r] = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4_t*>(codes + r * tile_stride_c + (int64_t)g * kTileBytes));
+      }
+    }
+  };
+
+  // The pass's activations, shared by the four wavefronts through a ring of three
+  // LDS stages in MFMA fragment order: slot (b * 4 + i) * 64 + l holds the 16 bytes
+  // of K step i that lane l of token block b multiplies.  Thread t fills slots
+  // t + 256 m (m < NB), one 16-byte load each per group; group g + 1 is staged
+  // while group g is multiplied and group g + 2 is in flight, with one barrier per
+  // group (a stage is rewritten two groups after its last reader).
+  constexpr int kStages = 3;
+  __shared__ u32x4_t s_x[kStages][NB * 4 * 64];
+  const int tid = threadIdx.x;
+
+  for (int tb0 = 0; tb0 < n_e; tb0 += 16 * NB) {
+    const uint16_t* xrow[NB];  // this thread's staging source of each slot (null: a padding token)
+#pragma unroll
+    for (int m = 0; m < NB; ++m) {
+      const int sl = tid + 256 * m, b = sl / 256, i = (sl / 64) % 4, l = sl % 64;
+      const int c = tb0 + 16 * b + (l & 15);
+      const uint16_t* base = nullptr;
+      if (c < n_e)
+        base = GATEUP ? f.x + (int64_t)(f.sorted_pairs[row0 + c] / f.k) * f.d
+                      : hin + (int64_t)(row0 + c) * f.I;
+      xrow[m] = base ? base + 32 * i + 8 * (l >> 4) : nullptr;
+    }
+    u32x4_t xr[2][NB];
+    auto xload = [&](u32x4_t* v, int g) {
+#pragma unroll
+      for (int m = 0; m < NB; ++m)
+        v[m] = (xrow[m] && g < g1) ? *reinterpret_cast<const u32x4_t*>(xrow[m] + g * kGroup)
+                                   : u32x4_t{0u, 0u, 0u, 0u};
+    };
+    auto xstage = [&](int stage, const u32x4_t* v) {
+#pragma unroll
+      for (int m = 0; m < NB; ++m) s_x[stage][tid + 256 * m] = v[m];
+    };
+    f32x4_t tot[RT][NB];
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) tot[r][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    __syncthreads();  // the previous pass is done with every stage
+    xload(xr[0], g0);
+    xstage(0, xr[0]);
+    xload(xr[1], g0 + 1);
+    int j = 0;  // groups done in this pass
+    for (int gc = g0; gc < g1; gc += GPW) {
+      load_chunk(gc);
+      s_sw[wave][lane] = swv;  // the chunk's scales (the wavefront's LDS ops run in order)
+#pragma unroll
+      for (int gi = 0; gi < GPW; ++gi, ++j) {
+        const int g = gc + gi;
+        if (g >= g1) break;  // uniform
+        xstage((j + 1) % kStages, xr[(j + 1) & 1]);  // group g + 1 (zeros past the range)
+        xload(xr[j & 1], g + 2);
+        __syncthreads();
+        const u32x4_t* st = s_x[j % kStages];
+        f32x4_t acc[RT][NB], as[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          as[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int r = 0; r < RT; ++r) acc[r][b] = as[b];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          bf16x8_t xv[NB];
+#pragma unroll
+          for (int b = 0; b < NB; ++b) xv[b] = as_bf16x8(st[(b * 4 + i) * 64 + lane]);
+#pragma unroll
+          for (int r = 0; r < RT; ++r) {
+            const bf16x8_t w = as_bf16x8(decode_word_biased(cw[gi][r][i], 0x00780078u, 0x3F803F80u));
+#pragma unroll
+            for (int b = 0; b < NB; ++b) acc[r][b] = mfma16x16x32(w, xv[b], acc[r][b]);
+          }
+#pragma unroll
+          for (int b = 0; b < NB; ++b) as[b] = mfma16x16x32(ones, xv[b], as[b]);
+        }
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+          const u32x2_t sw = reinterpret_cast<const u32x2_t*>(s_sw[wave])[(r * GPW + gi) * 4 + kq];
+          const float s4[4] = {bf16_bits_to_f32(sw[0] & 0xFFFFu), bf16_bits_to_f32(sw[0] >> 16),
+                               bf16_bits_to_f32(sw[1] & 0xFFFFu), bf16_bits_to_f32(sw[1] >> 16)};
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              tot[r][b][q] = fmaf(s4[q], fmaf(16.f, acc[r][b][q], -24.f * as[b][q]), tot[r][b][q]);
+        }
+      }
+    }
+    // the wavefront's stripe over the split's whole K range: SwiGLU and h (gate/up)
+    // or the split's fp32 part of the output rows (down)
+    if (has_stripe) {
+      if (GATEUP) {
+#pragma unroll
+        for (int p = 0; p < RT / 2; ++p)
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            const int c = tb0 + 16 * b + col;
+            float hf[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) hf[q] = silu_f32(tot[2 * p][b][q]) * tot[2 * p + 1][b][q];
+            if (c < n_e) {
+              const int hcol = kTileRows * ((RT / 2) * stripe + p) + 4 * kq;
+              const u32x2_t o = pack_bf16x4(hf[0], hf[1], hf[2], hf[3]);
+              *reinterpret_cast<u32x2_t*>(hout + (int64_t)(row0 + c) * f.I + hcol) = o;
+            }
+          }
+      } else {
+        float* yout = y + (int64_t)split * f.P * f.d;
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            const int c = tb0 + 16 * b + col;
+            if (c < n_e) {
+              const int n = kTileRows * (RT * stripe + r) + 4 * kq;
+              *reinterpret_cast<f32x4_t*>(yout + (int64_t)(row0 + c) * f.d + n) = tot[r][b];
+            }
+          }
+      }
+    }
+  }
+}
+
 constexpr int kGateUpRT = 2, kDownRT = 4;
 constexpr int kPersistRT = 4, kPersistNG = 8, kRingRT = 2, kRingNG = 4;
 constexpr int kDenseRT = 2, kDenseNB = 4;  // LDS-activation gate/up: tiles per stripe, ring depth
 
-int decode_down_gpw(int I, int ksplit) {
+int decode_down_gpw(int I, int ksplit, int nb) {
   const int G = I / kGroup;
   const int gs_per = (G + ksplit - 1) / ksplit;
-  return (gs_per + 3) / 4 <= 2 ? 2 : 4;
+  if (nb <= 1) return (gs_per + 3) / 4 <= 2 ? 2 : 4;  // a quarter of the split per wavefront
+  return gs_per <= 8 ? 2 : 4;  // 2: one occupancy step more (fewer registers)
 }
 
 // Resident blocks per CU for a kernel, times the CU count (cached per slot).
@@ -763,20 +962,28 @@ static int persistent_grid(Kern kern, int slot, int threads = 256) {
   return cached[slot];
 }
 
+template <int NB, int GPW, bool GATEUP>
+static void launch_one(const FfnDev& f, const uint16_t* hin, uint16_t* hout, float* y, int ksplit, int64_t grid,
+                       hipStream_t s) {
+  if constexpr (NB == 1)
+    hipLaunchKernelGGL((k_ffn_decode_ksw<1, GATEUP ? 2 : 4, GPW, GATEUP>), dim3((unsigned)grid), dim3(256), 0, s, f,
+                       hin, hout, y, ksplit);
+  else
+    hipLaunchKernelGGL((k_ffn_decode<NB, GATEUP ? 2 : 4, GPW, GATEUP>), dim3((unsigned)grid), dim3(256), 0, s, f,
+                       hin, hout, y, ksplit);
+}
+
 template <int NB>
 static void launch_nb(const FfnDev& f, uint16_t* h, float* y, int ksplit, hipStream_t s, int64_t grid_gu,
                       int64_t grid_dn, int gpw_dn) {
   timing_begin(K_GATEUP_DECODE, s);
-  hipLaunchKernelGGL((k_ffn_decode<NB, kGateUpRT, 4, true>), dim3((unsigned)grid_gu), dim3(256), 0, s, f,
-                     (const uint16_t*)nullptr, h, (float*)nullptr, 1);
+  launch_one<NB, 4, true>(f, nullptr, h, nullptr, 1, grid_gu, s);
   timing_end(K_GATEUP_DECODE, s);
   timing_begin(K_DOWN_DECODE, s);
   if (gpw_dn == 2)
-    hipLaunchKernelGGL((k_ffn_decode<NB, kDownRT, 2, false>), dim3((unsigned)grid_dn), dim3(256), 0, s, f,
-                       (const uint16_t*)h, (uint16_t*)nullptr, y, ksplit);
+    launch_one<NB, 2, false>(f, h, nullptr, y, ksplit, grid_dn, s);
   else
-    hipLaunchKernelGGL((k_ffn_decode<NB, kDownRT, 4, false>), dim3((unsigned)grid_dn), dim3(256), 0, s, f,
-                       (const uint16_t*)h, (uint16_t*)nullptr, y, ksplit);
+    launch_one<NB, 4, false>(f, h, nullptr, y, ksplit, grid_dn, s);
   timing_end(K_DOWN_DECODE, s);
 }
 
@@ -856,9 +1063,12 @@ int launch_decode(const FfnDev& f_in, uint16_t* h, float* y, int ksplit, int nb,
     timing_end(K_DOWN_DECODE, s);
     return check_launch("grouped expert FFN (decode, T <= 16)");
   }
-  const int64_t grid_gu = umax * (2 * f.I / (kTileRows * kGateUpRT));
-  const int64_t grid_dn = umax * (f.d / (kTileRows * kDownRT)) * ksplit;
-  const int gpw_dn = decode_down_gpw(f.I, ksplit);
+  // a block per (active expert, stripe[, K split]) with one token block, else
+  // per (active expert, four stripes[, K split])
+  const int per_block = nb <= 1 ? 1 : 4;
+  const int64_t grid_gu = umax * ceil_div(2 * f.I / (kTileRows * kGateUpRT), per_block);
+  const int64_t grid_dn = umax * ceil_div(f.d / (kTileRows * kDownRT), per_block) * ksplit;
+  const int gpw_dn = decode_down_gpw(f.I, ksplit, nb);
   if (nb <= 1)
     launch_nb<1>(f, h, y, ksplit, s, grid_gu, grid_dn, gpw_dn);
   else

@@ -49,7 +49,10 @@ enum moe_status {
 
 /* Status name of a code (static string). */
 const char* moe_status_string(int status);
-/* Message of the last failing call on this thread ("" if none). */
+/* Message of the last failing call on this thread ("" if none).  With the
+ * environment variable MOE_W4A16_LOG=1 each such message is also printed to
+ * stderr when it is recorded; with 2, every moe_w4a16_grouped_ffn call also
+ * prints the kernels it chose (decode or prefill variant, K split).  Read once. */
 const char* moe_last_error(void);
 /* ABI version of this library. */
 int moe_abi_version(void);

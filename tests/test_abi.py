@@ -207,3 +207,34 @@ def test_mat_layout_matches_oracle(L):
         offs, total = omat.blob_layout_m1(d, I)
         assert (lay.w13_hi, lay.w13_lo, lay.w13_scales, lay.w2_hi, lay.w2_lo, lay.w2_scales) == offs
         assert lay.blob_bytes == total and lay.two_bit_bytes == omat.two_bit_prefix_m1(d, I)
+
+
+def _run_with_log(level):
+    import subprocess
+    import sys
+    code = (
+        "import ctypes\n"
+        "from w4a16_grouped_expert_amd import _lib\n"
+        "L = _lib.lib()\n"
+        "vp = ctypes.c_void_p(16)\n"
+        "assert L.moe_route(vp, vp, 4, 64, 8, 9, 1, vp, vp, vp, None) == 2\n"
+        "print('msg=' + L.moe_last_error().decode())\n"
+    )
+    env = dict(os.environ)
+    env.pop("MOE_W4A16_LOG", None)
+    if level is not None:
+        env["MOE_W4A16_LOG"] = str(level)
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    msg = r.stdout.strip().splitlines()[-1][len("msg="):]
+    return msg, [l for l in r.stderr.splitlines() if l.startswith("[w4a16_moe]")]
+
+
+def test_log_level_env():
+    """MOE_W4A16_LOG=1 echoes each recorded error message to stderr; unset, the
+    library prints nothing (the message stays available through moe_last_error)."""
+    msg, lines = _run_with_log(None)
+    assert msg and lines == []
+    msg1, lines1 = _run_with_log(1)
+    assert msg1 == msg
+    assert lines1 == ["[w4a16_moe] error: " + msg]

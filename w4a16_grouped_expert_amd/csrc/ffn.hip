@@ -263,6 +263,10 @@ extern "C" int moe_w4a16_grouped_ffn(const moe_ffn_args* a, void* stream) {
   // the combine inside the down pass
   const bool fused = mode == MOE_MODE_DECODE && a->T <= 16 && a->combine && !a->slot_of_expert && w.dc_part &&
                      a->bank_stride < ((int64_t)1 << 31) && dc_units_per_wave(f.umax, a->I / kGroup, a->d / 32) > 0;
+  log_info("moe_w4a16_grouped_ffn: T=%d d=%d I=%d E=%d k=%d: %s kernels%s, down K split %d, token blocks %d", a->T,
+           a->d, a->I, a->E, a->k, mode == MOE_MODE_DECODE ? "decode" : "prefill (MFMA-tiled)",
+           fused ? " with the combine in the down pass" : "", mode == MOE_MODE_DECODE ? w.ksplit : 1,
+           mode == MOE_MODE_DECODE ? decode_token_blocks(a->T, a->E, a->k) : 0);
   if (mode == MOE_MODE_DECODE) {
     rc = launch_decode(f, w.h, w.y, w.ksplit, decode_token_blocks(a->T, a->E, a->k), s, fused ? a->out : nullptr, w.dc_part,
                        w.dc_counters);

@@ -1,5 +1,7 @@
 // Host runtime of the W4A16 MoE library: error state, status strings, blob
 // layout, and the per-kernel event timing used by the benchmark.
+#include <cstdio>
+#include <cstdlib>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -10,6 +12,16 @@ namespace moe {
 
 static thread_local std::string g_last_error;
 
+// MOE_W4A16_LOG: 0 or unset silent, 1 errors to stderr, 2 also each grouped
+// call's choices (read once, at the first message)
+int log_level() {
+  static const int level = [] {
+    const char* v = std::getenv("MOE_W4A16_LOG");
+    return v ? std::atoi(v) : 0;
+  }();
+  return level;
+}
+
 void set_error(const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -17,6 +29,17 @@ void set_error(const char* fmt, ...) {
   vsnprintf(buf, sizeof(buf), fmt, ap);
   va_end(ap);
   g_last_error = buf;
+  if (log_level() >= 1) std::fprintf(stderr, "[w4a16_moe] error: %s\n", buf);
+}
+
+void log_info(const char* fmt, ...) {
+  if (log_level() < 2) return;
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  std::fprintf(stderr, "[w4a16_moe] %s\n", buf);
 }
 
 void clear_error() { g_last_error.clear(); }
@@ -61,7 +84,7 @@ void timing_begin(int id, hipStream_t s) {
   std::lock_guard<std::mutex> lk(g_timing_mu);
   hipEvent_t e = pool_get();
   if (!e) return;
-  hipEventRecord(e, s);
+  if (hipEventRecord(e, s) != hipSuccess) return;  // no interval opened
   g_open_start[id] = e;
   g_open[id] = 1;
 }
@@ -72,7 +95,10 @@ void timing_end(int id, hipStream_t s) {
   if (!g_open[id]) return;
   hipEvent_t e = pool_get();
   if (!e) return;
-  hipEventRecord(e, s);
+  if (hipEventRecord(e, s) != hipSuccess) {  // the interval is dropped
+    g_open[id] = 0;
+    return;
+  }
   g_pending[id].push_back({g_open_start[id], e});
   g_open[id] = 0;
 }
@@ -80,7 +106,7 @@ void timing_end(int id, hipStream_t s) {
 static void drain_locked() {
   for (int id = 0; id < K_NUM; ++id) {
     for (auto& tl : g_pending[id]) {
-      hipEventSynchronize(tl.stop);
+      (void)hipEventSynchronize(tl.stop);  // on failure the elapsed-time query fails too and the sample is skipped
       float ms = 0.f;
       if (hipEventElapsedTime(&ms, tl.start, tl.stop) == hipSuccess) {
         g_total_ms[id] += ms;

@@ -14,9 +14,8 @@ namespace moe {
 
 // ---------------------------------------------------------------- host-side errors
 
-void set_error(const char* fmt, ...);  // also printed to stderr at MOE_W4A16_LOG >= 1
+void set_error(const char* fmt, ...);
 void clear_error();
-void log_info(const char* fmt, ...);   // printed to stderr at MOE_W4A16_LOG >= 2
 
 #define MOE_CHECK_ARG(cond, code, ...)      \
   do {                                       \

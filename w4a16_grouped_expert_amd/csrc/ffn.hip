@@ -13,6 +13,8 @@
 
 namespace moe {
 
+void log_info(const char* fmt, ...);  // runtime.hip: printed to stderr at MOE_W4A16_LOG >= 2
+
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, int ksplit, int64_t P, int d, int k,
                                                  const int32_t* __restrict__ pair_pos,
                                                  const float* __restrict__ w, uint16_t* __restrict__ out,

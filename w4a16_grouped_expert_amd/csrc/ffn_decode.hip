@@ -821,7 +821,20 @@ __global__ __launch_bounds__(256) void k_ffn_decode(FfnDev f, const uint16_t* __
   // group (a stage is rewritten two groups after its last reader).
   constexpr int kStages = 3;
   __shared__ u32x4_t s_x[kStages][NB * 4 * 64];
+  // Per-token activation sums of a group, split by K step: wavefront w sums step w
+  // of the group staged one ahead (one MFMA per token block against all-ones
+  // weights) and stores it at [stage][16 b + token][w]; each wavefront then adds
+  // the four parts instead of every wavefront summing the whole group itself.
+  __shared__ f32x4_t s_xs[kStages][NB * 16];
   const int tid = threadIdx.x;
+  auto xsum_part = [&](int stage) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+      const f32x4_t p = mfma16x16x32(ones, as_bf16x8(s_x[stage][(b * 4 + wave) * 64 + lane]), z);
+      if (kq == 0) reinterpret_cast<float*>(&s_xs[stage][16 * b + col])[wave] = p[0];
+    }
+  };
 
   for (int tb0 = 0; tb0 < n_e; tb0 += 16 * NB) {
     const uint16_t* xrow[NB];  // this thread's staging source of each slot (null: a padding token)
@@ -856,6 +869,8 @@ __global__ __launch_bounds__(256) void k_ffn_decode(FfnDev f, const uint16_t* __
     xload(xr[0], g0);
     xstage(0, xr[0]);
     xload(xr[1], g0 + 1);
+    __syncthreads();
+    xsum_part(0);
     int j = 0;  // groups done in this pass
     for (int gc = g0; gc < g1; gc += GPW) {
       load_chunk(gc);
@@ -868,13 +883,18 @@ __global__ __launch_bounds__(256) void k_ffn_decode(FfnDev f, const uint16_t* __
         xload(xr[j & 1], g + 2);
         __syncthreads();
         const u32x4_t* st = s_x[j % kStages];
-        f32x4_t acc[RT][NB], as[NB];
+        float xs[NB];  // the group's activation sums (parts stored at the previous group or the prologue)
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-          as[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int r = 0; r < RT; ++r) acc[r][b] = as[b];
+          const f32x4_t v = s_xs[j % kStages][16 * b + col];
+          xs[b] = (v[0] + v[1]) + (v[2] + v[3]);
         }
+        xsum_part((j + 1) % kStages);  // group g + 1, staged before the barrier above
+        f32x4_t acc[RT][NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int r = 0; r < RT; ++r) acc[r][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           bf16x8_t xv[NB];
@@ -886,8 +906,6 @@ __global__ __launch_bounds__(256) void k_ffn_decode(FfnDev f, const uint16_t* __
 #pragma unroll
             for (int b = 0; b < NB; ++b) acc[r][b] = mfma16x16x32(w, xv[b], acc[r][b]);
           }
-#pragma unroll
-          for (int b = 0; b < NB; ++b) as[b] = mfma16x16x32(ones, xv[b], as[b]);
         }
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
@@ -898,7 +916,7 @@ __global__ __launch_bounds__(256) void k_ffn_decode(FfnDev f, const uint16_t* __
           for (int b = 0; b < NB; ++b)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-              tot[r][b][q] = fmaf(s4[q], fmaf(16.f, acc[r][b][q], -24.f * as[b][q]), tot[r][b][q]);
+              tot[r][b][q] = fmaf(s4[q], fmaf(16.f, acc[r][b][q], -24.f * xs[b]), tot[r][b][q]);
         }
       }
     }

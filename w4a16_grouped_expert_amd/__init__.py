@@ -11,7 +11,7 @@ from .api import (MODE_AUTO, active_experts, MODE_DECODE, MODE_PREFILL, AlignOut
                   moe_w4a16_grouped_ffn_into, moe_w4a16_grouped_ffn_noalloc_into, NOALLOC_SCRATCH_BYTES,
                   pack_experts, pack_w4_g128, timing_enable, timing_read,
                   timing_reset, bf16_expert_bytes, pack_bf16_experts, moe_bf16_grouped_ffn, moe_bf16_grouped_ffn_into,
-                  mat_layout, mat_from_w4, moe_mat_grouped_ffn_into, alloc_layer_counters,
+                  mat_layout, mat_from_w4, moe_mat_grouped_ffn_into, alloc_layer_counters, layer_routing_timed_out,
                   decode_layer_workspace_bytes, moe_decode_layer, moe_decode_layer_into,
                   moe_mat_decode_layer_into)
 from ._lib import LIB_PATH, MoeError, lib  # noqa: F401

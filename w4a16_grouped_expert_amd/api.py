@@ -297,8 +297,18 @@ def moe_mat_decode_layer_into(x, w_router, bank: torch.Tensor, I: int, k: int, r
     return out
 
 
+def layer_routing_timed_out(counters: torch.Tensor) -> bool:
+    """Whether a moe_decode_layer call on these counters gave up its bounded wait
+    for the routing (the last counter; the outputs of that call are invalid).
+    Synchronises the device (every stream) before reading the flag."""
+    torch.cuda.synchronize(counters.device)
+    return bool(int(counters[DECODE_LAYER_COUNTERS - 1].item()))
+
+
 def moe_decode_layer(x, w_router, bank: torch.Tensor, I: int, k: int, renormalize=True, stream=None):
-    """Allocating convenience form of moe_decode_layer_into: returns (out, route)."""
+    """Allocating convenience form of moe_decode_layer_into: returns (out, route).
+    It reads the routing-wait flag after the call (a device round trip) and raises
+    MoeError if the wait timed out."""
     T, d = x.shape
     E = w_router.shape[0]
     route = alloc_route(T, E, k, x.device)
@@ -306,6 +316,8 @@ def moe_decode_layer(x, w_router, bank: torch.Tensor, I: int, k: int, renormaliz
     ws = torch.empty(max(decode_layer_workspace_bytes(T, d, I, E, k), 256), dtype=torch.uint8, device=x.device)
     ctr = alloc_layer_counters(x.device)
     moe_decode_layer_into(x, w_router, bank, I, k, route, out, ws, ctr, renormalize, stream=stream)
+    if layer_routing_timed_out(ctr):
+        raise _lib.MoeError("moe_decode_layer", 5, "the bounded wait for the routing timed out; outputs are invalid")
     return out, route
 
 
